@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused matmul + tensor-parallel collective path on one MI355X.
+
+A step is one TP8 + sequence-parallel MLP pass of one rank at LLaMA2-70B shapes:
+  ALL_GATHER_MATMUL     8 shards of 512 x 8192 gathered to G 4096 x 8192, G @ W
+                        with W 8192 x 7168 (fused gate/up, 2 * 28672 / 8)
+  MATMUL_REDUCE_SCATTER X 4096 x 3584 @ W 3584 x 8192, the 8 ranks' partials
+                        reduce-scattered to this rank's 512 x 8192 slice
+both bf16, split into `--split` m-chunks.  The other ranks' shards and partial
+sums are seeded buffers in the same HBM.  Prints one JSON line on stdout
+(progress goes to stderr).
+
+    python bench.py [--steps K] [--warmup W] [--split S] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "per-rank GEMM+reduce TFLOP/s & % bf16 MFMA peak at LLaMA2-70B TP8 shapes"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_inputs(torch, tgc, synth, split, dev):
+    ag = synth.WORKLOADS["llama70b_ag"]
+    rs = synth.WORKLOADS["llama70b_rs"]
+    world, rank = 8, 0
+    bf16 = torch.bfloat16
+    inp = {"world": world, "rank": rank, "ag": ag, "rs": rs}
+    shard = ag.m // world
+    shards = [synth.normal(ag.wid, synth.T_PEER, r, (shard, ag.k), ag.x_sigma, "bf16") for r in range(world)]
+    inp["ag_shards_cpu"] = shards
+    inp["ag_x"] = shards[rank].to(dev)
+    inp["ag_peers"] = [None if r == rank else shards[r].to(dev) for r in range(world)]
+    inp["ag_w_cpu"] = synth.normal(ag.wid, synth.T_W, 0, (ag.k, ag.n), ag.w_sigma, "bf16")
+    inp["ag_w"] = inp["ag_w_cpu"].to(dev)
+    inp["ag_y"] = torch.empty((ag.m, ag.n), dtype=bf16, device=dev)
+    need = tgc.workspace_bytes(tgc.OP_ALLGATHER_MATMUL, ag.m, ag.n, ag.k, tgc.COC_BF16, world, split)
+    inp["ag_ws"] = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    b = rs.m // world
+    inp["rs_x_cpu"] = synth.normal(rs.wid, synth.T_X, rank, (rs.m, rs.k), rs.x_sigma, "bf16")
+    inp["rs_w_cpu"] = synth.normal(rs.wid, synth.T_W, rank, (rs.k, rs.n), rs.w_sigma, "bf16")
+    inp["rs_x"] = inp["rs_x_cpu"].to(dev)
+    inp["rs_w"] = inp["rs_w_cpu"].to(dev)
+    peers, peers_cpu = [], []
+    for r in range(world):
+        if r == rank:
+            peers.append(None)
+            peers_cpu.append(None)
+            continue
+        sl = synth.normal(rs.wid, synth.T_PEER, r, (b, rs.n), rs.peer_sigma, "bf16")
+        full = torch.full((rs.m, rs.n), float("nan"), dtype=bf16, device=dev)  # rows never read
+        full[rank * b:(rank + 1) * b] = sl.to(dev)
+        peers.append(full)
+        peers_cpu.append(sl)
+    inp["rs_peers"] = peers
+    inp["rs_peer_slices_cpu"] = peers_cpu
+    inp["rs_y"] = torch.empty((b, rs.n), dtype=bf16, device=dev)
+    inp["rs_part"] = torch.empty((rs.m, rs.n), dtype=bf16, device=dev)
+    return inp
+
+
+def flops_of(inp):
+    ag, rs = inp["ag"], inp["rs"]
+    return 2.0 * ag.m * ag.n * ag.k, 2.0 * rs.m * rs.n * rs.k
+
+
+def cpu_baseline(inp, frac):
+    """The oracle on the same step with m scaled by `frac` (all n and k)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+
+    def f64(t):
+        return oracle.decode(t.contiguous().view(__import__("torch").int16).numpy().view(np.uint16), "bf16")
+
+    ag, rs, world, rank = inp["ag"], inp["rs"], inp["world"], inp["rank"]
+    shard_rows = max(1, int(ag.m // world * frac))
+    slice_rows = max(1, int(rs.m // world * frac))
+    t0 = time.perf_counter()
+    # ALL_GATHER_MATMUL on the first `shard_rows` rows of every shard
+    shards = [f64(s[:shard_rows]) for s in inp["ag_shards_cpu"]]
+    y_ag, _ = oracle.allgather_matmul(shards, f64(inp["ag_w_cpu"]))
+    # MATMUL_REDUCE_SCATTER on the first `slice_rows` rows of every rank's slice
+    b = rs.m // world
+    rows = np.concatenate([np.arange(r * b, r * b + slice_rows) for r in range(world)])
+    x = f64(inp["rs_x_cpu"][rows])
+    peers = []
+    for r in range(world):
+        if r == rank:
+            peers.append(None)
+            continue
+        full = np.zeros((world * slice_rows, rs.n))
+        full[rank * slice_rows:(rank + 1) * slice_rows] = f64(inp["rs_peer_slices_cpu"][r][:slice_rows])
+        peers.append(full)
+    y_rs, p_rs = oracle.matmul_reduce_scatter(x, f64(inp["rs_w_cpu"]), peers, rank)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * world * shard_rows * ag.n * ag.k + 2.0 * world * slice_rows * rs.n * rs.k
+    assert np.all(np.isfinite(y_ag)) and np.all(np.isfinite(y_rs))
+    return {
+        "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"the same step with m scaled to {frac:g} (AG {world}x{shard_rows} gathered rows, "
+                  f"RS {world}x{slice_rows} rows), all n and k; float64 numpy oracle incl. decoding the "
+                  f"bf16 inputs; {dt:.2f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--split", type=int, default=4, choices=[1, 2, 4, 8])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-frac", type=float, default=0.25)
+    args = ap.parse_args()
+
+    world_env = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world_env != 1:
+        print(f"bench.py measures one rank's share on a single GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world_env}) is not supported: the other ranks are emulated as "
+              f"buffers in the same HBM, so run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tensor_gemm_collective_amd as tgc
+    from tensor_gemm_collective_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    tgc.lib()
+    log("generating inputs ...")
+    inp = make_inputs(torch, tgc, synth, args.split, dev)
+    torch.cuda.synchronize()
+    f_ag, f_rs = flops_of(inp)
+    rank, split = inp["rank"], args.split
+
+    def run_ag():
+        tgc.allgather_matmul(inp["ag_x"], inp["ag_peers"], inp["ag_w"], rank, y=inp["ag_y"], ws=inp["ag_ws"],
+                             split=split)
+
+    def run_rs():
+        tgc.matmul_reduce_scatter(inp["rs_x"], inp["rs_w"], inp["rs_peers"], rank, y=inp["rs_y"],
+                                  partial_out=inp["rs_part"], split=split)
+
+    def step():
+        run_ag()
+        run_rs()
+
+    log(f"warmup {args.warmup} steps ...")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps, kernel timing events on
+    tgc.profile_enable(True)
+    tgc.profile_read()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = tgc.profile_read()
+    tgc.profile_enable(False)
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step (host wall {wall / args.steps * 1e3:.4f} ms/step)")
+
+    # ---- per-op breakdown (outside the timed region)
+    def time_op(fn, iters=10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    ms_ag = time_op(run_ag)
+    ms_rs = time_op(run_rs)
+
+    value = (f_ag + f_rs) / (ms_step * 1e-3) / 1e12
+    g = prof["gemm"]
+    avg_ms = g["ms"] / max(1, g["launches"])
+    flops_per_launch = g["work"] / max(1, g["launches"])
+    achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
+    comm_ms = (prof["reduce"]["ms"] + prof["gather"]["ms"]) / args.steps
+    gemm_ms = g["ms"] / args.steps
+    hidden = (gemm_ms + comm_ms - ms_step) / comm_ms if comm_ms > 0 else None
+
+    def gbs(c):
+        return round(c["work"] / (c["ms"] * 1e-3) / 1e9, 1) if c["ms"] > 0 else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, emulated peer shards/partials)",
+        "config": {
+            "workload": "LLaMA2-70B TP8+SP MLP, one rank: ALL_GATHER_MATMUL 8x(512x8192) @ 8192x7168 "
+                        "then MATMUL_REDUCE_SCATTER 4096x3584 @ 3584x8192 -> 512x8192",
+            "world": inp["world"], "rank": rank, "split": split, "deterministic": 0,
+        },
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "breakdown": {
+            "allgather_matmul": {"ms": round(ms_ag, 5), "tflops": round(f_ag / (ms_ag * 1e-3) / 1e12, 2)},
+            "matmul_reduce_scatter": {"ms": round(ms_rs, 5), "tflops": round(f_rs / (ms_rs * 1e-3) / 1e12, 2)},
+            "kernel_ms_per_step": {k: round(v["ms"] / args.steps, 5) for k, v in prof.items()},
+            "kernel_launches_per_step": {k: v["launches"] / args.steps for k, v in prof.items()},
+            "reduce_gbs": gbs(prof["reduce"]),
+            "gather_gbs": gbs(prof["gather"]),
+            "comm_hidden_frac": None if hidden is None else round(hidden, 3),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_mfma (m-chunk matmul)",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_ms * 1e3, 3),
+            "flops_per_launch": flops_per_launch,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_frac)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,258 @@
+/*
+ * coc.h -- fused matmul + tensor-parallel collective ("communication over
+ * computation", CoC) for AMD Instinct MI355X (gfx950), one rank's share.
+ *
+ * Pages cited by title and section:
+ *   CoC guide    Ascend PyTorch developer guide, MindSpeed page
+ *                "Communication-over-Computation (计算通信并行)".
+ *   Overlap blog "MindSpeed LLM通信计算重叠与MC2如何榨干昇腾芯片算力".
+ *
+ * What is computed (CoC guide, "Problem analysis"): the forward of
+ * ColumnParallelLinear / RowParallelLinear is a matmul tightly coupled with a
+ * collective -- AllReduce without sequence parallelism, AllGather before /
+ * ReduceScatter after the matmul with it.  CoC (CoC guide, "Approach") splits
+ * the left matrix along m into 2, 4 or 8 pieces so the matmul of one piece
+ * runs while the collective of another is in flight.
+ *
+ * One-GPU model of a rank.  This library runs rank `rank` of a
+ * tensor-parallel group of `world` ranks on a single GPU: what the other
+ * ranks would contribute over the interconnect (their partial products or
+ * their sequence shards) is handed in as buffers in the same device memory
+ * (`peer_bufs`).  The communication step becomes a streaming read of those
+ * buffers; the split/pipeline structure is the same one a multi-GPU version
+ * would use with remote pointers.
+ *
+ * Common conventions
+ *   - All matrices are dense and row-major.  X is m x k, W is k x n,
+ *     Y and partials are m x n (leading dimensions = number of columns).
+ *   - Every pointer argument except `peer_bufs` itself is a DEVICE pointer
+ *     owned by the caller and must be 16-byte aligned.  `peer_bufs` is a
+ *     HOST array of `world` device pointers, read during the call only;
+ *     entry `rank` is ignored (may be NULL).  The library never allocates,
+ *     frees or retains caller memory.
+ *   - Inputs and outputs must not overlap.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous in stream order: work the library puts on its internal
+ *     side stream is joined back into `stream` before the call returns, so
+ *     later work on `stream` sees the outputs.  Inputs must stay valid until
+ *     that work completes.  Different host threads may use different streams
+ *     concurrently; two threads must not use the same stream concurrently.
+ *   - `split` is the number of m-chunks the work is pipelined over: 1
+ *     (serial, no overlap), 2, 4 or 8 (CoC guide, "Usage": the split count
+ *     options; the m dimension must divide by it, CoC guide "Approach" and
+ *     Overlap blog, third-layer caveats).
+ *   - `deterministic` != 0 selects the deterministic variants (CoC guide,
+ *     "Approach", fused-operator list): partial sums are added in ascending
+ *     rank order 0..world-1 in binary32 with this rank's own partial taken
+ *     as stored in `partial_out`, and the sum is rounded once to the dtype.
+ *     The bits of the result then do not depend on `split`, on the run, or
+ *     on which rank computes it.  Non-deterministic mode may use any order.
+ *   - Rounding to fp16 / bf16 is round-to-nearest-even everywhere; matmuls
+ *     accumulate in binary32.
+ *   - Size limits: world in [1, COC_MAX_WORLD], rank in [0, world);
+ *     n and k multiples of 8; each of m*k, k*n, m*n below 2^31 elements.
+ *     m, n or k may be 0.
+ *
+ * Errors.  Arguments are validated on the host before anything is enqueued;
+ * on any error the call returns a non-zero coc_status, enqueues nothing and
+ * writes nothing, and coc_last_error() returns a description (per host
+ * thread).  COC_ERR_HIP wraps a failing HIP runtime call and carries its
+ * message.  No C++ exception crosses this interface.
+ */
+#ifndef COC_H
+#define COC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define COC_MAX_WORLD 8
+#define COC_MAX_SPLIT 8
+
+typedef enum coc_dtype {
+    COC_F32 = 0,   /* IEEE binary32 */
+    COC_F16 = 1,   /* IEEE binary16 */
+    COC_BF16 = 2   /* bfloat16 */
+} coc_dtype;
+
+typedef enum coc_quant_mode {
+    COC_PER_TENSOR = 0,   /* one scale                          */
+    COC_PER_CHANNEL = 1,  /* one scale per output column n      */
+    COC_PER_GROUP = 2     /* one scale per (k / group, n)       */
+} coc_quant_mode;
+
+typedef enum coc_status {
+    COC_OK = 0,
+    COC_ERR_NULL = 1,       /* a required pointer is NULL                      */
+    COC_ERR_SPLIT = 2,      /* split not in {1, 2, 4, 8}                       */
+    COC_ERR_SHAPE = 3,      /* sizes inconsistent / not divisible / too large  */
+    COC_ERR_WORLD = 4,      /* world or rank out of range                      */
+    COC_ERR_DTYPE = 5,      /* dtype or quant mode not supported               */
+    COC_ERR_ALIGN = 6,      /* a device pointer is not 16-byte aligned         */
+    COC_ERR_WORKSPACE = 7,  /* workspace missing or too small                  */
+    COC_ERR_HIP = 8,        /* the HIP runtime reported an error               */
+    COC_ERR_ALIAS = 9       /* an output overlaps an input or another output   */
+} coc_status;
+
+typedef enum coc_op {
+    COC_OP_MATMUL_ALL_REDUCE = 0,
+    COC_OP_MATMUL_REDUCE_SCATTER = 1,
+    COC_OP_ALLGATHER_MATMUL = 2,
+    COC_OP_ALLGATHER_MATMUL_V2 = 3,
+    COC_OP_MATMUL_ALL_REDUCE_W8A16 = 4
+} coc_op;
+
+/*
+ * MATMUL_ALL_REDUCE (CoC guide, "Approach", fused-operator list: compute
+ * first, then communicate; with its deterministic variant).  The RowParallel
+ * forward without sequence parallelism.
+ *
+ *   partial_out = round_dt(X @ W)                       (m x n, this rank's send buffer)
+ *   y           = round_dt(sum_r P_r),  P_rank = partial_out,
+ *                 P_r = peer_bufs[r] (m x n) for r != rank
+ *
+ * x: m x k, w: k x n, y: m x n, partial_out: m x n, all of dtype `dt`.
+ * The left matrix is split into `split` contiguous row blocks; chunk i's
+ * matmul overlaps the reduction of chunk i-1.  Requires m % split == 0.
+ * `ws` is unused (may be NULL, ws_bytes 0).
+ */
+coc_status coc_matmul_all_reduce(const void* x, const void* w, void* y, void* partial_out,
+                                 const void* const* peer_bufs, int32_t world, int32_t rank,
+                                 int64_t m, int64_t n, int64_t k, coc_dtype dt,
+                                 int32_t split, int32_t deterministic,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * MATMUL_REDUCE_SCATTER (CoC guide, "Approach", fused-operator list: compute
+ * first, then communicate; with its deterministic variant).  The RowParallel
+ * forward with sequence parallelism: rank r keeps rows
+ * [r*m/world, (r+1)*m/world) of the reduced product.
+ *
+ *   partial_out = round_dt(X @ W)                                  (m x n)
+ *   y[j, :]     = round_dt(sum_r P_r[rank*m/world + j, :]),  j < m/world
+ *
+ * x: m x k, w: k x n, partial_out: m x n, y: (m/world) x n, peer_bufs[r]:
+ * full m x n partials of which only this rank's row slice is read.  Chunk i
+ * holds the i-th 1/split of every rank's row slice, so every chunk carries
+ * reduction work for this rank.  Requires m % world == 0 and
+ * (m/world) % split == 0.  `ws` is unused.
+ */
+coc_status coc_matmul_reduce_scatter(const void* x, const void* w, void* y, void* partial_out,
+                                     const void* const* peer_bufs, int32_t world, int32_t rank,
+                                     int64_t m, int64_t n, int64_t k, coc_dtype dt,
+                                     int32_t split, int32_t deterministic,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ALL_GATHER_MATMUL and ALL_GATHER_MATMUL_V2 (CoC guide, "Approach",
+ * fused-operator list: communicate first, then compute; V2 also hands back
+ * the all-gathered intermediate).  The ColumnParallel forward with sequence
+ * parallelism.
+ *
+ *   G = [S_0; S_1; ...; S_{world-1}]   (m x k, S_rank = x_shard, S_r = peer_bufs[r])
+ *   y = round_dt(G @ W)                 (m x n)
+ *
+ * x_shard and peer_bufs[r]: (m/world) x k shards; w: k x n; y: m x n.
+ * gathered_out == NULL selects ALL_GATHER_MATMUL (G is staged in `ws`, which
+ * must hold coc_workspace_bytes(COC_OP_ALLGATHER_MATMUL, ...) bytes);
+ * gathered_out != NULL selects ALL_GATHER_MATMUL_V2 and receives G (m x k,
+ * bit-exact copy of the shards; `ws` unused).  The gather of chunk i+1
+ * overlaps the matmul of chunk i; the pipeline starts with the chunk that
+ * holds this rank's own shard.  Requires m % world == 0 and m % split == 0.
+ * `deterministic` is accepted; the op is deterministic in either mode.
+ */
+coc_status coc_allgather_matmul(const void* x_shard, const void* const* peer_bufs, const void* w,
+                                void* y, void* gathered_out, int32_t world, int32_t rank,
+                                int64_t m, int64_t n, int64_t k, coc_dtype dt,
+                                int32_t split, int32_t deterministic,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * w8A16 pseudo-quantised MATMUL_ALL_REDUCE (CoC guide, "Approach", last item
+ * of the fused-operator list: fp16, int8 weights, per-tensor / per-channel /
+ * per-group scales).  Weight-only symmetric quantisation, no zero point:
+ *
+ *   W~[kk, j]   = q[kk, j] * s(kk, j)
+ *       PER_TENSOR  s = scales[0]
+ *       PER_CHANNEL s = scales[j]                    (n scales)
+ *       PER_GROUP   s = scales[(kk / group_size) * n + j]   ((k/group_size) x n)
+ *   partial_out = round_f16(X @ W~),  y = round_f16(sum_r P_r)  as in
+ *   coc_matmul_all_reduce.
+ *
+ * x_f16: m x k fp16; w_q: k x n int8; scales_f16: fp16 as above; y_f16,
+ * partial_out, peer_bufs[r]: m x n fp16.  The int8 weight is dequantised to
+ * fp16 (rounded to nearest even) inside the matmul main loop.  PER_GROUP
+ * requires group_size > 0, group_size % 8 == 0 and k % group_size == 0
+ * (group_size is ignored otherwise).  Requires m % split == 0.  `ws` unused.
+ */
+coc_status coc_matmul_all_reduce_w8a16(const void* x_f16, const int8_t* w_q, const void* scales_f16,
+                                       coc_quant_mode mode, int32_t group_size,
+                                       void* y_f16, void* partial_out,
+                                       const void* const* peer_bufs, int32_t world, int32_t rank,
+                                       int64_t m, int64_t n, int64_t k,
+                                       int32_t split, int32_t deterministic,
+                                       void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes an op needs at these sizes (0 when it needs none).
+ * dt is ignored for COC_OP_MATMUL_ALL_REDUCE_W8A16.  Returns 0 for invalid
+ * arguments as well; the op call itself reports the error. */
+size_t coc_workspace_bytes(coc_op op, int64_t m, int64_t n, int64_t k, coc_dtype dt,
+                           int32_t world, int32_t split);
+
+/* Static name of a status code. */
+const char* coc_status_string(coc_status s);
+
+/* Description of the last failure on the calling host thread ("" if none).
+ * The pointer stays valid until the next call on that thread. */
+const char* coc_last_error(void);
+
+/*
+ * Row map of one pipeline chunk: the rows
+ *   { base + b * stride + j : 0 <= b < nblk, 0 <= j < rows_per_blk }
+ * of the m-row left matrix (matmul rows) or of the gathered matrix.
+ * `red_base` is the first row of the reduction / gather this chunk carries
+ * (for reduce-scatter: the row of the partials; `out_base` is the matching
+ * row of y), `red_rows` the number of rows it covers.
+ */
+typedef struct coc_chunk {
+    int64_t base;
+    int64_t stride;
+    int64_t rows_per_blk;
+    int32_t nblk;
+    int32_t order;          /* position of this chunk in the pipeline */
+    int64_t red_base;
+    int64_t out_base;
+    int64_t red_rows;
+} coc_chunk;
+
+/* Host-only plan introspection: validates (op, m, world, rank, split) like
+ * the op calls do (shape rules only; no pointers) and writes up to
+ * `max_chunks` chunk descriptors in pipeline order.  Returns the status; on
+ * COC_OK *n_chunks is the chunk count.  Touches no GPU state. */
+coc_status coc_plan(coc_op op, int64_t m, int32_t world, int32_t rank, int32_t split,
+                    coc_chunk* chunks, int32_t max_chunks, int32_t* n_chunks);
+
+/*
+ * Kernel timing, for measurement.  While enabled (per process), every
+ * matmul, reduce and gather launch of the library is bracketed by a pair of
+ * HIP events recorded on the stream that launch goes to.
+ * coc_profile_read() waits for the recorded events, adds up their elapsed
+ * times per kernel class, fills the arrays (index 0 = matmul, 1 = reduce /
+ * reduce-scatter, 2 = gather) and clears the record.  Returns COC_OK or
+ * COC_ERR_HIP.  Not for use while another thread issues library calls.
+ */
+#define COC_KCLASS_GEMM 0
+#define COC_KCLASS_REDUCE 1
+#define COC_KCLASS_GATHER 2
+#define COC_NUM_KCLASS 3
+void coc_profile_enable(int32_t on);
+coc_status coc_profile_read(double* total_ms, int64_t* launches, double* work_units);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COC_H */

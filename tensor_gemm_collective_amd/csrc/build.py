@@ -1,0 +1,70 @@
+"""Build libcoc.so (gfx950) in-tree with hipcc.
+
+    python -m tensor_gemm_collective_amd.csrc.build [-v]
+
+Objects go to tensor_gemm_collective_amd/csrc/_build/, the library to
+tensor_gemm_collective_amd/libcoc.so.  Always recompiles.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.dirname(HERE)
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(HERE, "_build")
+LIB_PATH = os.path.join(PKG, "libcoc.so")
+ARCH = "gfx950"
+
+DEVICE_SOURCES = ["kernels.hip"]
+HOST_SOURCES = ["coc_plan.cpp", "coc_api.cpp"]
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{HERE}"]
+# Device code: gfx950 only, packed-fp32 instructions disabled.
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wno-unused-command-line-argument"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose and (r.stdout or r.stderr):
+        print(r.stdout + r.stderr, flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    cc = hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = []
+    for s in DEVICE_SOURCES:
+        obj = os.path.join(BUILD_DIR, s + ".o")
+        jobs.append([cc, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(HERE, s), "-o", obj])
+    for s in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, s + ".o")
+        jobs.append([cc, *COMMON, "-c", os.path.join(HERE, s), "-o", obj])
+    with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), jobs))
+    objs = [j[-1] for j in jobs]
+    tmp = LIB_PATH + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,446 @@
+// The C ABI of the fused ops: pointer validation, per-stream contexts and the
+// two-stream pipeline that overlaps the matmul of one m-chunk with the
+// collective of another.
+//
+// Pipeline (CoC guide, "Solution": compute and communication cut into finer
+// sub-tasks that run as a pipeline; Overlap blog, "core idea": cut both small
+// and let them hide each other):
+//   compute-first ops (all-reduce, reduce-scatter, w8a16 all-reduce):
+//       caller stream:  gemm[0]  gemm[1]  gemm[2] ...
+//       side stream:           reduce[0] reduce[1] ...   (reduce[i] waits on gemm[i])
+//   communicate-first ops (all-gather matmul, V2):
+//       side stream:    gather[0] gather[1] gather[2] ...
+//       caller stream:            gemm[0]   gemm[1]  ... (gemm[i] waits on gather[i])
+// The side stream is forked from and joined back into the caller's stream
+// with events, so the call is ordered like a single kernel on that stream.
+// split == 1 is the serial baseline: everything on the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "coc_internal.h"
+
+namespace coc {
+namespace {
+
+coc_status hip_fail(hipError_t e, const char* what) {
+    return fail(COC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define COC_HIP(expr)                                         \
+    do {                                                      \
+        hipError_t e_ = (expr);                               \
+        if (e_ != hipSuccess) return hip_fail(e_, #expr);     \
+    } while (0)
+
+#define COC_TRY(expr)                       \
+    do {                                    \
+        coc_status s_ = (expr);             \
+        if (s_ != COC_OK) return s_;        \
+    } while (0)
+
+// ------------------------------------------------------------------ contexts
+// One side stream plus pipeline events per (device, caller stream).  Streams
+// are created with the default priority and never destroyed (the process
+// owns them until exit).
+struct StreamCtx {
+    hipStream_t side = nullptr;
+    hipEvent_t ev[COC_MAX_SPLIT] = {};
+    hipEvent_t fork = nullptr;
+    hipEvent_t join = nullptr;
+};
+
+std::mutex g_ctx_mu;
+std::map<std::pair<int, hipStream_t>, StreamCtx*> g_ctx;
+
+coc_status get_ctx(hipStream_t main, StreamCtx** out) {
+    int dev = 0;
+    COC_HIP(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lk(g_ctx_mu);
+    auto key = std::make_pair(dev, main);
+    auto it = g_ctx.find(key);
+    if (it != g_ctx.end()) {
+        *out = it->second;
+        return COC_OK;
+    }
+    StreamCtx* c = new StreamCtx;
+    COC_HIP(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
+    for (auto& e : c->ev) COC_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    COC_HIP(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming));
+    COC_HIP(hipEventCreateWithFlags(&c->join, hipEventDisableTiming));
+    g_ctx[key] = c;
+    *out = c;
+    return COC_OK;
+}
+
+// ------------------------------------------------------------------ timing
+struct ProfRec {
+    hipEvent_t a, b;
+    int cls;
+    double work;
+};
+std::atomic<int> g_prof_on{0};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+coc_status prof_event(hipEvent_t* e) {
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (!g_prof_pool.empty()) {
+            *e = g_prof_pool.back();
+            g_prof_pool.pop_back();
+            return COC_OK;
+        }
+    }
+    COC_HIP(hipEventCreate(e));
+    return COC_OK;
+}
+
+// Launch through `fn` (returns a hipError_t value), bracketed by timing
+// events on `s` when timing is enabled.  `work` is the launch's algorithmic
+// flops (matmul) or bytes (reduce, gather).
+template <class F>
+coc_status launch(int cls, double work, hipStream_t s, F&& fn) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) {
+        const int e = fn();
+        if (e != hipSuccess) return hip_fail(hipError_t(e), "kernel launch");
+        return COC_OK;
+    }
+    hipEvent_t a, b;
+    COC_TRY(prof_event(&a));
+    COC_TRY(prof_event(&b));
+    COC_HIP(hipEventRecord(a, s));
+    const int e = fn();
+    if (e != hipSuccess) return hip_fail(hipError_t(e), "kernel launch");
+    COC_HIP(hipEventRecord(b, s));
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_recs.push_back({a, b, cls, work});
+    return COC_OK;
+}
+
+// ------------------------------------------------------------------ validation
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+    const char* name;
+};
+
+bool overlaps(const Range& a, const Range& b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+Range mk(const void* p, int64_t bytes, const char* name) {
+    const uintptr_t lo = (uintptr_t)p;
+    return Range{lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0), name};
+}
+
+coc_status check_ptr(const void* p, int64_t bytes, const char* name) {
+    if (bytes <= 0) return COC_OK;
+    if (!p) return fail(COC_ERR_NULL, "%s is NULL", name);
+    if ((uintptr_t)p % 16 != 0) return fail(COC_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    return COC_OK;
+}
+
+coc_status check_alias(const std::vector<Range>& outs, const std::vector<Range>& ins) {
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(COC_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (const Range& r : ins)
+            if (overlaps(outs[i], r)) return fail(COC_ERR_ALIAS, "%s overlaps %s", outs[i].name, r.name);
+    }
+    return COC_OK;
+}
+
+// Peer pointers: host array of `world` device pointers, entry `rank` ignored.
+coc_status check_peers(const void* const* peers, const Plan& P, int64_t bytes, std::vector<Range>* ins) {
+    if (P.world == 1 || bytes <= 0) return COC_OK;
+    if (!peers) return fail(COC_ERR_NULL, "peer_bufs is NULL");
+    static const char* names[COC_MAX_WORLD] = {"peer_bufs[0]", "peer_bufs[1]", "peer_bufs[2]",
+                                               "peer_bufs[3]", "peer_bufs[4]", "peer_bufs[5]",
+                                               "peer_bufs[6]", "peer_bufs[7]"};
+    for (int r = 0; r < P.world; ++r) {
+        if (r == P.rank) continue;
+        COC_TRY(check_ptr(peers[r], bytes, names[r]));
+        ins->push_back(mk(peers[r], bytes, names[r]));
+    }
+    return COC_OK;
+}
+
+// ------------------------------------------------------------------ pipelines
+GemmLaunch gemm_for_chunk(const GemmLaunch& g0, const coc_chunk& c) {
+    GemmLaunch g = g0;
+    g.base = c.base;
+    g.stride = c.stride;
+    g.rpb = c.rows_per_blk;
+    g.nblk = c.nblk;
+    return g;
+}
+
+double gemm_flops(const Plan& P, const coc_chunk& c) {
+    return 2.0 * double(c.rows_per_blk) * double(c.nblk) * double(P.n) * double(P.k);
+}
+
+// Compute first, then reduce: all-reduce, reduce-scatter, w8a16 all-reduce.
+coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLaunch& r0,
+                             hipStream_t main) {
+    const size_t es = elem_size(P.dt);
+    auto gemm = [&](int i) {
+        const GemmLaunch g = gemm_for_chunk(g0, P.chunk[i]);
+        return launch(KC_GEMM, gemm_flops(P, P.chunk[i]), main, [&] { return launch_gemm(g, main); });
+    };
+    auto reduce = [&](int i, hipStream_t s) {
+        ReduceLaunch r = r0;
+        r.src_row0 = P.chunk[i].red_base;
+        r.dst_row0 = P.chunk[i].out_base;
+        r.rows = P.chunk[i].red_rows;
+        const double bytes = double(r.nsrc + 1) * double(r.rows) * double(P.n) * double(es);
+        return launch(KC_REDUCE, bytes, s, [&] { return launch_reduce(r, s); });
+    };
+    if (P.split == 1) {
+        COC_TRY(gemm(0));
+        return reduce(0, main);
+    }
+    StreamCtx* c = nullptr;
+    COC_TRY(get_ctx(main, &c));
+    for (int i = 0; i < P.nchunks; ++i) {
+        COC_TRY(gemm(i));
+        COC_HIP(hipEventRecord(c->ev[i], main));
+        COC_HIP(hipStreamWaitEvent(c->side, c->ev[i], 0));
+        COC_TRY(reduce(i, c->side));
+    }
+    COC_HIP(hipEventRecord(c->join, c->side));
+    COC_HIP(hipStreamWaitEvent(main, c->join, 0));
+    return COC_OK;
+}
+
+// Communicate first, then compute: all-gather matmul (and V2).
+coc_status run_comm_first(const Plan& P, const GemmLaunch& g0, const GatherLaunch& a0,
+                          hipStream_t main) {
+    const size_t es = elem_size(P.dt);
+    auto gather = [&](int i, hipStream_t s) {
+        GatherLaunch a = a0;
+        a.row0 = P.chunk[i].red_base;
+        a.rows = P.chunk[i].red_rows;
+        const double bytes = 2.0 * double(a.rows) * double(P.k) * double(es);
+        return launch(KC_GATHER, bytes, s, [&] { return launch_gather(a, s); });
+    };
+    auto gemm = [&](int i) {
+        const GemmLaunch g = gemm_for_chunk(g0, P.chunk[i]);
+        return launch(KC_GEMM, gemm_flops(P, P.chunk[i]), main, [&] { return launch_gemm(g, main); });
+    };
+    if (P.split == 1) {
+        COC_TRY(gather(0, main));
+        return gemm(0);
+    }
+    StreamCtx* c = nullptr;
+    COC_TRY(get_ctx(main, &c));
+    COC_HIP(hipEventRecord(c->fork, main));
+    COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
+    for (int i = 0; i < P.nchunks; ++i) {
+        COC_TRY(gather(i, c->side));
+        COC_HIP(hipEventRecord(c->ev[i], c->side));
+        COC_HIP(hipStreamWaitEvent(main, c->ev[i], 0));
+        COC_TRY(gemm(i));
+    }
+    return COC_OK;
+}
+
+GemmKind kind_of(coc_dtype dt) {
+    return dt == COC_F32 ? GK_F32 : (dt == COC_F16 ? GK_F16 : GK_BF16);
+}
+
+// Shared body of the all-reduce / reduce-scatter / w8a16 entry points.
+coc_status compute_first_op(coc_op op, const void* x, const void* w, const void* scales,
+                            int32_t qmode, int32_t group, void* y, void* partial,
+                            const void* const* peers, int32_t world, int32_t rank, int64_t m,
+                            int64_t n, int64_t k, coc_dtype dt, int32_t split, int32_t det,
+                            void* stream) {
+    clear_error();
+    Plan P;
+    COC_TRY(make_plan(op, m, n, k, dt, world, rank, split, det, &P));
+    const bool w8 = op == COC_OP_MATMUL_ALL_REDUCE_W8A16;
+    const int64_t es = (int64_t)elem_size(P.dt);
+    const int64_t y_rows = op == COC_OP_MATMUL_REDUCE_SCATTER ? m / world : m;
+    if (w8) {
+        if (qmode != COC_PER_TENSOR && qmode != COC_PER_CHANNEL && qmode != COC_PER_GROUP)
+            return fail(COC_ERR_DTYPE, "unknown quant mode %d", qmode);
+        if (qmode == COC_PER_GROUP && (group <= 0 || group % 8 != 0 || k % group != 0))
+            return fail(COC_ERR_SHAPE, "per-group needs group_size > 0, group_size %% 8 == 0 and "
+                                       "k %% group_size == 0 (group_size=%d k=%lld)",
+                        group, (long long)k);
+    }
+    if (m == 0 || n == 0) return COC_OK;  // no output elements
+
+    std::vector<Range> ins, outs;
+    COC_TRY(check_ptr(x, m * k * es, "x"));
+    COC_TRY(check_ptr(w, k * n * (w8 ? 1 : es), "w"));
+    COC_TRY(check_ptr(y, y_rows * n * es, "y"));
+    COC_TRY(check_ptr(partial, m * n * es, "partial_out"));
+    ins.push_back(mk(x, m * k * es, "x"));
+    ins.push_back(mk(w, k * n * (w8 ? 1 : es), "w"));
+    int64_t scale_elems = 0;
+    if (w8 && k > 0) {
+        scale_elems = qmode == COC_PER_TENSOR ? 1 : (qmode == COC_PER_CHANNEL ? n : (k / group) * n);
+        COC_TRY(check_ptr(scales, scale_elems * 2, "scales"));
+        ins.push_back(mk(scales, scale_elems * 2, "scales"));
+    }
+    COC_TRY(check_peers(peers, P, m * n * es, &ins));
+    outs.push_back(mk(y, y_rows * n * es, "y"));
+    outs.push_back(mk(partial, m * n * es, "partial_out"));
+    COC_TRY(check_alias(outs, ins));
+
+    GemmLaunch g0{};
+    g0.kind = w8 ? GK_W8_F16 : kind_of(P.dt);
+    g0.a = x;
+    g0.b = w;
+    g0.c = partial;
+    g0.scales = scales;
+    g0.qmode = qmode;
+    g0.group = qmode == COC_PER_GROUP ? group : 0;
+    g0.n = n;
+    g0.k = k;
+
+    ReduceLaunch r0{};
+    r0.dt = P.dt;
+    r0.nsrc = world;
+    for (int r = 0; r < world; ++r) r0.src[r] = (r == rank) ? partial : peers[r];
+    r0.dst = y;
+    r0.n = n;
+    return run_compute_first(P, g0, r0, (hipStream_t)stream);
+}
+
+}  // namespace
+}  // namespace coc
+
+using namespace coc;
+
+extern "C" {
+
+coc_status coc_matmul_all_reduce(const void* x, const void* w, void* y, void* partial_out,
+                                 const void* const* peer_bufs, int32_t world, int32_t rank,
+                                 int64_t m, int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                 int32_t deterministic, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return compute_first_op(COC_OP_MATMUL_ALL_REDUCE, x, w, nullptr, 0, 0, y, partial_out, peer_bufs,
+                            world, rank, m, n, k, dt, split, deterministic, stream);
+}
+
+coc_status coc_matmul_reduce_scatter(const void* x, const void* w, void* y, void* partial_out,
+                                     const void* const* peer_bufs, int32_t world, int32_t rank,
+                                     int64_t m, int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                     int32_t deterministic, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return compute_first_op(COC_OP_MATMUL_REDUCE_SCATTER, x, w, nullptr, 0, 0, y, partial_out,
+                            peer_bufs, world, rank, m, n, k, dt, split, deterministic, stream);
+}
+
+coc_status coc_matmul_all_reduce_w8a16(const void* x_f16, const int8_t* w_q, const void* scales_f16,
+                                       coc_quant_mode mode, int32_t group_size, void* y_f16,
+                                       void* partial_out, const void* const* peer_bufs,
+                                       int32_t world, int32_t rank, int64_t m, int64_t n, int64_t k,
+                                       int32_t split, int32_t deterministic, void* ws,
+                                       size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return compute_first_op(COC_OP_MATMUL_ALL_REDUCE_W8A16, x_f16, w_q, scales_f16, (int32_t)mode,
+                            group_size, y_f16, partial_out, peer_bufs, world, rank, m, n, k, COC_F16,
+                            split, deterministic, stream);
+}
+
+coc_status coc_allgather_matmul(const void* x_shard, const void* const* peer_bufs, const void* w,
+                                void* y, void* gathered_out, int32_t world, int32_t rank, int64_t m,
+                                int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                int32_t deterministic, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    const coc_op op = gathered_out ? COC_OP_ALLGATHER_MATMUL_V2 : COC_OP_ALLGATHER_MATMUL;
+    Plan P;
+    COC_TRY(make_plan(op, m, n, k, dt, world, rank, split, deterministic, &P));
+    const int64_t es = (int64_t)elem_size(P.dt);
+    const int64_t shard = m / world;
+    if (m == 0 || (n == 0 && !gathered_out) || (n == 0 && k == 0)) return COC_OK;
+
+    void* g = gathered_out;
+    if (!g && m * k > 0) {
+        const size_t need = workspace_bytes(P);
+        if (!ws) return fail(COC_ERR_WORKSPACE, "ALL_GATHER_MATMUL needs a %zu-byte workspace", need);
+        if (ws_bytes < need)
+            return fail(COC_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+        if ((uintptr_t)ws % 16 != 0) return fail(COC_ERR_ALIGN, "ws is not 16-byte aligned");
+        g = ws;
+    }
+    std::vector<Range> ins, outs;
+    COC_TRY(check_ptr(x_shard, shard * k * es, "x_shard"));
+    COC_TRY(check_ptr(w, k * n * es, "w"));
+    COC_TRY(check_ptr(y, m * n * es, "y"));
+    COC_TRY(check_ptr(gathered_out, gathered_out ? m * k * es : 0, "gathered_out"));
+    ins.push_back(mk(x_shard, shard * k * es, "x_shard"));
+    ins.push_back(mk(w, k * n * es, "w"));
+    COC_TRY(check_peers(peer_bufs, P, shard * k * es, &ins));
+    outs.push_back(mk(y, m * n * es, "y"));
+    outs.push_back(mk(g, m * k * es, gathered_out ? "gathered_out" : "ws"));
+    COC_TRY(check_alias(outs, ins));
+
+    GatherLaunch a0{};
+    a0.dt = P.dt;
+    a0.nsrc = world;
+    for (int r = 0; r < world; ++r) a0.src[r] = (r == rank) ? x_shard : peer_bufs[r];
+    a0.shard_rows = shard;
+    a0.dst = g;
+    a0.k = k;
+
+    GemmLaunch g0{};
+    g0.kind = kind_of(P.dt);
+    g0.a = g;
+    g0.b = w;
+    g0.c = y;
+    g0.n = n;
+    g0.k = k;
+    return run_comm_first(P, g0, a0, (hipStream_t)stream);
+}
+
+void coc_profile_enable(int32_t on) { g_prof_on.store(on ? 1 : 0); }
+
+coc_status coc_profile_read(double* total_ms, int64_t* launches, double* work_units) {
+    clear_error();
+    std::vector<ProfRec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        recs.swap(g_prof_recs);
+    }
+    double ms[COC_NUM_KCLASS] = {0, 0, 0};
+    int64_t cnt[COC_NUM_KCLASS] = {0, 0, 0};
+    double work[COC_NUM_KCLASS] = {0, 0, 0};
+    coc_status st = COC_OK;
+    for (const ProfRec& r : recs) {
+        float t = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+        if (e != hipSuccess && st == COC_OK) st = hip_fail(e, "hipEventElapsedTime");
+        ms[r.cls] += t;
+        cnt[r.cls] += 1;
+        work[r.cls] += r.work;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        for (const ProfRec& r : recs) {
+            g_prof_pool.push_back(r.a);
+            g_prof_pool.push_back(r.b);
+        }
+    }
+    for (int i = 0; i < COC_NUM_KCLASS; ++i) {
+        if (total_ms) total_ms[i] = ms[i];
+        if (launches) launches[i] = cnt[i];
+        if (work_units) work_units[i] = work[i];
+    }
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,566 @@
+// gfx950 kernels of the fused matmul + collective path.
+//
+//   gemm_mfma   m-chunk matmul, bf16 / fp16 inputs (or int8 weights dequantised
+//               to fp16 in the main loop), binary32 accumulation on MFMA,
+//               round-to-nearest-even to the storage dtype.  The "Matmul" of
+//               the CoC guide's matmul/collective pairs ("Problem analysis").
+//   gemm_f32    the same for binary32 inputs on the vector ALUs.
+//   reduce_rows fixed-order sum of the ranks' partials for a block of rows:
+//               the AllReduce / ReduceScatter half of a pair.
+//   gather_rows bit copy of sequence shards into the gathered matrix: the
+//               AllGather half of the ColumnParallel pair.
+//
+// Every kernel takes fully validated sizes; all global accesses are guarded by
+// the row / column / k bounds passed in.
+#include <hip/hip_runtime.h>
+
+#include "coc_internal.h"
+
+namespace coc {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------ conversions
+// binary32 -> bfloat16, round to nearest even: add 0x7fff plus the lowest kept
+// bit, then drop the low 16 bits (a carry into the exponent handles rounding
+// up to the next binade and to infinity).  NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// binary32 -> binary16 with the hardware conversion (round to nearest even
+// in the default mode, binary16 subnormals kept).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    _Float16 h = (_Float16)f;
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    if constexpr (DT == COC_BF16)
+        return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    else
+        return f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float unpack_lo(uint32_t w) {
+    if constexpr (DT == COC_BF16) return bf16_bits_to_f32(w & 0xffffu);
+    else return f16_bits_to_f32(w & 0xffffu);
+}
+template <int DT>
+__device__ __forceinline__ float unpack_hi(uint32_t w) {
+    if constexpr (DT == COC_BF16) return bf16_bits_to_f32(w >> 16);
+    else return f16_bits_to_f32(w >> 16);
+}
+
+// ------------------------------------------------------------------ row maps
+// A chunk's rows: { base + b*stride + j : b < nblk, j < rpb }, local index
+// r = b*rpb + j.
+__device__ __forceinline__ int64_t map_row(int32_t r, int32_t rpb, int64_t base, int64_t stride) {
+    const int32_t b = r / rpb;
+    return base + (int64_t)b * stride + (r - b * rpb);
+}
+
+struct GemmParams {
+    const uint8_t* a;
+    const uint8_t* b;
+    uint8_t* c;
+    const uint16_t* scales;
+    int64_t base, stride;
+    int32_t rpb, rows, n, k;
+    int32_t tiles_m, tiles_n;
+    int32_t qmode, group;
+};
+
+// ------------------------------------------------------------------ MFMA GEMM
+// Tile BM x BN x 64, 256 threads as 2 x 2 waves, each wave BM/2 x BN/2 made of
+// 32x32 MFMA blocks (v_mfma_f32_32x32x16_{bf16,f16}).
+//
+// Both operands sit in LDS K-contiguous: A as [BM rows][64 k], the weight as
+// [BN columns][64 k] (W is k x n row-major in memory, so each thread loads an
+// 8 k x 8 n block with 16-byte row loads and transposes it in registers before
+// the LDS store).  The 16-byte chunk c of LDS row `row` is stored at position
+// c ^ swz(row), which keeps both the row-wise stores and the MFMA operand
+// reads of 8 consecutive lanes on distinct banks.
+//
+// The MFMA computes C^T = W^T X^T: operand A is the weight fragment (32
+// columns n), operand B the activation fragment (32 rows m).  Each lane then
+// holds 4 consecutive n of one row m per 32x32 block, written as one 8-byte
+// store.  The k ordering inside one MFMA step is the same for every tile
+// shape, so the bits of an output element do not depend on BM / BN.
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+template <int KIND>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (KIND == GK_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <int BM, int BN, int KIND>
+__global__ __launch_bounds__(256) void gemm_mfma(GemmParams p) {
+    constexpr int BK = 64;
+    constexpr int NT = 256;
+    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int A_ITERS = BM * 8 / NT;   // 16-byte A chunks per thread
+    constexpr int NB = BN / 8;             // 8-column blocks of the weight tile
+    static_assert(BN <= NT, "one 8x8 weight block per thread at most");
+    constexpr int OUT_DT = (KIND == GK_BF16) ? COC_BF16 : COC_F16;
+
+    __shared__ u32x4 smem[2 * (BM + BN) * 8];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int bid = blockIdx.x;
+    const int tm = bid % p.tiles_m;
+    const int tn = bid / p.tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // ---- A rows handled by this thread (row map evaluated once)
+    const int akc = t & 7;
+    const uint8_t* arow[A_ITERS];
+    bool aval[A_ITERS];
+#pragma unroll
+    for (int i = 0; i < A_ITERS; ++i) {
+        const int r = m0 + (t >> 3) + 32 * i;
+        aval[i] = r < p.rows;
+        const int64_t gr = aval[i] ? map_row(r, p.rpb, p.base, p.stride) : 0;
+        arow[i] = p.a + gr * (int64_t)p.k * 2;
+    }
+    // ---- weight block handled by this thread
+    const bool bact = t < BN;
+    const int bkb = t / NB, bnb = t % NB;
+    const int bcol = n0 + bnb * 8;
+    const bool bcolv = bact && bcol < p.n;
+
+    u32x4 ra[A_ITERS];
+    u32x4 rb[8];      // 16-bit weights: 8 k rows x 8 columns
+    u32x2 rq[8];      // int8 weights:   8 k rows x 8 columns
+    u32x4 rs;         // fp16 scales of the 8 columns (per-channel / per-group)
+    uint32_t s0 = 0;  // per-tensor scale bits
+    if constexpr (KIND == GK_W8_F16) {
+        rs = u32x4{0, 0, 0, 0};
+        if (p.qmode == COC_PER_TENSOR) {
+            s0 = p.scales[0];
+        } else if (p.qmode == COC_PER_CHANNEL && bcolv) {
+            rs = *(const u32x4*)(p.scales + bcol);
+        }
+    }
+
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_ITERS; ++i) {
+            const int kk = k0 + akc * 8;
+            ra[i] = (aval[i] && kk < p.k) ? *(const u32x4*)(arow[i] + (int64_t)kk * 2)
+                                          : u32x4{0, 0, 0, 0};
+        }
+        const int kr0 = k0 + bkb * 8;
+        const bool bv = bcolv && kr0 < p.k;
+        if constexpr (KIND == GK_W8_F16) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                rq[j] = bv ? *(const u32x2*)(p.b + (int64_t)(kr0 + j) * p.n + bcol) : u32x2{0, 0};
+            if (p.qmode == COC_PER_GROUP && bv)
+                rs = *(const u32x4*)(p.scales + (int64_t)(kr0 / p.group) * p.n + bcol);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                rb[j] = bv ? *(const u32x4*)(p.b + ((int64_t)(kr0 + j) * p.n + bcol) * 2)
+                           : u32x4{0, 0, 0, 0};
+        }
+    };
+
+    auto store = [&](int buf) {
+        u32x4* As = smem + buf * (BM + BN) * 8;
+        u32x4* Bs = As + BM * 8;
+#pragma unroll
+        for (int i = 0; i < A_ITERS; ++i) {
+            const int row = (t >> 3) + 32 * i;
+            As[row * 8 + (akc ^ swz(row))] = ra[i];
+        }
+        if (bact) {
+            if constexpr (KIND == GK_W8_F16) {
+                // dequantise: w = fp16(q) * scale, rounded to nearest even in fp16
+                uint32_t h[8][8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    uint32_t sb;
+                    if (p.qmode == COC_PER_TENSOR) sb = s0;
+                    else sb = (c & 1) ? (rs[c >> 1] >> 16) : (rs[c >> 1] & 0xffffu);
+                    const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)sb);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int8_t q = (int8_t)((rq[j][c >> 2] >> (8 * (c & 3))) & 0xffu);
+                        const _Float16 w = (_Float16)(int)q * sc;
+                        h[j][c] = __builtin_bit_cast(uint16_t, w);
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int nl = bnb * 8 + c;
+                    u32x4 v;
+#pragma unroll
+                    for (int pp = 0; pp < 4; ++pp) v[pp] = h[2 * pp][c] | (h[2 * pp + 1][c] << 16);
+                    Bs[nl * 8 + (bkb ^ swz(nl))] = v;
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int nl = bnb * 8 + c;
+                    u32x4 v;
+#pragma unroll
+                    for (int pp = 0; pp < 4; ++pp) {
+                        const uint32_t lo = rb[2 * pp][c >> 1];
+                        const uint32_t hi = rb[2 * pp + 1][c >> 1];
+                        v[pp] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                                        : ((lo & 0xffffu) | (hi << 16));
+                    }
+                    Bs[nl * 8 + (bkb ^ swz(nl))] = v;
+                }
+            }
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    constexpr int MFMA_KIND = (KIND == GK_BF16) ? GK_BF16 : GK_F16;
+    auto compute = [&](int buf) {
+        const u32x4* As = smem + buf * (BM + BN) * 8;
+        const u32x4* Bs = As + BM * 8;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int kc = ks * 2 + (lane >> 5);
+            u32x4 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = wm * WTM + i * 32 + (lane & 31);
+                af[i] = As[row * 8 + (kc ^ swz(row))];
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int row = wn * WTN + j * 32 + (lane & 31);
+                bf[j] = Bs[row * 8 + (kc ^ swz(row))];
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<MFMA_KIND>(bf[j], af[i], acc[i][j]);
+        }
+    };
+
+    const int KT = (p.k + BK - 1) / BK;
+    if (KT > 0) {
+        load(0);
+        store(0);
+        __syncthreads();
+        for (int kt = 0; kt < KT; ++kt) {
+            if (kt + 1 < KT) load((kt + 1) * BK);
+            compute(kt & 1);
+            if (kt + 1 < KT) store((kt + 1) & 1);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: lane holds n = j*8 + (lane/32)*4 + {0..3} of row m = lane%32
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int r = m0 + wm * WTM + i * 32 + (lane & 31);
+        if (r >= p.rows) continue;
+        const int64_t gr = map_row(r, p.rpb, p.base, p.stride);
+        uint8_t* crow = p.c + gr * (int64_t)p.n * 2;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
+                if (col < p.n) {
+                    u32x2 v;
+                    v[0] = pack2<OUT_DT>(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+                    v[1] = pack2<OUT_DT>(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+                    *(u32x2*)(crow + (int64_t)col * 2) = v;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ fp32 GEMM
+// 64 x 64 x 16 tiles, 256 threads, 4 x 4 outputs per thread, fused
+// multiply-add in k order (binary32 throughout).
+__global__ __launch_bounds__(256) void gemm_f32(GemmParams p) {
+    constexpr int BM = 64, BN = 64, BK = 16;
+    __shared__ float As[BK][BM + 4];
+    __shared__ float Bs[BK][BN + 4];
+    const int t = threadIdx.x;
+    const int tx = t & 15, ty = t >> 4;
+    const int tm = blockIdx.x % p.tiles_m, tn = blockIdx.x / p.tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int ar = t >> 2, akc = (t & 3) * 4;
+    const bool arv = m0 + ar < p.rows;
+    const float* arow =
+        (const float*)p.a + (arv ? map_row(m0 + ar, p.rpb, p.base, p.stride) : 0) * (int64_t)p.k;
+    const int bkr = t >> 4, bcol = n0 + (t & 15) * 4;
+    const bool bcv = bcol < p.n;
+
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+    for (int k0 = 0; k0 < p.k; k0 += BK) {
+        f32x4 va = {0, 0, 0, 0};
+        if (arv && k0 + akc < p.k) va = *(const f32x4*)(arow + k0 + akc);
+        f32x4 vb = {0, 0, 0, 0};
+        if (bcv && k0 + bkr < p.k) vb = *(const f32x4*)((const float*)p.b + (int64_t)(k0 + bkr) * p.n + bcol);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[akc + e][ar] = va[e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bs[bkr][(t & 15) * 4 + e] = vb[e];
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+    const int col = n0 + tx * 4;
+    if (col >= p.n) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = m0 + ty * 4 + i;
+        if (r >= p.rows) continue;
+        float* crow = (float*)p.c + map_row(r, p.rpb, p.base, p.stride) * (int64_t)p.n;
+        *(f32x4*)(crow + col) = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+    }
+}
+
+// ------------------------------------------------------------------ reduce
+// dst[dst_row0 + r][:] = round(sum_{s=0}^{nsrc-1} src[s][src_row0 + r][:]),
+// binary32 accumulation in ascending source order.  One 16-byte vector per
+// thread per step (8 x 16-bit or 4 x 32-bit elements); the loads of all
+// sources are issued before the adds.
+struct ReduceParams {
+    const uint8_t* src[COC_MAX_WORLD];
+    uint8_t* dst;
+    int64_t src_row0, dst_row0;
+    int64_t row_bytes;   // n * element size
+    int32_t nsrc;
+    int32_t vpr;         // 16-byte vectors per row
+    int32_t total;       // rows * vpr
+};
+
+template <int DT>
+__global__ __launch_bounds__(256) void reduce_rows(ReduceParams p) {
+    const int stride = gridDim.x * 256;
+    for (int v = blockIdx.x * 256 + threadIdx.x; v < p.total; v += stride) {
+        const int row = v / p.vpr;
+        const int cv = v - row * p.vpr;
+        const int64_t so = (p.src_row0 + row) * p.row_bytes + (int64_t)cv * 16;
+        const int64_t dof = (p.dst_row0 + row) * p.row_bytes + (int64_t)cv * 16;
+        u32x4 x[COC_MAX_WORLD];
+#pragma unroll
+        for (int s = 0; s < COC_MAX_WORLD; ++s)
+            if (s < p.nsrc) x[s] = *(const u32x4*)(p.src[s] + so);
+        u32x4 out;
+        if constexpr (DT == COC_F32) {
+            f32x4 acc = __builtin_bit_cast(f32x4, x[0]);
+#pragma unroll
+            for (int s = 1; s < COC_MAX_WORLD; ++s) {
+                if (s < p.nsrc) {
+                    const f32x4 y = __builtin_bit_cast(f32x4, x[s]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = acc[e] + y[e];
+                }
+            }
+            out = __builtin_bit_cast(u32x4, acc);
+        } else {
+            float acc[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = unpack_lo<DT>(x[0][e]);
+                acc[2 * e + 1] = unpack_hi<DT>(x[0][e]);
+            }
+#pragma unroll
+            for (int s = 1; s < COC_MAX_WORLD; ++s) {
+                if (s < p.nsrc) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[2 * e] = acc[2 * e] + unpack_lo<DT>(x[s][e]);
+                        acc[2 * e + 1] = acc[2 * e + 1] + unpack_hi<DT>(x[s][e]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = pack2<DT>(acc[2 * e], acc[2 * e + 1]);
+        }
+        *(u32x4*)(p.dst + dof) = out;
+    }
+}
+
+// ------------------------------------------------------------------ gather
+// dst row g (g in [row0, row0 + rows)) = row g % shard_rows of shard
+// g / shard_rows; 16-byte vector copies.
+struct GatherParams {
+    const uint8_t* src[COC_MAX_WORLD];
+    uint8_t* dst;
+    int64_t row_bytes;   // k * element size
+    int32_t shard_rows;
+    int32_t row0;
+    int32_t vpr;
+    int32_t total;
+};
+
+__global__ __launch_bounds__(256) void gather_rows(GatherParams p) {
+    const int stride = gridDim.x * 256;
+    for (int v = blockIdx.x * 256 + threadIdx.x; v < p.total; v += stride) {
+        const int row = v / p.vpr;
+        const int cv = v - row * p.vpr;
+        const int g = p.row0 + row;
+        const int s = g / p.shard_rows;
+        const int local = g - s * p.shard_rows;
+        const uint8_t* sp = p.src[0];
+#pragma unroll
+        for (int i = 1; i < COC_MAX_WORLD; ++i)
+            if (s == i) sp = p.src[i];
+        const u32x4 x = *(const u32x4*)(sp + (int64_t)local * p.row_bytes + (int64_t)cv * 16);
+        *(u32x4*)(p.dst + (int64_t)g * p.row_bytes + (int64_t)cv * 16) = x;
+    }
+}
+
+int grid_for(int64_t total_vec) {
+    const int64_t want = (total_vec + 255) / 256;
+    const int64_t cap = 256 * 8;
+    return (int)(want < cap ? (want > 0 ? want : 1) : cap);
+}
+
+template <int BM, int BN, int KIND>
+hipError_t launch_mfma(GemmParams p, hipStream_t s) {
+    p.tiles_m = (p.rows + BM - 1) / BM;
+    p.tiles_n = (p.n + BN - 1) / BN;
+    const int blocks = p.tiles_m * p.tiles_n;
+    hipLaunchKernelGGL((gemm_mfma<BM, BN, KIND>), dim3(blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_mfma_kind(GemmParams p, hipStream_t s) {
+    // Tile shape: the largest tile that still gives every compute unit a
+    // workgroup for this chunk.  All shapes share the k loop, so the choice
+    // never changes the result bits.
+    const int64_t t256 = ((p.rows + 255) / 256) * ((p.n + 255) / 256);
+    const int64_t t256x128 = ((p.rows + 255) / 256) * ((p.n + 127) / 128);
+    if (t256 >= 256) return launch_mfma<256, 256, KIND>(p, s);
+    if (t256x128 >= 256) return launch_mfma<256, 128, KIND>(p, s);
+    return launch_mfma<128, 128, KIND>(p, s);
+}
+
+}  // namespace
+
+int launch_gemm(const GemmLaunch& g, void* stream) {
+    const int64_t rows = int64_t(g.nblk) * g.rpb;
+    if (rows == 0 || g.n == 0) return hipSuccess;
+    GemmParams p{};
+    p.a = (const uint8_t*)g.a;
+    p.b = (const uint8_t*)g.b;
+    p.c = (uint8_t*)g.c;
+    p.scales = (const uint16_t*)g.scales;
+    p.base = g.base;
+    p.stride = g.stride;
+    p.rpb = (int32_t)g.rpb;
+    p.rows = (int32_t)rows;
+    p.n = (int32_t)g.n;
+    p.k = (int32_t)g.k;
+    p.qmode = g.qmode;
+    p.group = g.group > 0 ? g.group : 1;
+    hipStream_t s = (hipStream_t)stream;
+    switch (g.kind) {
+        case GK_F32: {
+            p.tiles_m = (p.rows + 63) / 64;
+            p.tiles_n = (p.n + 63) / 64;
+            hipLaunchKernelGGL(gemm_f32, dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
+            return hipGetLastError();
+        }
+        case GK_F16: return launch_mfma_kind<GK_F16>(p, s);
+        case GK_BF16: return launch_mfma_kind<GK_BF16>(p, s);
+        case GK_W8_F16: return launch_mfma_kind<GK_W8_F16>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+int launch_reduce(const ReduceLaunch& r, void* stream) {
+    if (r.rows == 0 || r.n == 0) return hipSuccess;
+    ReduceParams p{};
+    for (int i = 0; i < COC_MAX_WORLD; ++i) p.src[i] = (const uint8_t*)(i < r.nsrc ? r.src[i] : r.src[0]);
+    p.dst = (uint8_t*)r.dst;
+    p.src_row0 = r.src_row0;
+    p.dst_row0 = r.dst_row0;
+    p.row_bytes = r.n * (int64_t)elem_size(r.dt);
+    p.nsrc = r.nsrc;
+    p.vpr = (int32_t)(p.row_bytes / 16);
+    p.total = (int32_t)(r.rows * p.vpr);
+    hipStream_t s = (hipStream_t)stream;
+    const int grid = grid_for(p.total);
+    switch (r.dt) {
+        case COC_F32: hipLaunchKernelGGL(reduce_rows<COC_F32>, dim3(grid), dim3(256), 0, s, p); break;
+        case COC_F16: hipLaunchKernelGGL(reduce_rows<COC_F16>, dim3(grid), dim3(256), 0, s, p); break;
+        case COC_BF16: hipLaunchKernelGGL(reduce_rows<COC_BF16>, dim3(grid), dim3(256), 0, s, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+int launch_gather(const GatherLaunch& g, void* stream) {
+    if (g.rows == 0 || g.k == 0) return hipSuccess;
+    GatherParams p{};
+    for (int i = 0; i < COC_MAX_WORLD; ++i) p.src[i] = (const uint8_t*)(i < g.nsrc ? g.src[i] : g.src[0]);
+    p.dst = (uint8_t*)g.dst;
+    p.row_bytes = g.k * (int64_t)elem_size(g.dt);
+    p.shard_rows = (int32_t)g.shard_rows;
+    p.row0 = (int32_t)g.row0;
+    p.vpr = (int32_t)(p.row_bytes / 16);
+    p.total = (int32_t)(g.rows * p.vpr);
+    hipStream_t s = (hipStream_t)stream;
+    hipLaunchKernelGGL(gather_rows, dim3(grid_for(p.total)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace coc

@@ -1,0 +1,320 @@
+"""GPU parity of the HIP path against the CPU oracle, at sizes the oracle
+finishes in seconds (several tiles, ragged tails), plus the properties the
+method fixes: bit-exact gather, bitwise-stable deterministic reduction,
+chunk-count invariance, reduce-scatter == all-reduce slice.
+
+All calls go through the Python binding into libcoc.so (C ABI).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_gemm_collective_amd as tgc
+from tensor_gemm_collective_amd import synth
+from tests._util import (TOL, TORCH_DT, assert_bits_equal, assert_close, dev, encode_dtype, f64,
+                         log, raw)
+
+pytestmark = pytest.mark.gpu
+
+WID_TEST = 100   # workload ids >= 100: parity-test inputs
+
+
+def _ints(tag, shape, lo, hi, dtype):
+    return synth.integers(WID_TEST + tag, synth.T_X, 0, shape, lo, hi, dtype)
+
+
+def _peers_ints(tag, world, rank, shape, dtype, lo=-64, hi=64):
+    return [None if r == rank else synth.integers(WID_TEST + tag, synth.T_PEER, r, shape, lo, hi, dtype)
+            for r in range(world)]
+
+
+# ------------------------------------------------------------------ fp32 small case
+@pytest.mark.parametrize("split", [1, 2, 4, 8])
+@pytest.mark.parametrize("det", [0, 1])
+def test_toy_fp32_all_reduce_equals_unsplit_layer(split, det):
+    """X 256x512 and W 512x256 uniform[-1,1], K split over tp=2; rank 0 computes
+    K shard 0, the peer partial is K shard 1's product (from the oracle)."""
+    log(f"toy fp32 AR split={split} det={det}")
+    wl = synth.WORKLOADS["toy_f32"]
+    xf = synth.uniform(wl.wid, synth.T_X, 0, (256, 512), -1, 1, "f32")
+    wf = synth.uniform(wl.wid, synth.T_W, 0, (512, 256), -1, 1, "f32")
+    x0, w0 = xf[:, :256].contiguous(), wf[:256].contiguous()
+    p1 = oracle.round_f32(oracle.matmul(f64(xf[:, 256:], "f32"), f64(wf[256:], "f32")))
+    peer = torch.from_numpy(p1.astype(np.float32))
+    y, p = tgc.matmul_all_reduce(dev(x0), dev(w0), [None, dev(peer)], 0, split=split, deterministic=det)
+    torch.cuda.synchronize()
+    full = oracle.matmul(f64(xf, "f32"), f64(wf, "f32"))
+    assert_close(y, full, "f32", "y vs unsplit X_full @ W_full")
+    assert_close(p, oracle.matmul(f64(x0, "f32"), f64(w0, "f32")), "f32", "partial_out")
+
+
+# ------------------------------------------------------------------ exact integer GEMM
+GEMM_SHAPES = [
+    (300, 200, 136),     # ragged in m, n and k
+    (1, 8, 8),
+    (64, 8, 520),
+    (517, 1032, 72),
+    (2048 + 40, 8192, 64),   # 256x256 tiles, ragged m
+    (1024, 8192, 72),        # 256x128 tiles
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+def test_gemm_integer_inputs_bit_exact(dtype, m, n, k):
+    """Small integers: the binary32 accumulation is exact, so partial_out must be
+    the correctly rounded exact product, bit for bit; y (deterministic) must be
+    the fixed-order sum of the stored partials, bit for bit."""
+    log(f"integer GEMM {dtype} m={m} n={n} k={k}")
+    x = _ints(1, (m, k), -4, 4, dtype)
+    w = synth.integers(WID_TEST + 1, synth.T_W, 0, (k, n), -4, 4, dtype)
+    peers = _peers_ints(1, 2, 0, (m, n), dtype)
+    y, p = tgc.matmul_all_reduce(dev(x), dev(w), [None, dev(peers[1])], 0, split=1, deterministic=1)
+    torch.cuda.synchronize()
+    exact = oracle.matmul(f64(x, dtype), f64(w, dtype))
+    assert_bits_equal(p, encode_dtype(exact, dtype), "partial_out")
+    y_ref = oracle.reduce_fixed_order([oracle.round_dtype(exact, dtype), f64(peers[1], dtype)], dtype)
+    assert_bits_equal(y, encode_dtype(y_ref, dtype), "y")
+
+
+def test_gemm_k_zero_gives_zero_partial():
+    log("AR k=0")
+    m, n = 64, 64
+    x = torch.empty((m, 0), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((0, n), dtype=torch.bfloat16, device="cuda")
+    peer = _ints(2, (m, n), -8, 8, "bf16")
+    y, p = tgc.matmul_all_reduce(x, w, [None, dev(peer)], 0, split=2, deterministic=1)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(p.float()).item() == 0
+    assert_bits_equal(y, peer, "y == the peer partial")
+
+
+# ------------------------------------------------------------------ all-reduce, random values
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("split", [1, 2, 4, 8])
+def test_all_reduce_random(dtype, split):
+    log(f"AR random {dtype} split={split}")
+    m, n, k, world, rank = 512, 1032, 520, 8, 3
+    x = synth.normal(WID_TEST + 3, synth.T_X, rank, (m, k), 1.0, dtype)
+    w = synth.normal(WID_TEST + 3, synth.T_W, rank, (k, n), 0.02, dtype)
+    peers = synth.peers_random(WID_TEST + 3, world, rank, (m, n), 0.46, dtype)
+    for det in (0, 1):
+        y, p = tgc.matmul_all_reduce(dev(x), dev(w), [dev(q) for q in peers], rank, split=split,
+                                     deterministic=det)
+        torch.cuda.synchronize()
+        y_ref, p_ref = oracle.matmul_all_reduce(f64(x, dtype), f64(w, dtype),
+                                                [None if q is None else f64(q, dtype) for q in peers], rank)
+        assert_close(p, p_ref, dtype, "partial_out")
+        assert_close(y, y_ref, dtype, f"y det={det}")
+        if det:
+            # deterministic reduction of what is stored, bit for bit
+            parts = [f64(p, dtype) if r == rank else f64(peers[r], dtype) for r in range(world)]
+            assert_bits_equal(y, encode_dtype(oracle.reduce_fixed_order(parts, dtype), dtype), "y det bits")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_deterministic_bits_independent_of_split_and_run(dtype):
+    log(f"AR det invariance {dtype}")
+    m, n, k, world, rank = 256, 512, 264, 8, 6
+    x = synth.normal(WID_TEST + 4, synth.T_X, rank, (m, k), 1.0, dtype)
+    w = synth.normal(WID_TEST + 4, synth.T_W, rank, (k, n), 0.02, dtype)
+    peers = [dev(q) for q in synth.peers_random(WID_TEST + 4, world, rank, (m, n), 0.33, dtype)]
+    xd, wd = dev(x), dev(w)
+    ref = None
+    for split in (1, 2, 4, 8):
+        for run in range(10 if split == 4 else 2):
+            y, p = tgc.matmul_all_reduce(xd, wd, peers, rank, split=split, deterministic=1)
+            torch.cuda.synchronize()
+            if ref is None:
+                ref = (raw(y), raw(p))
+            else:
+                assert_bits_equal(y, ref[0], f"y split={split} run={run}")
+                assert_bits_equal(p, ref[1], f"partial split={split} run={run}")
+
+
+# ------------------------------------------------------------------ reduce-scatter
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("split", [1, 2, 4, 8])
+def test_reduce_scatter(dtype, split):
+    log(f"RS {dtype} split={split}")
+    m, n, k, world, rank = 1024, 520, 264, 8, 5
+    b = m // world
+    x = synth.normal(WID_TEST + 5, synth.T_X, rank, (m, k), 1.0, dtype)
+    w = synth.normal(WID_TEST + 5, synth.T_W, rank, (k, n), 0.02, dtype)
+    peers_full = synth.peers_random(WID_TEST + 5, world, rank, (m, n), 0.33, dtype)
+    # only this rank's slice rows of the peers may be read: poison the rest
+    peers_rs = []
+    for q in peers_full:
+        if q is None:
+            peers_rs.append(None)
+            continue
+        z = torch.full((m, n), float("nan"), dtype=TORCH_DT[dtype])
+        z[rank * b:(rank + 1) * b] = q[rank * b:(rank + 1) * b]
+        peers_rs.append(dev(z))
+    xd, wd = dev(x), dev(w)
+    for det in (0, 1):
+        y, p = tgc.matmul_reduce_scatter(xd, wd, peers_rs, rank, split=split, deterministic=det)
+        torch.cuda.synchronize()
+        assert y.shape == (b, n)
+        y_ref, p_ref = oracle.matmul_reduce_scatter(
+            f64(x, dtype), f64(w, dtype), [None if q is None else f64(q, dtype) for q in peers_full], rank)
+        assert_close(p, p_ref, dtype, "partial_out")
+        assert_close(y, y_ref, dtype, f"y det={det}")
+    # deterministic RS == the same rows of deterministic AR, bit for bit
+    y_ar, _ = tgc.matmul_all_reduce(xd, wd, [dev(q) for q in peers_full], rank, split=split, deterministic=1)
+    y_rs, _ = tgc.matmul_reduce_scatter(xd, wd, peers_rs, rank, split=split, deterministic=1)
+    torch.cuda.synchronize()
+    assert_bits_equal(y_rs, raw(y_ar)[rank * b:(rank + 1) * b], "RS vs AR slice")
+
+
+# ------------------------------------------------------------------ all-gather matmul
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("split", [1, 2, 4, 8])
+@pytest.mark.parametrize("rank", [0, 5])
+def test_allgather_matmul(dtype, split, rank):
+    log(f"AG {dtype} split={split} rank={rank}")
+    world, shard, k, n = 8, 64, 264, 392
+    m = world * shard
+    shards = [synth.normal(WID_TEST + 6, synth.T_PEER, r, (shard, k), 1.0, dtype) for r in range(world)]
+    w = synth.normal(WID_TEST + 6, synth.T_W, 0, (k, n), 0.02, dtype)
+    peers = [None if r == rank else dev(shards[r]) for r in range(world)]
+    xs, wd = dev(shards[rank]), dev(w)
+    y_ref, g_ref = oracle.allgather_matmul([f64(s, dtype) for s in shards], f64(w, dtype))
+    y1 = tgc.allgather_matmul(xs, peers, wd, rank, split=split)
+    y2, g2 = tgc.allgather_matmul(xs, peers, wd, rank, split=split, v2=True)
+    torch.cuda.synchronize()
+    assert_bits_equal(g2, torch.cat(shards), "gathered_out (V2)")
+    assert_close(y1, y_ref, dtype, "y")
+    assert_bits_equal(y2, y1, "V2 y == non-V2 y")
+    if split == 1:
+        return
+    y_s1 = tgc.allgather_matmul(xs, peers, wd, rank, split=1)
+    torch.cuda.synchronize()
+    assert_bits_equal(y1, y_s1, "y independent of split")
+
+
+# ------------------------------------------------------------------ w8a16
+@pytest.mark.parametrize("mode", ["per_tensor", "per_channel", "per_group"])
+@pytest.mark.parametrize("split", [1, 4])
+def test_w8a16_exact_with_power_of_two_scales(mode, split):
+    """X in {-2..2}, q in {-15..15}, scales 2^-6..2^-2 differing per channel and
+    group: every product and the binary32 sums are exact, so partial_out is the
+    correctly rounded exact result, bit for bit, whatever the scale index."""
+    log(f"w8a16 exact {mode} split={split}")
+    m, n, k, g, world, rank = 256, 520, 512, 128, 4, 1
+    x = _ints(7, (m, k), -2, 2, "f16")
+    q = synth.integers(WID_TEST + 7, synth.T_W, 0, (k, n), -15, 15, "i8")
+    shape = {"per_tensor": (1,), "per_channel": (n,), "per_group": (k // g, n)}[mode]
+    s = synth.pow2_scales(WID_TEST + 7, 0, shape)
+    peers = _peers_ints(7, world, rank, (m, n), "f16")
+    y, p = tgc.matmul_all_reduce_w8a16(dev(x), dev(q), dev(s), mode, [dev(t) for t in peers], rank,
+                                       group_size=g, split=split, deterministic=1)
+    torch.cuda.synchronize()
+    exact = oracle.matmul(f64(x, "f16"), oracle.dequant_weight(q.numpy(), f64(s, "f16"), mode, g))
+    assert_bits_equal(p, encode_dtype(exact, "f16"), "partial_out")
+    parts = [oracle.round_dtype(exact, "f16") if r == rank else f64(peers[r], "f16") for r in range(world)]
+    assert_bits_equal(y, encode_dtype(oracle.reduce_fixed_order(parts, "f16"), "f16"), "y")
+
+
+@pytest.mark.parametrize("mode,group", [("per_tensor", 0), ("per_channel", 0), ("per_group", 128),
+                                        ("per_group", 64)])
+def test_w8a16_random(mode, group):
+    log(f"w8a16 random {mode} g={group}")
+    m, n, k, world, rank = 384, 1024, 512, 8, 2
+    x = synth.normal(WID_TEST + 8, synth.T_X, 0, (m, k), 1.0, "f16")
+    q = synth.integers(WID_TEST + 8, synth.T_W, 0, (k, n), -127, 127, "i8")
+    shape = {"per_tensor": (1,), "per_channel": (n,), "per_group": (k // max(group, 1), n)}[mode]
+    s = synth.fp16_scales(WID_TEST + 8, 0, shape)
+    peers = synth.peers_random(WID_TEST + 8, world, rank, (m, n), 20.0, "f16")
+    y, p = tgc.matmul_all_reduce_w8a16(dev(x), dev(q), dev(s), mode, [dev(t) for t in peers], rank,
+                                       group_size=group, split=4, deterministic=0)
+    torch.cuda.synchronize()
+    y_ref, p_ref = oracle.matmul_all_reduce_w8a16(
+        f64(x, "f16"), q.numpy(), f64(s, "f16"), mode, group,
+        [None if t is None else f64(t, "f16") for t in peers], rank)
+    assert_close(p, p_ref, "f16", "partial_out")
+    assert_close(y, y_ref, "f16", "y")
+
+
+# ------------------------------------------------------------------ edge cases and semantics
+def test_world_one_is_plain_matmul():
+    log("AR world=1")
+    x = synth.normal(WID_TEST + 9, synth.T_X, 0, (128, 64), 1.0, "bf16")
+    w = synth.normal(WID_TEST + 9, synth.T_W, 0, (64, 96), 0.02, "bf16")
+    y, p = tgc.matmul_all_reduce(dev(x), dev(w), [None], 0, split=4, deterministic=1)
+    torch.cuda.synchronize()
+    assert_bits_equal(y, p, "y == partial_out")
+    assert_close(p, oracle.matmul(f64(x, "bf16"), f64(w, "bf16")), "bf16", "partial_out")
+
+
+def test_empty_m_is_noop():
+    log("AR m=0")
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    y, p = tgc.matmul_all_reduce(x, w, [None, torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")], 0)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64)
+
+
+def test_outputs_guard_bands_untouched():
+    """Outputs placed inside larger buffers: nothing outside them is written."""
+    log("AR guard bands")
+    m, n, k, world = 256, 264, 128, 4
+    x = synth.normal(WID_TEST + 10, synth.T_X, 0, (m, k), 1.0, "bf16")
+    w = synth.normal(WID_TEST + 10, synth.T_W, 0, (k, n), 0.02, "bf16")
+    peers = [dev(q) for q in synth.peers_random(WID_TEST + 10, world, 0, (m, n), 0.2, "bf16")]
+    pad = 64 * n      # 64 rows of guard on each side (16-byte aligned offsets)
+    ybuf = torch.full((m * n + 2 * pad,), 12345.0, dtype=torch.bfloat16, device="cuda")
+    pbuf = torch.full((m * n + 2 * pad,), -777.0, dtype=torch.bfloat16, device="cuda")
+    y = ybuf[pad:pad + m * n].view(m, n)
+    p = pbuf[pad:pad + m * n].view(m, n)
+    tgc.matmul_all_reduce(dev(x), dev(w), peers, 0, y=y, partial_out=p, split=4, deterministic=1)
+    torch.cuda.synchronize()
+    for buf, val in ((ybuf, 12345.0), (pbuf, -777.0)):
+        assert torch.all(buf[:pad] == val) and torch.all(buf[pad + m * n:] == val)
+    assert_close(p, oracle.matmul(f64(x, "bf16"), f64(w, "bf16")), "bf16", "partial_out")
+
+
+def test_invalid_arguments_enqueue_nothing():
+    log("AR error paths with real tensors")
+    m, n, k = 64, 64, 64
+    x = torch.ones((m + 1, k), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones((k, n), dtype=torch.bfloat16, device="cuda")
+    peers = [None, torch.ones((m, n), dtype=torch.bfloat16, device="cuda")]
+    y = torch.full((m, n), 3.0, dtype=torch.bfloat16, device="cuda")
+    p = torch.full((m, n), 3.0, dtype=torch.bfloat16, device="cuda")
+    # misaligned x (one element into the buffer)
+    xv = x.view(-1)[1:1 + m * k].view(m, k)
+    with pytest.raises(tgc.CocError) as ei:
+        tgc.matmul_all_reduce(xv, w, peers, 0, y=y, partial_out=p)
+    assert ei.value.status_name == "COC_ERR_ALIGN"
+    with pytest.raises(tgc.CocError) as ei:
+        tgc.matmul_all_reduce(x[:m], w, peers, 0, y=y, partial_out=p, split=3)
+    assert ei.value.status_name == "COC_ERR_SPLIT"
+    with pytest.raises(tgc.CocError) as ei:
+        tgc.matmul_all_reduce(x[:m], w, peers, 0, y=y, partial_out=y)
+    assert ei.value.status_name == "COC_ERR_ALIAS"
+    torch.cuda.synchronize()
+    assert torch.all(y == 3.0) and torch.all(p == 3.0)
+
+
+def test_stream_order_without_host_sync():
+    """Outputs are visible to later work on the caller's stream with no host sync."""
+    log("stream semantics")
+    m, n, k, world = 512, 512, 256, 8
+    x = dev(synth.normal(WID_TEST + 11, synth.T_X, 0, (m, k), 1.0, "bf16"))
+    w = dev(synth.normal(WID_TEST + 11, synth.T_W, 0, (k, n), 0.02, "bf16"))
+    peers = [dev(q) for q in synth.peers_random(WID_TEST + 11, world, 0, (m, n), 0.3, "bf16")]
+    y_ref, _ = tgc.matmul_all_reduce(x, w, peers, 0, split=4, deterministic=1)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        outs = []
+        for _ in range(4):
+            y, _ = tgc.matmul_all_reduce(x, w, peers, 0, split=4, deterministic=1)
+            outs.append(y.clone())       # consumer on the same stream, no sync
+            y.fill_(0)
+    s.synchronize()
+    for o in outs:
+        assert_bits_equal(o, y_ref, "consumer on caller stream")
