@@ -129,7 +129,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--split", type=int, default=4, choices=[1, 2, 4, 8])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-frac", type=float, default=0.25)
+    ap.add_argument("--cpu-frac", type=float, default=1.0)
     args = ap.parse_args()
 
     world_env = int(os.environ.get("WORLD_SIZE", "1"))
