@@ -27,7 +27,7 @@ HOST_SOURCES = ["coc_plan.cpp", "coc_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{HERE}"]
 # Device code: gfx950 only, packed-fp32 instructions disabled.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-Wno-unused-command-line-argument"]
+          "-Wno-unused-command-line-argument", "-Wno-inline-asm"]
 
 
 def hipcc() -> str:

@@ -1,9 +1,11 @@
 // gfx950 kernels of the fused matmul + collective path.
 //
-//   gemm_mfma   m-chunk matmul, bf16 / fp16 inputs (or int8 weights dequantised
-//               to fp16 in the main loop), binary32 accumulation on MFMA,
+//   gemm_dma    m-chunk matmul, bf16 / fp16 inputs, direct-to-LDS loads and
+//               LDS transpose reads, binary32 accumulation on MFMA,
 //               round-to-nearest-even to the storage dtype.  The "Matmul" of
 //               the CoC guide's matmul/collective pairs ("Problem analysis").
+//   gemm_w8     the same with int8 weights dequantised to fp16 in the main
+//               loop (w8A16).
 //   gemm_f32    the same for binary32 inputs on the vector ALUs.
 //   reduce_rows fixed-order sum of the ranks' partials for a block of rows:
 //               the AllReduce / ReduceScatter half of a pair.
@@ -13,6 +15,8 @@
 // Every kernel takes fully validated sizes; all global accesses are guarded by
 // the row / column / k bounds passed in.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "coc_internal.h"
 
@@ -88,22 +92,15 @@ struct GemmParams {
     int32_t qmode, group;
 };
 
-// ------------------------------------------------------------------ MFMA GEMM
-// Tile BM x BN x 64, 256 threads as 2 x 2 waves, each wave BM/2 x BN/2 made of
-// 32x32 MFMA blocks (v_mfma_f32_32x32x16_{bf16,f16}).
-//
-// Both operands sit in LDS K-contiguous: A as [BM rows][64 k], the weight as
-// [BN columns][64 k] (W is k x n row-major in memory, so each thread loads an
-// 8 k x 8 n block with 16-byte row loads and transposes it in registers before
-// the LDS store).  The 16-byte chunk c of LDS row `row` is stored at position
-// c ^ swz(row), which keeps both the row-wise stores and the MFMA operand
-// reads of 8 consecutive lanes on distinct banks.
-//
-// The MFMA computes C^T = W^T X^T: operand A is the weight fragment (32
-// columns n), operand B the activation fragment (32 rows m).  Each lane then
-// holds 4 consecutive n of one row m per 32x32 block, written as one 8-byte
-// store.  The k ordering inside one MFMA step is the same for every tile
-// shape, so the bits of an output element do not depend on BM / BN.
+// ------------------------------------------------------------------ MFMA GEMMs
+// Both GEMM kernels compute C^T = W^T X^T on v_mfma_f32_32x32x16_{bf16,f16}:
+// MFMA operand A is a weight fragment (lane l: column n = l % 32, 8 k values
+// (l / 32) * 8 + 0..7 of the current 16-k step), operand B an activation
+// fragment (lane l: row m = l % 32, the same 8 k values).  Each lane then
+// holds 4 consecutive n of one row m per 32x32 block (one 8-byte store).
+// Every kernel and tile shape walks k in the same 16-k steps in increasing
+// order, so the bits of an output element depend neither on the tile shape
+// nor on the kernel that produced it.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 template <int KIND>
@@ -116,8 +113,15 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// Register-staged kernel for int8 weights (w8A16): tile BM x BN x 64, 256
+// threads as 2 x 2 waves.  Each thread loads an 8 k x 8 n block of int8
+// weights, dequantises it to fp16 (q * scale, rounded to nearest even) in
+// registers and stores it K-contiguous to LDS ([BN columns][64 k]); A goes to
+// LDS as [BM rows][64 k].  The 16-byte chunk c of an LDS row sits at
+// c ^ swz(row), which keeps the row stores and the MFMA operand reads of 8
+// consecutive lanes on distinct banks.
 template <int BM, int BN, int KIND>
-__global__ __launch_bounds__(256) void gemm_mfma(GemmParams p) {
+__global__ __launch_bounds__(256) void gemm_w8(GemmParams p) {
     constexpr int BK = 64;
     constexpr int NT = 256;
     constexpr int WTM = BM / 2, WTN = BN / 2;
@@ -313,6 +317,262 @@ __global__ __launch_bounds__(256) void gemm_mfma(GemmParams p) {
     }
 }
 
+// Direct-to-LDS kernel for bf16 / fp16 (gfx950).  Tile BM x BN, k in stages
+// of 32, an LDS ring of STAGES stages, 64 * WM * WN threads (WM x WN waves,
+// wave tile BM/WM x BN/WN).
+//
+//   * Both operands go from global memory straight into LDS with 16-byte
+//     global_load_lds_dwordx4 (lane L of a wave-instruction lands at byte
+//     16 * L of a 1 KB LDS block); no VGPR staging, no LDS store instructions.
+//     Each lane picks the global chunk that belongs at its LDS slot, which is
+//     how the XOR swizzles below are applied.
+//   * A (X rows, k-contiguous) is stored [BM rows][32 k], 64 B per row; chunk c
+//     of row r sits at c ^ gA(r), so the 16-byte MFMA operand reads of 16
+//     consecutive rows hit distinct banks.
+//   * The weight (k x n row-major in memory) is stored as it comes, [32 k][BN
+//     n]; chunk c of k-row K sits at c ^ gB(K).  The MFMA fragment (lane l:
+//     column l % 32, 8 consecutive k) is read with two ds_read_b64_tr_b16: in
+//     each 16-lane group, lane i receives element i % 4 of the 8-byte chunks
+//     addressed by lanes 4j + i / 4 (j = 0..3), so lane 4j + q pointing at
+//     k-row K0 + j, columns n0 + 4q .. n0 + 4q + 3 hands lane i column n0 + i
+//     at k-rows K0 .. K0 + 3.
+//   * Lanes outside the matrix (m, n or k tail) load 16 zero bytes from a
+//     device constant instead, so every wave issues the same number of loads
+//     per stage and vmcnt counts stay exact; the k tail is zero-filled this way.
+//   * Per stage: read the second half's fragments, run the first half's MFMAs,
+//     wait for this wave's loads of the next stage, barrier, issue the loads of
+//     stage kt + STAGES - 1 into the slot every wave has finished with, read
+//     the next stage's first fragments, run the second half's MFMAs.  The DMA
+//     loads are issued through inline asm so the compiler does not order every
+//     LDS read behind them; the explicit vmcnt wait + s_barrier is the ordering.
+__device__ const u32x4 g_zero16 = {0, 0, 0, 0};
+
+#define COC_LDS __attribute__((address_space(3)))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int gA32(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
+__device__ __forceinline__ int gB32(int K) { return (K & 3) << 2; }
+
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(const COC_LDS void*)p;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int KIND>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
+    constexpr int NW = WM * WN;
+    constexpr int BK = 32;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int A_INS = A_BYTES / 1024, B_INS = B_BYTES / 1024;
+    static_assert(A_INS % NW == 0 && B_INS % NW == 0, "loads must split evenly over waves");
+    static_assert(BN % 128 == 0, "B swizzle works on 16-chunk groups");
+    static_assert(STAGES == 3 || STAGES == 4, "stage ring");
+    constexpr int APW = A_INS / NW, BPW = B_INS / NW, LPW = APW + BPW;
+    constexpr int BROW = BN / 8;   // 16-byte chunks per weight k-row
+    constexpr int OUT_DT = (KIND == GK_BF16) ? COC_BF16 : COC_F16;
+    __shared__ __attribute__((aligned(1024))) uint8_t sm0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm2[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm3[STAGES == 4 ? STAGE : 16];
+    auto stage = [&](auto S) -> uint8_t* {
+        constexpr int s_ = decltype(S)::value;
+        if constexpr (s_ == 0) return sm0;
+        else if constexpr (s_ == 1) return sm1;
+        else if constexpr (s_ == 2) return sm2;
+        else return sm3;
+    };
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int tm = blockIdx.x % p.tiles_m, tn = blockIdx.x / p.tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // global sources of this wave's loads (row map applied once)
+    const uint8_t* asrc[APW];
+    int akof[APW];
+    bool aok[APW];
+#pragma unroll
+    for (int i = 0; i < APW; ++i) {
+        const int q = (wave * APW + i) * 64 + lane;
+        const int row = q >> 2;
+        aok[i] = m0 + row < p.rows;
+        const int64_t gr = aok[i] ? map_row(m0 + row, p.rpb, p.base, p.stride) : 0;
+        asrc[i] = p.a + gr * (int64_t)p.k * 2;
+        akof[i] = ((q & 3) ^ gA32(row)) * 8;
+    }
+    const uint8_t* bsrc[BPW];
+    int bkr[BPW];
+    bool bok[BPW];
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+        const int q = (wave * BPW + i) * 64 + lane;
+        const int K = q / BROW;
+        const int col = n0 + ((q % BROW) ^ gB32(K)) * 8;
+        bok[i] = col < p.n;
+        bkr[i] = K;
+        bsrc[i] = p.b + (int64_t)(bok[i] ? col : 0) * 2;
+    }
+    const uint8_t* zero = (const uint8_t*)&g_zero16;
+
+    auto issue = [&](int kt, auto S) {
+        const int k0 = kt * BK;
+        uint8_t* st = stage(S);
+#pragma unroll
+        for (int i = 0; i < APW; ++i) {
+            const uint8_t* src =
+                (aok[i] && k0 + akof[i] < p.k) ? asrc[i] + (int64_t)(k0 + akof[i]) * 2 : zero;
+            dma16(src, lds_u32(st + (wave * APW + i) * 1024));
+        }
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) {
+            const uint8_t* src =
+                (bok[i] && k0 + bkr[i] < p.k) ? bsrc[i] + (int64_t)(k0 + bkr[i]) * p.n * 2 : zero;
+            dma16(src, lds_u32(st + A_BYTES + (wave * BPW + i) * 1024));
+        }
+    };
+
+    // fragment offsets within a stage
+    int aoff[2][FM];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * WTM + i * 32 + (lane & 31);
+            aoff[ks][i] = row * 64 + (((ks * 2 + (lane >> 5)) ^ gA32(row)) << 4);
+        }
+    int boff[2][2][FN];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int r = lane & 15, grp = (lane >> 4) & 1, hk = lane >> 5;
+                const int K = ks * 16 + hk * 8 + h * 4 + (r >> 2);
+                const int col = wn * WTN + j * 32 + grp * 16 + 4 * (r & 3);
+                boff[ks][h][j] = A_BYTES + K * BN * 2 + (((col >> 3) ^ gB32(K)) << 4) + (col & 7) * 2;
+            }
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    auto rd = [&](const COC_LDS uint8_t* st, int ks, u32x4* af, u32x4* bf) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = *(const COC_LDS u32x4*)(st + aoff[ks][i]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((COC_LDS s16x4*)(st + boff[ks][0][j]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((COC_LDS s16x4*)(st + boff[ks][1][j]));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            bf[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        }
+    };
+    auto mm = [&](const u32x4* af, const u32x4* bf) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<KIND>(bf[j], af[i], acc[i][j]);
+    };
+
+    const int KT = (p.k + BK - 1) / BK;
+    std::integral_constant<int, 0> S0;
+    std::integral_constant<int, 1> S1;
+    std::integral_constant<int, 2> S2;
+    std::integral_constant<int, 3> S3;
+    if (0 < KT) issue(0, S0);
+    if (1 < KT) issue(1, S1);
+    if constexpr (STAGES == 4) {
+        if (2 < KT) issue(2, S2);
+    }
+    u32x4 a0[FM], b0[FN], a1[FM], b1[FN];
+    if (KT > 0) {
+        if constexpr (STAGES == 4) {
+            if (KT > 2) wait_vmcnt<2 * LPW>();
+            else if (KT > 1) wait_vmcnt<LPW>();
+            else wait_vmcnt<0>();
+        } else {
+            if (KT > 1) wait_vmcnt<LPW>();
+            else wait_vmcnt<0>();
+        }
+        block_barrier();
+        rd((const COC_LDS uint8_t*)stage(S0), 0, a0, b0);
+    }
+    auto body = [&](int kt, auto S) {
+        constexpr int cs = decltype(S)::value;
+        rd((const COC_LDS uint8_t*)stage(S), 1, a1, b1);
+        mm(a0, b0);
+        if (kt + 1 < KT) {
+            // this wave's loads of stage kt + 1 are done; later stages may stay in flight
+            if constexpr (STAGES == 4) {
+                if (kt + 2 < KT) wait_vmcnt<LPW>();
+                else wait_vmcnt<0>();
+            } else {
+                wait_vmcnt<0>();
+            }
+        }
+        block_barrier();
+        if (kt + STAGES - 1 < KT)
+            issue(kt + STAGES - 1, std::integral_constant<int, (cs + STAGES - 1) % STAGES>{});
+        if (kt + 1 < KT)
+            rd((const COC_LDS uint8_t*)stage(std::integral_constant<int, (cs + 1) % STAGES>{}), 0, a0, b0);
+        mm(a1, b1);
+    };
+    for (int kt = 0; kt < KT; kt += STAGES) {
+        body(kt, S0);
+        if (kt + 1 < KT) body(kt + 1, S1);
+        if (kt + 2 < KT) body(kt + 2, S2);
+        if constexpr (STAGES == 4) {
+            if (kt + 3 < KT) body(kt + 3, S3);
+        }
+    }
+
+    // ---- epilogue: lane holds n = q*8 + (lane/32)*4 + {0..3} of row m = lane%32
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int r = m0 + wm * WTM + i * 32 + (lane & 31);
+        if (r >= p.rows) continue;
+        const int64_t gr = map_row(r, p.rpb, p.base, p.stride);
+        uint8_t* crow = p.c + gr * (int64_t)p.n * 2;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
+                if (col < p.n) {
+                    u32x2 v;
+                    v[0] = pack2<OUT_DT>(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+                    v[1] = pack2<OUT_DT>(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+                    *(u32x2*)(crow + (int64_t)col * 2) = v;
+                }
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ fp32 GEMM
 // 64 x 64 x 16 tiles, 256 threads, 4 x 4 outputs per thread, fused
 // multiply-add in k order (binary32 throughout).
@@ -472,25 +732,41 @@ int grid_for(int64_t total_vec) {
     return (int)(want < cap ? (want > 0 ? want : 1) : cap);
 }
 
-template <int BM, int BN, int KIND>
-hipError_t launch_mfma(GemmParams p, hipStream_t s) {
+template <int BM, int BN>
+hipError_t launch_w8(GemmParams p, hipStream_t s) {
     p.tiles_m = (p.rows + BM - 1) / BM;
     p.tiles_n = (p.n + BN - 1) / BN;
-    const int blocks = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((gemm_mfma<BM, BN, KIND>), dim3(blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_w8<BM, BN, GK_W8_F16>), dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_w8_any(GemmParams p, hipStream_t s) {
+    const int64_t t256 = ((p.rows + 255) / 256) * ((p.n + 255) / 256);
+    const int64_t t256x128 = ((p.rows + 255) / 256) * ((p.n + 127) / 128);
+    if (t256 >= 256) return launch_w8<256, 256>(p, s);
+    if (t256x128 >= 256) return launch_w8<256, 128>(p, s);
+    return launch_w8<128, 128>(p, s);
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int KIND>
+hipError_t launch_dma(GemmParams p, hipStream_t s) {
+    p.tiles_m = (p.rows + BM - 1) / BM;
+    p.tiles_n = (p.n + BN - 1) / BN;
+    hipLaunchKernelGGL((gemm_dma<BM, BN, WM, WN, STAGES, KIND>), dim3(p.tiles_m * p.tiles_n),
+                       dim3(64 * WM * WN), 0, s, p);
     return hipGetLastError();
 }
 
 template <int KIND>
-hipError_t launch_mfma_kind(GemmParams p, hipStream_t s) {
-    // Tile shape: the largest tile that still gives every compute unit a
-    // workgroup for this chunk.  All shapes share the k loop, so the choice
-    // never changes the result bits.
+hipError_t launch_dma_kind(GemmParams p, hipStream_t s) {
+    // Tile shape: the largest tile that still gives (nearly) every compute
+    // unit a workgroup for this chunk.  All shapes share the k loop, so the
+    // choice never changes the result bits.
     const int64_t t256 = ((p.rows + 255) / 256) * ((p.n + 255) / 256);
     const int64_t t256x128 = ((p.rows + 255) / 256) * ((p.n + 127) / 128);
-    if (t256 >= 256) return launch_mfma<256, 256, KIND>(p, s);
-    if (t256x128 >= 256) return launch_mfma<256, 128, KIND>(p, s);
-    return launch_mfma<128, 128, KIND>(p, s);
+    if (t256 >= 256) return launch_dma<256, 256, 2, 4, 3, KIND>(p, s);
+    if (t256x128 >= 224) return launch_dma<256, 128, 4, 2, 4, KIND>(p, s);
+    return launch_dma<128, 128, 2, 2, 4, KIND>(p, s);
 }
 
 }  // namespace
@@ -519,9 +795,9 @@ int launch_gemm(const GemmLaunch& g, void* stream) {
             hipLaunchKernelGGL(gemm_f32, dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
             return hipGetLastError();
         }
-        case GK_F16: return launch_mfma_kind<GK_F16>(p, s);
-        case GK_BF16: return launch_mfma_kind<GK_BF16>(p, s);
-        case GK_W8_F16: return launch_mfma_kind<GK_W8_F16>(p, s);
+        case GK_F16: return launch_dma_kind<GK_F16>(p, s);
+        case GK_BF16: return launch_dma_kind<GK_BF16>(p, s);
+        case GK_W8_F16: return launch_w8_any(p, s);
     }
     return hipErrorInvalidValue;
 }
