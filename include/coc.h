@@ -251,6 +251,15 @@ coc_status coc_plan(coc_op op, int64_t m, int32_t world, int32_t rank, int32_t s
 void coc_profile_enable(int32_t on);
 coc_status coc_profile_read(double* total_ms, int64_t* launches, double* work_units);
 
+/* Per-launch view of the same record: for each recorded launch, in issue
+ * order, its kernel class, start and end in ms relative to the start of the
+ * first recorded launch, and its algorithmic work.  Fills at most `max`
+ * entries, sets *n to the number of records, and clears the record (like
+ * coc_profile_read; use one or the other).  Overlapping intervals mean the
+ * launches ran concurrently. */
+coc_status coc_profile_records(int32_t* kclass, double* start_ms, double* end_ms, double* work_units,
+                               int32_t max, int32_t* n);
+
 #ifdef __cplusplus
 }
 #endif

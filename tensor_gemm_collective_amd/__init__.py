@@ -19,4 +19,5 @@ from .coc import (  # noqa: F401
     plan,
     profile_enable,
     profile_read,
+    profile_records,
 )

@@ -34,7 +34,7 @@ KCLASS = ("gemm", "reduce", "gather")
 EXPORTS = (
     "coc_matmul_all_reduce", "coc_matmul_reduce_scatter", "coc_allgather_matmul",
     "coc_matmul_all_reduce_w8a16", "coc_workspace_bytes", "coc_status_string",
-    "coc_last_error", "coc_plan", "coc_profile_enable", "coc_profile_read",
+    "coc_last_error", "coc_plan", "coc_profile_enable", "coc_profile_read", "coc_profile_records",
 )
 
 
@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
     L.coc_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64),
                                    ctypes.POINTER(ctypes.c_double)]
     L.coc_profile_read.restype = _i32
+    dp = ctypes.POINTER(ctypes.c_double)
+    L.coc_profile_records.argtypes = [ctypes.POINTER(_i32), dp, dp, dp, _i32, ctypes.POINTER(_i32)]
+    L.coc_profile_records.restype = _i32
     _lib = L
     return L
 
@@ -231,3 +234,14 @@ def profile_read():
     work = (ctypes.c_double * 3)()
     _check(lib().coc_profile_read(ms, cnt, work))
     return {KCLASS[i]: {"ms": ms[i], "launches": cnt[i], "work": work[i]} for i in range(3)}
+
+
+def profile_records(max_records: int = 1 << 16):
+    """Per-launch (class, start ms, end ms, work) records since the last read."""
+    cls = (_i32 * max_records)()
+    t0 = (ctypes.c_double * max_records)()
+    t1 = (ctypes.c_double * max_records)()
+    work = (ctypes.c_double * max_records)()
+    n = _i32(0)
+    _check(lib().coc_profile_records(cls, t0, t1, work, max_records, ctypes.byref(n)))
+    return [(KCLASS[cls[i]], t0[i], t1[i], work[i]) for i in range(min(n.value, max_records))]

@@ -6,14 +6,17 @@
 // sub-tasks that run as a pipeline; Overlap blog, "core idea": cut both small
 // and let them hide each other):
 //   compute-first ops (all-reduce, reduce-scatter, w8a16 all-reduce):
-//       caller stream:  gemm[0]  gemm[1]  gemm[2] ...
-//       side stream:           reduce[0] reduce[1] ...   (reduce[i] waits on gemm[i])
+//       compute streams: gemm[0] gemm[1] gemm[2] ...  (alternating caller / 2nd stream)
+//       comm stream:            reduce[0] reduce[1] ...  (reduce[i] waits on gemm[i])
 //   communicate-first ops (all-gather matmul, V2):
-//       side stream:    gather[0] gather[1] gather[2] ...
-//       caller stream:            gemm[0]   gemm[1]  ... (gemm[i] waits on gather[i])
-// The side stream is forked from and joined back into the caller's stream
-// with events, so the call is ordered like a single kernel on that stream.
-// split == 1 is the serial baseline: everything on the caller's stream.
+//       comm stream:     gather[0] gather[1] gather[2] ...
+//       compute streams:          gemm[0]   gemm[1]  ...  (gemm[i] waits on gather[i])
+// The chunk matmuls do not depend on each other, so consecutive chunks go to
+// two compute streams and the next chunk's workgroups fill the compute units
+// the previous chunk's last wave leaves idle.  The library streams are forked
+// from and joined back into the caller's stream with events, so a call is
+// ordered like a single kernel on that stream.  split == 1 is the serial
+// baseline: everything on the caller's stream.
 #include <hip/hip_runtime_api.h>
 
 #include <atomic>
@@ -48,10 +51,12 @@ coc_status hip_fail(hipError_t e, const char* what) {
 // are created with the default priority and never destroyed (the process
 // owns them until exit).
 struct StreamCtx {
-    hipStream_t side = nullptr;
+    hipStream_t side = nullptr;    // reduce / gather
+    hipStream_t gemm2 = nullptr;   // second compute stream
     hipEvent_t ev[COC_MAX_SPLIT] = {};
     hipEvent_t fork = nullptr;
     hipEvent_t join = nullptr;
+    hipEvent_t join2 = nullptr;
 };
 
 std::mutex g_ctx_mu;
@@ -69,9 +74,11 @@ coc_status get_ctx(hipStream_t main, StreamCtx** out) {
     }
     StreamCtx* c = new StreamCtx;
     COC_HIP(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
+    COC_HIP(hipStreamCreateWithFlags(&c->gemm2, hipStreamNonBlocking));
     for (auto& e : c->ev) COC_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
     COC_HIP(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming));
     COC_HIP(hipEventCreateWithFlags(&c->join, hipEventDisableTiming));
+    COC_HIP(hipEventCreateWithFlags(&c->join2, hipEventDisableTiming));
     g_ctx[key] = c;
     *out = c;
     return COC_OK;
@@ -189,9 +196,9 @@ double gemm_flops(const Plan& P, const coc_chunk& c) {
 coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLaunch& r0,
                              hipStream_t main) {
     const size_t es = elem_size(P.dt);
-    auto gemm = [&](int i) {
+    auto gemm = [&](int i, hipStream_t s) {
         const GemmLaunch g = gemm_for_chunk(g0, P.chunk[i]);
-        return launch(KC_GEMM, gemm_flops(P, P.chunk[i]), main, [&] { return launch_gemm(g, main); });
+        return launch(KC_GEMM, gemm_flops(P, P.chunk[i]), s, [&] { return launch_gemm(g, s); });
     };
     auto reduce = [&](int i, hipStream_t s) {
         ReduceLaunch r = r0;
@@ -202,17 +209,22 @@ coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLa
         return launch(KC_REDUCE, bytes, s, [&] { return launch_reduce(r, s); });
     };
     if (P.split == 1) {
-        COC_TRY(gemm(0));
+        COC_TRY(gemm(0, main));
         return reduce(0, main);
     }
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
+    COC_HIP(hipEventRecord(c->fork, main));
+    COC_HIP(hipStreamWaitEvent(c->gemm2, c->fork, 0));
     for (int i = 0; i < P.nchunks; ++i) {
-        COC_TRY(gemm(i));
-        COC_HIP(hipEventRecord(c->ev[i], main));
+        hipStream_t cs = (i & 1) ? c->gemm2 : main;
+        COC_TRY(gemm(i, cs));
+        COC_HIP(hipEventRecord(c->ev[i], cs));
         COC_HIP(hipStreamWaitEvent(c->side, c->ev[i], 0));
         COC_TRY(reduce(i, c->side));
     }
+    COC_HIP(hipEventRecord(c->join2, c->gemm2));
+    COC_HIP(hipStreamWaitEvent(main, c->join2, 0));
     COC_HIP(hipEventRecord(c->join, c->side));
     COC_HIP(hipStreamWaitEvent(main, c->join, 0));
     return COC_OK;
@@ -229,24 +241,31 @@ coc_status run_comm_first(const Plan& P, const GemmLaunch& g0, const GatherLaunc
         const double bytes = 2.0 * double(a.rows) * double(P.k) * double(es);
         return launch(KC_GATHER, bytes, s, [&] { return launch_gather(a, s); });
     };
-    auto gemm = [&](int i) {
+    auto gemm = [&](int i, hipStream_t s) {
         const GemmLaunch g = gemm_for_chunk(g0, P.chunk[i]);
-        return launch(KC_GEMM, gemm_flops(P, P.chunk[i]), main, [&] { return launch_gemm(g, main); });
+        return launch(KC_GEMM, gemm_flops(P, P.chunk[i]), s, [&] { return launch_gemm(g, s); });
     };
     if (P.split == 1) {
         COC_TRY(gather(0, main));
-        return gemm(0);
+        return gemm(0, main);
     }
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
     COC_HIP(hipEventRecord(c->fork, main));
     COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
+    COC_HIP(hipStreamWaitEvent(c->gemm2, c->fork, 0));
     for (int i = 0; i < P.nchunks; ++i) {
+        hipStream_t cs = (i & 1) ? c->gemm2 : main;
         COC_TRY(gather(i, c->side));
         COC_HIP(hipEventRecord(c->ev[i], c->side));
-        COC_HIP(hipStreamWaitEvent(main, c->ev[i], 0));
-        COC_TRY(gemm(i));
+        COC_HIP(hipStreamWaitEvent(cs, c->ev[i], 0));
+        COC_TRY(gemm(i, cs));
     }
+    // main has waited for the gather of every chunk it ran; gemm2 holds the rest
+    COC_HIP(hipEventRecord(c->join2, c->gemm2));
+    COC_HIP(hipStreamWaitEvent(main, c->join2, 0));
+    COC_HIP(hipEventRecord(c->join, c->side));
+    COC_HIP(hipStreamWaitEvent(main, c->join, 0));
     return COC_OK;
 }
 
@@ -439,6 +458,46 @@ coc_status coc_profile_read(double* total_ms, int64_t* launches, double* work_un
         if (total_ms) total_ms[i] = ms[i];
         if (launches) launches[i] = cnt[i];
         if (work_units) work_units[i] = work[i];
+    }
+    return st;
+}
+
+coc_status coc_profile_records(int32_t* kclass, double* start_ms, double* end_ms, double* work_units,
+                               int32_t max, int32_t* n) {
+    clear_error();
+    std::vector<ProfRec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        recs.swap(g_prof_recs);
+    }
+    coc_status st = COC_OK;
+    if (!n) st = fail(COC_ERR_NULL, "n is NULL");
+    int32_t k = 0;
+    for (size_t i = 0; i < recs.size() && st == COC_OK; ++i) {
+        const ProfRec& r = recs[i];
+        float t0 = 0.f, t1 = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t0, recs[0].a, r.a);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t1, recs[0].a, r.b);
+        if (e != hipSuccess) {
+            st = hip_fail(e, "hipEventElapsedTime");
+            break;
+        }
+        if (k < max) {
+            if (kclass) kclass[k] = r.cls;
+            if (start_ms) start_ms[k] = t0;
+            if (end_ms) end_ms[k] = t1;
+            if (work_units) work_units[k] = r.work;
+        }
+        ++k;
+    }
+    if (n) *n = k;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        for (const ProfRec& r : recs) {
+            g_prof_pool.push_back(r.a);
+            g_prof_pool.push_back(r.b);
+        }
     }
     return st;
 }

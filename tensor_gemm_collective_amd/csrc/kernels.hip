@@ -92,6 +92,18 @@ struct GemmParams {
     int32_t qmode, group;
 };
 
+// ------------------------------------------------------------------ tile order
+// Workgroups are handed to the 8 XCDs (each with its own L2) round-robin by
+// id.  This bijection gives XCD x a contiguous run of tile numbers, and tile
+// numbers run m-fastest, so the tiles sharing a weight column block sit on
+// one XCD and that block is fetched into one L2 instead of several.
+__device__ __forceinline__ int xcd_tile(int b, int total) {
+    constexpr int NX = 8;
+    const int q = total / NX, r = total % NX;
+    const int x = b % NX, local = b / NX;
+    return x * q + (x < r ? x : r) + local;
+}
+
 // ------------------------------------------------------------------ MFMA GEMMs
 // Both GEMM kernels compute C^T = W^T X^T on v_mfma_f32_32x32x16_{bf16,f16}:
 // MFMA operand A is a weight fragment (lane l: column n = l % 32, 8 k values
@@ -138,9 +150,9 @@ __global__ __launch_bounds__(256) void gemm_w8(GemmParams p) {
     const int wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    const int bid = blockIdx.x;
-    const int tm = bid % p.tiles_m;
-    const int tn = bid / p.tiles_m;
+    const int tile = xcd_tile(blockIdx.x, p.tiles_m * p.tiles_n);
+    const int tm = tile % p.tiles_m;
+    const int tn = tile / p.tiles_m;
     const int m0 = tm * BM, n0 = tn * BN;
 
     // ---- A rows handled by this thread (row map evaluated once)
@@ -403,7 +415,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int tm = blockIdx.x % p.tiles_m, tn = blockIdx.x / p.tiles_m;
+    const int tile = xcd_tile(blockIdx.x, p.tiles_m * p.tiles_n);
+    const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
     const int m0 = tm * BM, n0 = tn * BN;
 
     // global sources of this wave's loads (row map applied once)
@@ -648,47 +661,69 @@ struct ReduceParams {
     int32_t total;       // rows * vpr
 };
 
+// Two sources are loaded at a time and added in rank order before the next
+// pair is fetched (scheduling fences keep the compiler from hoisting all
+// loads), which keeps the kernel at 32 VGPRs or fewer: the 256x256 matmul
+// leaves about that much per SIMD lane free, so reduce waves can share a
+// compute unit with a running matmul instead of waiting for it to drain.
+template <int DT>
+__device__ __forceinline__ void acc_add(float* acc, u32x4 x) {
+    if constexpr (DT == COC_F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = acc[e] + __uint_as_float(x[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = acc[2 * e] + unpack_lo<DT>(x[e]);
+            acc[2 * e + 1] = acc[2 * e + 1] + unpack_hi<DT>(x[e]);
+        }
+    }
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void reduce_rows(ReduceParams p) {
+    constexpr int E = (DT == COC_F32) ? 4 : 8;
     const int stride = gridDim.x * 256;
     for (int v = blockIdx.x * 256 + threadIdx.x; v < p.total; v += stride) {
         const int row = v / p.vpr;
         const int cv = v - row * p.vpr;
         const int64_t so = (p.src_row0 + row) * p.row_bytes + (int64_t)cv * 16;
         const int64_t dof = (p.dst_row0 + row) * p.row_bytes + (int64_t)cv * 16;
-        u32x4 x[COC_MAX_WORLD];
+        // binary32 left-to-right sum of the sources in rank order: acc = src0,
+        // then acc += src1, acc += src2, ...
+        float acc[E];
+        {
+            const u32x4 x0 = *(const u32x4*)(p.src[0] + so);
+            u32x4 x1 = {0, 0, 0, 0};
+            if (p.nsrc > 1) x1 = *(const u32x4*)(p.src[1] + so);
+            if constexpr (DT == COC_F32) {
 #pragma unroll
-        for (int s = 0; s < COC_MAX_WORLD; ++s)
-            if (s < p.nsrc) x[s] = *(const u32x4*)(p.src[s] + so);
+                for (int e = 0; e < 4; ++e) acc[e] = __uint_as_float(x0[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] = unpack_lo<DT>(x0[e]);
+                    acc[2 * e + 1] = unpack_hi<DT>(x0[e]);
+                }
+            }
+            if (p.nsrc > 1) acc_add<DT>(acc, x1);
+        }
+#pragma unroll
+        for (int s = 2; s < COC_MAX_WORLD; s += 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (s < p.nsrc) {
+                const u32x4 x0 = *(const u32x4*)(p.src[s] + so);
+                u32x4 x1 = {0, 0, 0, 0};
+                if (s + 1 < p.nsrc) x1 = *(const u32x4*)(p.src[s + 1] + so);
+                acc_add<DT>(acc, x0);
+                if (s + 1 < p.nsrc) acc_add<DT>(acc, x1);
+            }
+        }
         u32x4 out;
         if constexpr (DT == COC_F32) {
-            f32x4 acc = __builtin_bit_cast(f32x4, x[0]);
 #pragma unroll
-            for (int s = 1; s < COC_MAX_WORLD; ++s) {
-                if (s < p.nsrc) {
-                    const f32x4 y = __builtin_bit_cast(f32x4, x[s]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = acc[e] + y[e];
-                }
-            }
-            out = __builtin_bit_cast(u32x4, acc);
+            for (int e = 0; e < 4; ++e) out[e] = __float_as_uint(acc[e]);
         } else {
-            float acc[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = unpack_lo<DT>(x[0][e]);
-                acc[2 * e + 1] = unpack_hi<DT>(x[0][e]);
-            }
-#pragma unroll
-            for (int s = 1; s < COC_MAX_WORLD; ++s) {
-                if (s < p.nsrc) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc[2 * e] = acc[2 * e] + unpack_lo<DT>(x[s][e]);
-                        acc[2 * e + 1] = acc[2 * e + 1] + unpack_hi<DT>(x[s][e]);
-                    }
-                }
-            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) out[e] = pack2<DT>(acc[2 * e], acc[2 * e + 1]);
         }
@@ -759,13 +794,14 @@ hipError_t launch_dma(GemmParams p, hipStream_t s) {
 
 template <int KIND>
 hipError_t launch_dma_kind(GemmParams p, hipStream_t s) {
-    // Tile shape: the largest tile that still gives (nearly) every compute
-    // unit a workgroup for this chunk.  All shapes share the k loop, so the
-    // choice never changes the result bits.
+    // Tile shape: the largest tile that still gives at least about half of the
+    // 256 compute units a workgroup (two chunk matmuls run side by side in the
+    // pipeline).  All shapes share the k loop, so the choice never changes the
+    // result bits.
     const int64_t t256 = ((p.rows + 255) / 256) * ((p.n + 255) / 256);
     const int64_t t256x128 = ((p.rows + 255) / 256) * ((p.n + 127) / 128);
-    if (t256 >= 256) return launch_dma<256, 256, 2, 4, 3, KIND>(p, s);
-    if (t256x128 >= 224) return launch_dma<256, 128, 4, 2, 4, KIND>(p, s);
+    if (t256 >= 120) return launch_dma<256, 256, 2, 4, 3, KIND>(p, s);
+    if (t256x128 >= 120) return launch_dma<256, 128, 4, 2, 4, KIND>(p, s);
     return launch_dma<128, 128, 2, 2, 4, KIND>(p, s);
 }
 
