@@ -47,23 +47,26 @@ def _run(cmd, verbose):
         print(r.stdout + r.stderr, flush=True)
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, defines=(), lib_path: str = LIB_PATH, build_dir: str = BUILD_DIR) -> str:
+    """Compile and link libcoc.so.  `defines` (e.g. ["COC_SC1_256=0"]) override
+    the build-time tuning knobs of kernels.hip."""
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
     jobs = []
     for s in DEVICE_SOURCES:
-        obj = os.path.join(BUILD_DIR, s + ".o")
-        jobs.append([cc, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(HERE, s), "-o", obj])
+        obj = os.path.join(build_dir, s + ".o")
+        jobs.append([cc, *COMMON, *DEVICE, *dflags, "-x", "hip", "-c", os.path.join(HERE, s), "-o", obj])
     for s in HOST_SOURCES:
-        obj = os.path.join(BUILD_DIR, s + ".o")
+        obj = os.path.join(build_dir, s + ".o")
         jobs.append([cc, *COMMON, "-c", os.path.join(HERE, s), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     objs = [j[-1] for j in jobs]
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -20,6 +20,22 @@
 
 #include "coc_internal.h"
 
+// Build-time tuning knobs (defaults are the measured best): the minimum tile
+// count of a chunk for the 256x256 and 256x128 matmul tiles, and whether those
+// kernels load with device scope (L1 bypass).
+#ifndef COC_TILE256_MIN
+#define COC_TILE256_MIN 100
+#endif
+#ifndef COC_TILE256x128_MIN
+#define COC_TILE256x128_MIN 120
+#endif
+#ifndef COC_SC1_256
+#define COC_SC1_256 1
+#endif
+#ifndef COC_SC1_128
+#define COC_SC1_128 0
+#endif
+
 namespace coc {
 namespace {
 
@@ -94,14 +110,27 @@ struct GemmParams {
 
 // ------------------------------------------------------------------ tile order
 // Workgroups are handed to the 8 XCDs (each with its own L2) round-robin by
-// id.  This bijection gives XCD x a contiguous run of tile numbers, and tile
-// numbers run m-fastest, so the tiles sharing a weight column block sit on
-// one XCD and that block is fetched into one L2 instead of several.
+// id.  The first bijection gives XCD x a contiguous run of tile numbers; the
+// second walks tile numbers in groups of up to 4 tile rows, m-fastest inside a
+// group.  A short chunk (<= 4 tile rows) thus keeps each weight column block on
+// one XCD, and a tall matrix gets 4-row x n blocks per XCD instead of tiles
+// from 16 rows whose activation blocks all sit 4 MB apart.
 __device__ __forceinline__ int xcd_tile(int b, int total) {
     constexpr int NX = 8;
     const int q = total / NX, r = total % NX;
     const int x = b % NX, local = b / NX;
     return x * q + (x < r ? x : r) + local;
+}
+
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int* tm, int* tn) {
+    constexpr int GM = 4;
+    const int t = xcd_tile(b, tiles_m * tiles_n);
+    const int per_group = GM * tiles_n;
+    const int g = t / per_group;
+    const int rows_in_group = (tiles_m - g * GM) < GM ? (tiles_m - g * GM) : GM;
+    const int in_g = t - g * per_group;
+    *tm = g * GM + in_g % rows_in_group;
+    *tn = in_g / rows_in_group;
 }
 
 // ------------------------------------------------------------------ MFMA GEMMs
@@ -150,9 +179,8 @@ __global__ __launch_bounds__(256) void gemm_w8(GemmParams p) {
     const int wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    const int tile = xcd_tile(blockIdx.x, p.tiles_m * p.tiles_n);
-    const int tm = tile % p.tiles_m;
-    const int tn = tile / p.tiles_m;
+    int tm, tn;
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     // ---- A rows handled by this thread (row map evaluated once)
@@ -365,9 +393,17 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int gA32(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 __device__ __forceinline__ int gB32(int K) { return (K & 3) << 2; }
 
+// DEV_SCOPE: device-scope load (sc1), which does not allocate in the
+// per-CU L1; each 16-byte chunk is read once per workgroup, so L1 caching buys
+// nothing and its miss queue was measured stalling the 256x256 kernel.
+template <bool DEV_SCOPE>
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
+    if constexpr (DEV_SCOPE)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1"
+                     :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
@@ -386,7 +422,7 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int KIND>
+template <int BM, int BN, int WM, int WN, int STAGES, int KIND, bool DEV_SCOPE>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
     constexpr int NW = WM * WN;
     constexpr int BK = 32;
@@ -415,8 +451,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int tile = xcd_tile(blockIdx.x, p.tiles_m * p.tiles_n);
-    const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
+    int tm, tn;
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     // global sources of this wave's loads (row map applied once)
@@ -453,13 +489,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
         for (int i = 0; i < APW; ++i) {
             const uint8_t* src =
                 (aok[i] && k0 + akof[i] < p.k) ? asrc[i] + (int64_t)(k0 + akof[i]) * 2 : zero;
-            dma16(src, lds_u32(st + (wave * APW + i) * 1024));
+            dma16<DEV_SCOPE>(src, lds_u32(st + (wave * APW + i) * 1024));
         }
 #pragma unroll
         for (int i = 0; i < BPW; ++i) {
             const uint8_t* src =
                 (bok[i] && k0 + bkr[i] < p.k) ? bsrc[i] + (int64_t)(k0 + bkr[i]) * p.n * 2 : zero;
-            dma16(src, lds_u32(st + A_BYTES + (wave * BPW + i) * 1024));
+            dma16<DEV_SCOPE>(src, lds_u32(st + A_BYTES + (wave * BPW + i) * 1024));
         }
     };
 
@@ -783,11 +819,11 @@ hipError_t launch_w8_any(GemmParams p, hipStream_t s) {
     return launch_w8<128, 128>(p, s);
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int KIND>
+template <int BM, int BN, int WM, int WN, int STAGES, int KIND, bool DEV_SCOPE>
 hipError_t launch_dma(GemmParams p, hipStream_t s) {
     p.tiles_m = (p.rows + BM - 1) / BM;
     p.tiles_n = (p.n + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_dma<BM, BN, WM, WN, STAGES, KIND>), dim3(p.tiles_m * p.tiles_n),
+    hipLaunchKernelGGL((gemm_dma<BM, BN, WM, WN, STAGES, KIND, DEV_SCOPE>), dim3(p.tiles_m * p.tiles_n),
                        dim3(64 * WM * WN), 0, s, p);
     return hipGetLastError();
 }
@@ -800,9 +836,9 @@ hipError_t launch_dma_kind(GemmParams p, hipStream_t s) {
     // result bits.
     const int64_t t256 = ((p.rows + 255) / 256) * ((p.n + 255) / 256);
     const int64_t t256x128 = ((p.rows + 255) / 256) * ((p.n + 127) / 128);
-    if (t256 >= 120) return launch_dma<256, 256, 2, 4, 3, KIND>(p, s);
-    if (t256x128 >= 120) return launch_dma<256, 128, 4, 2, 4, KIND>(p, s);
-    return launch_dma<128, 128, 2, 2, 4, KIND>(p, s);
+    if (t256 >= COC_TILE256_MIN) return launch_dma<256, 256, 2, 4, 3, KIND, COC_SC1_256 != 0>(p, s);
+    if (t256x128 >= COC_TILE256x128_MIN) return launch_dma<256, 128, 4, 2, 4, KIND, COC_SC1_128 != 0>(p, s);
+    return launch_dma<128, 128, 2, 2, 4, KIND, false>(p, s);
 }
 
 }  // namespace
