@@ -27,6 +27,28 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "per-rank GEMM+reduce TFLOP/s & % bf16 MFMA peak at LLaMA2-70B TP8 shapes"
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_dma_llama70b_tp8_sp_step_hbm_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "tensor_gemm_collective_amd", "csrc", "kernels.hip")
+
+
+def measured_traffic():
+    """HBM bytes per matmul launch from the committed rocprofv3 counter summary, or
+    None when kernels.hip has changed since those counters were taken."""
+    import hashlib
+    try:
+        fields = {}
+        for line in open(TRAFFIC_SUMMARY):
+            if ":" in line and not line.startswith(("#", "|", " ", "`")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        digest = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        if fields.get("kernels_sha256") != digest:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -301,7 +323,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "avg_launch_us": round(avg_ms * 1e3, 3),
             "launches_per_step": g["launches"] / args.steps,
             "flops_per_launch": flops_per_launch,

@@ -830,8 +830,8 @@ hipError_t launch_dma(GemmParams p, hipStream_t s) {
 
 template <int KIND>
 hipError_t launch_dma_kind(GemmParams p, hipStream_t s) {
-    // Tile shape: the largest tile that still gives at least about half of the
-    // 256 compute units a workgroup (two chunk matmuls run side by side in the
+    // Tile shape: the largest tile that still gives at least ~100 workgroups
+    // (two chunk matmuls run side by side on 256 compute units in the
     // pipeline).  All shapes share the k loop, so the choice never changes the
     // result bits.
     const int64_t t256 = ((p.rows + 255) / 256) * ((p.n + 255) / 256);
