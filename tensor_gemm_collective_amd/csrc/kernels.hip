@@ -33,7 +33,12 @@
 #define COC_SC1_256 1
 #endif
 #ifndef COC_SC1_128
-#define COC_SC1_128 0
+#define COC_SC1_128 1
+#endif
+// Wave rows of the 256x256 tile (4: 4 x 2 waves of 64 x 128; 2: 2 x 4 waves of
+// 128 x 64, fewer VGPRs so reduce waves fit beside it).
+#ifndef COC_T256_WM
+#define COC_T256_WM 2
 #endif
 
 namespace coc {
@@ -358,18 +363,19 @@ __global__ __launch_bounds__(256) void gemm_w8(GemmParams p) {
 }
 
 // Direct-to-LDS kernel for bf16 / fp16 (gfx950).  Tile BM x BN, k in stages
-// of 32, an LDS ring of STAGES stages, 64 * WM * WN threads (WM x WN waves,
-// wave tile BM/WM x BN/WN).
+// of BK (32 or 64), an LDS ring of STAGES stages, 64 * WM * WN threads (WM x WN
+// waves, wave tile BM/WM x BN/WN).
 //
 //   * Both operands go from global memory straight into LDS with 16-byte
 //     global_load_lds_dwordx4 (lane L of a wave-instruction lands at byte
 //     16 * L of a 1 KB LDS block); no VGPR staging, no LDS store instructions.
 //     Each lane picks the global chunk that belongs at its LDS slot, which is
 //     how the XOR swizzles below are applied.
-//   * A (X rows, k-contiguous) is stored [BM rows][32 k], 64 B per row; chunk c
-//     of row r sits at c ^ gA(r), so the 16-byte MFMA operand reads of 16
-//     consecutive rows hit distinct banks.
-//   * The weight (k x n row-major in memory) is stored as it comes, [32 k][BN
+//   * A (X rows, k-contiguous) is stored [BM rows][BK k]; chunk c of row r
+//     sits at c ^ gA(r), so the 16-byte MFMA operand reads of 16 consecutive
+//     rows hit distinct banks.  With BK = 64 every A row contributes a whole
+//     128-byte line per stage.
+//   * The weight (k x n row-major in memory) is stored as it comes, [BK k][BN
 //     n]; chunk c of k-row K sits at c ^ gB(K).  The MFMA fragment (lane l:
 //     column l % 32, 8 consecutive k) is read with two ds_read_b64_tr_b16: in
 //     each 16-lane group, lane i receives element i % 4 of the 8-byte chunks
@@ -379,19 +385,24 @@ __global__ __launch_bounds__(256) void gemm_w8(GemmParams p) {
 //   * Lanes outside the matrix (m, n or k tail) load 16 zero bytes from a
 //     device constant instead, so every wave issues the same number of loads
 //     per stage and vmcnt counts stay exact; the k tail is zero-filled this way.
-//   * Per stage: read the second half's fragments, run the first half's MFMAs,
-//     wait for this wave's loads of the next stage, barrier, issue the loads of
-//     stage kt + STAGES - 1 into the slot every wave has finished with, read
-//     the next stage's first fragments, run the second half's MFMAs.  The DMA
-//     loads are issued through inline asm so the compiler does not order every
-//     LDS read behind them; the explicit vmcnt wait + s_barrier is the ordering.
+//   * Per stage: wait for this wave's loads of the stage, barrier (every
+//     wave's loads are then visible and every wave is done with the slot the
+//     next loads go to), issue the loads of stage kt + STAGES - 1, then the
+//     MFMA k steps with the next step's fragments read ahead.  The DMA loads
+//     are issued through inline asm so the compiler does not order every LDS
+//     read behind them; the explicit vmcnt wait + s_barrier is the ordering.
 __device__ const u32x4 g_zero16 = {0, 0, 0, 0};
 
 #define COC_LDS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int gA32(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
-__device__ __forceinline__ int gB32(int K) { return (K & 3) << 2; }
+// A rows hold BK/8 16-byte chunks: 4 (BK 32) or 8 (BK 64).
+template <int BK>
+__device__ __forceinline__ int gA(int r) {
+    if constexpr (BK == 32) return ((r >> 2) ^ (r >> 1)) & 3;
+    else return (r ^ (r >> 3)) & 7;
+}
+__device__ __forceinline__ int gB(int K) { return (K & 3) << 2; }
 
 // DEV_SCOPE: device-scope load (sc1), which does not allocate in the
 // per-CU L1; each 16-byte chunk is read once per workgroup, so L1 caching buys
@@ -422,10 +433,12 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int KIND, bool DEV_SCOPE>
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int KIND, bool DEV_SCOPE>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
     constexpr int NW = WM * WN;
-    constexpr int BK = 32;
+    constexpr int KS = BK / 16;    // MFMA k steps per stage
+    constexpr int ACH = BK / 8;    // 16-byte chunks per A row
+    static_assert(BK == 32 || BK == 64, "stage depth");
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
@@ -433,13 +446,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
     constexpr int A_INS = A_BYTES / 1024, B_INS = B_BYTES / 1024;
     static_assert(A_INS % NW == 0 && B_INS % NW == 0, "loads must split evenly over waves");
     static_assert(BN % 128 == 0, "B swizzle works on 16-chunk groups");
-    static_assert(STAGES == 3 || STAGES == 4, "stage ring");
+    static_assert(STAGES >= 2 && STAGES <= 4, "stage ring");
     constexpr int APW = A_INS / NW, BPW = B_INS / NW, LPW = APW + BPW;
     constexpr int BROW = BN / 8;   // 16-byte chunks per weight k-row
     constexpr int OUT_DT = (KIND == GK_BF16) ? COC_BF16 : COC_F16;
     __shared__ __attribute__((aligned(1024))) uint8_t sm0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t sm1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t sm2[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm2[STAGES >= 3 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t sm3[STAGES == 4 ? STAGE : 16];
     auto stage = [&](auto S) -> uint8_t* {
         constexpr int s_ = decltype(S)::value;
@@ -462,11 +475,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < APW; ++i) {
         const int q = (wave * APW + i) * 64 + lane;
-        const int row = q >> 2;
+        const int row = q / ACH;
         aok[i] = m0 + row < p.rows;
         const int64_t gr = aok[i] ? map_row(m0 + row, p.rpb, p.base, p.stride) : 0;
         asrc[i] = p.a + gr * (int64_t)p.k * 2;
-        akof[i] = ((q & 3) ^ gA32(row)) * 8;
+        akof[i] = ((q % ACH) ^ gA<BK>(row)) * 8;
     }
     const uint8_t* bsrc[BPW];
     int bkr[BPW];
@@ -475,7 +488,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
     for (int i = 0; i < BPW; ++i) {
         const int q = (wave * BPW + i) * 64 + lane;
         const int K = q / BROW;
-        const int col = n0 + ((q % BROW) ^ gB32(K)) * 8;
+        const int col = n0 + ((q % BROW) ^ gB(K)) * 8;
         bok[i] = col < p.n;
         bkr[i] = K;
         bsrc[i] = p.b + (int64_t)(bok[i] ? col : 0) * 2;
@@ -500,17 +513,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
     };
 
     // fragment offsets within a stage
-    int aoff[2][FM];
+    int aoff[KS][FM];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int row = wm * WTM + i * 32 + (lane & 31);
-            aoff[ks][i] = row * 64 + (((ks * 2 + (lane >> 5)) ^ gA32(row)) << 4);
+            aoff[ks][i] = row * (BK * 2) + (((ks * 2 + (lane >> 5)) ^ gA<BK>(row)) << 4);
         }
-    int boff[2][2][FN];
+    int boff[KS][2][FN];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -518,7 +531,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
                 const int r = lane & 15, grp = (lane >> 4) & 1, hk = lane >> 5;
                 const int K = ks * 16 + hk * 8 + h * 4 + (r >> 2);
                 const int col = wn * WTN + j * 32 + grp * 16 + 4 * (r & 3);
-                boff[ks][h][j] = A_BYTES + K * BN * 2 + (((col >> 3) ^ gB32(K)) << 4) + (col & 7) * 2;
+                boff[ks][h][j] = A_BYTES + K * BN * 2 + (((col >> 3) ^ gB(K)) << 4) + (col & 7) * 2;
             }
 
     f32x16 acc[FM][FN];
@@ -553,47 +566,46 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
     std::integral_constant<int, 2> S2;
     std::integral_constant<int, 3> S3;
     if (0 < KT) issue(0, S0);
-    if (1 < KT) issue(1, S1);
+    if constexpr (STAGES >= 3) {
+        if (1 < KT) issue(1, S1);
+    }
     if constexpr (STAGES == 4) {
         if (2 < KT) issue(2, S2);
     }
-    u32x4 a0[FM], b0[FN], a1[FM], b1[FN];
-    if (KT > 0) {
-        if constexpr (STAGES == 4) {
-            if (KT > 2) wait_vmcnt<2 * LPW>();
-            else if (KT > 1) wait_vmcnt<LPW>();
-            else wait_vmcnt<0>();
-        } else {
-            if (KT > 1) wait_vmcnt<LPW>();
-            else wait_vmcnt<0>();
-        }
-        block_barrier();
-        rd((const COC_LDS uint8_t*)stage(S0), 0, a0, b0);
-    }
     auto body = [&](int kt, auto S) {
         constexpr int cs = decltype(S)::value;
-        rd((const COC_LDS uint8_t*)stage(S), 1, a1, b1);
-        mm(a0, b0);
-        if (kt + 1 < KT) {
-            // this wave's loads of stage kt + 1 are done; later stages may stay in flight
-            if constexpr (STAGES == 4) {
-                if (kt + 2 < KT) wait_vmcnt<LPW>();
-                else wait_vmcnt<0>();
-            } else {
-                wait_vmcnt<0>();
-            }
+        // this wave's loads of stage kt are done; stages issued after it may stay in flight
+        const int ahead = KT - 1 - kt;
+        if constexpr (STAGES == 4) {
+            if (ahead >= 2) wait_vmcnt<2 * LPW>();
+            else if (ahead == 1) wait_vmcnt<LPW>();
+            else wait_vmcnt<0>();
+        } else if constexpr (STAGES == 3) {
+            if (ahead >= 1) wait_vmcnt<LPW>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
         }
+        // every wave's loads of stage kt are visible, and every wave is done
+        // reading the slot the next loads go to
         block_barrier();
         if (kt + STAGES - 1 < KT)
             issue(kt + STAGES - 1, std::integral_constant<int, (cs + STAGES - 1) % STAGES>{});
-        if (kt + 1 < KT)
-            rd((const COC_LDS uint8_t*)stage(std::integral_constant<int, (cs + 1) % STAGES>{}), 0, a0, b0);
-        mm(a1, b1);
+        const COC_LDS uint8_t* st = (const COC_LDS uint8_t*)stage(S);
+        u32x4 af[2][FM], bf[2][FN];
+        rd(st, 0, af[0], bf[0]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) rd(st, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+            mm(af[ks & 1], bf[ks & 1]);
+        }
     };
     for (int kt = 0; kt < KT; kt += STAGES) {
         body(kt, S0);
         if (kt + 1 < KT) body(kt + 1, S1);
-        if (kt + 2 < KT) body(kt + 2, S2);
+        if constexpr (STAGES >= 3) {
+            if (kt + 2 < KT) body(kt + 2, S2);
+        }
         if constexpr (STAGES == 4) {
             if (kt + 3 < KT) body(kt + 3, S3);
         }
@@ -819,11 +831,11 @@ hipError_t launch_w8_any(GemmParams p, hipStream_t s) {
     return launch_w8<128, 128>(p, s);
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int KIND, bool DEV_SCOPE>
+template <int BM, int BN, int WM, int WN, int STAGES, int BK, int KIND, bool DEV_SCOPE>
 hipError_t launch_dma(GemmParams p, hipStream_t s) {
     p.tiles_m = (p.rows + BM - 1) / BM;
     p.tiles_n = (p.n + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_dma<BM, BN, WM, WN, STAGES, KIND, DEV_SCOPE>), dim3(p.tiles_m * p.tiles_n),
+    hipLaunchKernelGGL((gemm_dma<BM, BN, WM, WN, STAGES, BK, KIND, DEV_SCOPE>), dim3(p.tiles_m * p.tiles_n),
                        dim3(64 * WM * WN), 0, s, p);
     return hipGetLastError();
 }
@@ -836,9 +848,10 @@ hipError_t launch_dma_kind(GemmParams p, hipStream_t s) {
     // result bits.
     const int64_t t256 = ((p.rows + 255) / 256) * ((p.n + 255) / 256);
     const int64_t t256x128 = ((p.rows + 255) / 256) * ((p.n + 127) / 128);
-    if (t256 >= COC_TILE256_MIN) return launch_dma<256, 256, 2, 4, 3, KIND, COC_SC1_256 != 0>(p, s);
-    if (t256x128 >= COC_TILE256x128_MIN) return launch_dma<256, 128, 4, 2, 4, KIND, COC_SC1_128 != 0>(p, s);
-    return launch_dma<128, 128, 2, 2, 4, KIND, false>(p, s);
+    if (t256 >= COC_TILE256_MIN)
+        return launch_dma<256, 256, COC_T256_WM, 8 / COC_T256_WM, 2, 64, KIND, COC_SC1_256 != 0>(p, s);
+    if (t256x128 >= COC_TILE256x128_MIN) return launch_dma<256, 128, 4, 2, 3, 64, KIND, COC_SC1_128 != 0>(p, s);
+    return launch_dma<128, 128, 2, 2, 4, 32, KIND, false>(p, s);
 }
 
 }  // namespace
