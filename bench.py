@@ -144,6 +144,64 @@ def cpu_baseline(inp, frac):
     }
 
 
+def run_configs(torch, tgc, synth, dev, iters=10):
+    """Time every workload at its configured splits; one JSON line per case on stderr.
+    The GEMM-only comparator is torch.matmul (hipBLASLt) on the same shapes."""
+    def timeit(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    def emit(name, flops, ms, ref_ms, **kw):
+        line = {"case": name, "ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                "hipblaslt_gemm_only_ms": round(ref_ms, 5)}
+        line.update(kw)
+        print(json.dumps(line), file=sys.stderr, flush=True)
+
+    W = synth.WORKLOADS
+    wl = W["toy_f32"]
+    x = synth.uniform(wl.wid, synth.T_X, 0, (wl.m, wl.k), -1, 1, "f32").to(dev)
+    w = synth.uniform(wl.wid, synth.T_W, 0, (wl.k, wl.n), -1, 1, "f32").to(dev)
+    pr = [None, synth.uniform(wl.wid, synth.T_PEER, 1, (wl.m, wl.n), -1, 1, "f32").to(dev)]
+    ms = timeit(lambda: tgc.matmul_all_reduce(x, w, pr, 0, split=2))
+    emit("toy_f32 AR split2", 2.0 * wl.m * wl.n * wl.k, ms, timeit(lambda: torch.matmul(x, w)))
+
+    for name, det_list, splits in (("bloom7b_ar", (0, 1), (4, 2, 8)), ("bloom176b_ar", (1,), (2, 4, 8))):
+        wl = W[name]
+        x = synth.normal(wl.wid, synth.T_X, 0, (wl.m, wl.k), 1.0, "bf16").to(dev)
+        w = synth.normal(wl.wid, synth.T_W, 0, (wl.k, wl.n), 0.02, "bf16").to(dev)
+        pr = [None] + [synth.normal(wl.wid, synth.T_PEER, r, (wl.m, wl.n), wl.peer_sigma, "bf16").to(dev)
+                       for r in range(1, wl.world)]
+        y = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device=dev)
+        po = torch.empty_like(y)
+        ref = timeit(lambda: torch.matmul(x, w))
+        for det in det_list:
+            for sp in splits:
+                ms = timeit(lambda: tgc.matmul_all_reduce(x, w, pr, 0, y=y, partial_out=po, split=sp,
+                                                          deterministic=det))
+                emit(f"{name} split{sp} det{det}", 2.0 * wl.m * wl.n * wl.k, ms, ref)
+        del x, w, pr, y, po
+
+    wl = W["w8a16_ar"]
+    x = synth.normal(wl.wid, synth.T_X, 0, (wl.m, wl.k), 1.0, "f16").to(dev)
+    q = synth.integers(wl.wid, synth.T_W, 0, (wl.k, wl.n), -127, 127, "i8").to(dev)
+    pr = [None] + [synth.normal(wl.wid, synth.T_PEER, r, (wl.m, wl.n), wl.peer_sigma, "f16").to(dev)
+                   for r in range(1, wl.world)]
+    wf = q.to(torch.float16)
+    ref = timeit(lambda: torch.matmul(x, wf))
+    for mode, shape in (("per_tensor", (1,)), ("per_channel", (wl.n,)), ("per_group", (wl.k // wl.group, wl.n))):
+        sc = synth.fp16_scales(wl.wid, 0, shape).to(dev)
+        ms = timeit(lambda: tgc.matmul_all_reduce_w8a16(x, q, sc, mode, pr, 0, group_size=wl.group, split=4))
+        emit(f"w8a16_ar {mode} split4", 2.0 * wl.m * wl.n * wl.k, ms, ref)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +212,8 @@ def main():
     ap.add_argument("--cpu-frac", type=float, default=1.0)
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-op and serial timings after the timed region (profiling runs)")
+    ap.add_argument("--configs", action="store_true",
+                    help="after the main line, time every workload at its configured splits (stderr)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) three "
                          "times, for scaling the HBM byte counters, and exit")
@@ -335,6 +395,10 @@ def main():
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_frac)
     print(json.dumps(out), flush=True)
+    if args.configs:
+        del inp
+        torch.cuda.empty_cache()
+        run_configs(torch, tgc, synth, dev)
 
 
 if __name__ == "__main__":
