@@ -27,7 +27,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "per-rank GEMM+reduce TFLOP/s & % bf16 MFMA peak at LLaMA2-70B TP8 shapes"
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_dma_llama70b_tp8_sp_step_hbm_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_ring_llama70b_tp8_sp_step_hbm_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "tensor_gemm_collective_amd", "csrc", "kernels.hip")
 
 
@@ -378,7 +378,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_dma (m-chunk matmul)",
+            "kernel": "gemm_ring (m-chunk matmul)",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

@@ -48,7 +48,7 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False, defines=(), lib_path: str = LIB_PATH, build_dir: str = BUILD_DIR) -> str:
-    """Compile and link libcoc.so.  `defines` (e.g. ["COC_SC1_256=0"]) override
+    """Compile and link libcoc.so.  `defines` (e.g. ["COC_RING_MIN_TILES=128"]) override
     the build-time tuning knobs of kernels.hip."""
     cc = hipcc()
     os.makedirs(build_dir, exist_ok=True)
@@ -59,7 +59,7 @@ def build(verbose: bool = False, defines=(), lib_path: str = LIB_PATH, build_dir
         jobs.append([cc, *COMMON, *DEVICE, *dflags, "-x", "hip", "-c", os.path.join(HERE, s), "-o", obj])
     for s in HOST_SOURCES:
         obj = os.path.join(build_dir, s + ".o")
-        jobs.append([cc, *COMMON, "-c", os.path.join(HERE, s), "-o", obj])
+        jobs.append([cc, *COMMON, *dflags, "-c", os.path.join(HERE, s), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     objs = [j[-1] for j in jobs]

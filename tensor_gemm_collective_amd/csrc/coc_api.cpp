@@ -27,6 +27,12 @@
 
 #include "coc_internal.h"
 
+// Chunk matmuls alternate between the caller's stream and a second compute
+// stream (2), or all run on the caller's stream (1).
+#ifndef COC_COMPUTE_STREAMS
+#define COC_COMPUTE_STREAMS 2
+#endif
+
 namespace coc {
 namespace {
 
@@ -179,12 +185,13 @@ coc_status check_peers(const void* const* peers, const Plan& P, int64_t bytes, s
 }
 
 // ------------------------------------------------------------------ pipelines
-GemmLaunch gemm_for_chunk(const GemmLaunch& g0, const coc_chunk& c) {
+GemmLaunch gemm_for_chunk(const Plan& P, const GemmLaunch& g0, const coc_chunk& c) {
     GemmLaunch g = g0;
     g.base = c.base;
     g.stride = c.stride;
     g.rpb = c.rows_per_blk;
     g.nblk = c.nblk;
+    g.concurrent = P.split == 1 ? 1 : COC_COMPUTE_STREAMS;
     return g;
 }
 
@@ -197,7 +204,7 @@ coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLa
                              hipStream_t main) {
     const size_t es = elem_size(P.dt);
     auto gemm = [&](int i, hipStream_t s) {
-        const GemmLaunch g = gemm_for_chunk(g0, P.chunk[i]);
+        const GemmLaunch g = gemm_for_chunk(P, g0, P.chunk[i]);
         return launch(KC_GEMM, gemm_flops(P, P.chunk[i]), s, [&] { return launch_gemm(g, s); });
     };
     auto reduce = [&](int i, hipStream_t s) {
@@ -217,7 +224,7 @@ coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLa
     COC_HIP(hipEventRecord(c->fork, main));
     COC_HIP(hipStreamWaitEvent(c->gemm2, c->fork, 0));
     for (int i = 0; i < P.nchunks; ++i) {
-        hipStream_t cs = (i & 1) ? c->gemm2 : main;
+        hipStream_t cs = (COC_COMPUTE_STREAMS == 2 && (i & 1)) ? c->gemm2 : main;
         COC_TRY(gemm(i, cs));
         COC_HIP(hipEventRecord(c->ev[i], cs));
         COC_HIP(hipStreamWaitEvent(c->side, c->ev[i], 0));
@@ -242,7 +249,7 @@ coc_status run_comm_first(const Plan& P, const GemmLaunch& g0, const GatherLaunc
         return launch(KC_GATHER, bytes, s, [&] { return launch_gather(a, s); });
     };
     auto gemm = [&](int i, hipStream_t s) {
-        const GemmLaunch g = gemm_for_chunk(g0, P.chunk[i]);
+        const GemmLaunch g = gemm_for_chunk(P, g0, P.chunk[i]);
         return launch(KC_GEMM, gemm_flops(P, P.chunk[i]), s, [&] { return launch_gemm(g, s); });
     };
     if (P.split == 1) {
@@ -255,7 +262,7 @@ coc_status run_comm_first(const Plan& P, const GemmLaunch& g0, const GatherLaunc
     COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
     COC_HIP(hipStreamWaitEvent(c->gemm2, c->fork, 0));
     for (int i = 0; i < P.nchunks; ++i) {
-        hipStream_t cs = (i & 1) ? c->gemm2 : main;
+        hipStream_t cs = (COC_COMPUTE_STREAMS == 2 && (i & 1)) ? c->gemm2 : main;
         COC_TRY(gather(i, c->side));
         COC_HIP(hipEventRecord(c->ev[i], c->side));
         COC_HIP(hipStreamWaitEvent(cs, c->ev[i], 0));

@@ -57,6 +57,7 @@ struct GemmLaunch {
     int64_t n, k;        // lda = k, ldb = ldc = n
     int64_t base, stride, rpb;
     int32_t nblk;
+    int32_t concurrent;  // chunk matmuls expected to run side by side (tile choice only)
 };
 
 // Fixed-order sum of nsrc row blocks: dst[dst_row0 + j] = sum_r src[r][src_row0 + j],

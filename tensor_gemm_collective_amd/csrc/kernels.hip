@@ -1,9 +1,11 @@
 // gfx950 kernels of the fused matmul + collective path.
 //
-//   gemm_dma    m-chunk matmul, bf16 / fp16 inputs, direct-to-LDS loads and
-//               LDS transpose reads, binary32 accumulation on MFMA,
-//               round-to-nearest-even to the storage dtype.  The "Matmul" of
-//               the CoC guide's matmul/collective pairs ("Problem analysis").
+//   gemm_ring   m-chunk matmul, bf16 / fp16 inputs, k a multiple of 32:
+//               direct-to-LDS loads into an LDS ring, LDS transpose reads,
+//               binary32 accumulation on MFMA, round-to-nearest-even to the
+//               storage dtype.  The "Matmul" of the CoC guide's
+//               matmul/collective pairs ("Problem analysis").
+//   gemm_dma    the same for any k (a multiple of 8), 128 x 128 tiles.
 //   gemm_w8     the same with int8 weights dequantised to fp16 in the main
 //               loop (w8A16).
 //   gemm_f32    the same for binary32 inputs on the vector ALUs.
@@ -20,25 +22,11 @@
 
 #include "coc_internal.h"
 
-// Build-time tuning knobs (defaults are the measured best): the minimum tile
-// count of a chunk for the 256x256 and 256x128 matmul tiles, and whether those
-// kernels load with device scope (L1 bypass).
-#ifndef COC_TILE256_MIN
-#define COC_TILE256_MIN 100
-#endif
-#ifndef COC_TILE256x128_MIN
-#define COC_TILE256x128_MIN 120
-#endif
-#ifndef COC_SC1_256
-#define COC_SC1_256 1
-#endif
-#ifndef COC_SC1_128
-#define COC_SC1_128 1
-#endif
-// Wave rows of the 256x256 tile (4: 4 x 2 waves of 64 x 128; 2: 2 x 4 waves of
-// 128 x 64, fewer VGPRs so reduce waves fit beside it).
-#ifndef COC_T256_WM
-#define COC_T256_WM 2
+// Build-time tuning knob (default: the measured best): the fewest workgroups
+// the chunk matmuls running side by side should have together before the
+// ring kernel moves to a larger tile.
+#ifndef COC_RING_MIN_TILES
+#define COC_RING_MIN_TILES 200
 #endif
 
 namespace coc {
@@ -417,6 +405,13 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                      :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
 }
 
+// The same copy addressed as an SGPR base plus a 32-bit VGPR offset (device
+// scope), so per-stage address updates are scalar adds.
+__device__ __forceinline__ void dma16_sbase(uint32_t voff, const void* sbase, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 sc1"
+                 :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
     return (uint32_t)(uintptr_t)(const COC_LDS void*)p;
 }
@@ -634,6 +629,190 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
     }
 }
 
+// LDS-ring kernel for bf16 / fp16 with k a positive multiple of 32 (gfx950).
+// Tile BM x BN, WM x WN waves of BM/WM x BN/WN, k in stages of 32, an LDS ring
+// of S stages.  Measured best: 256 x 256 and 128 x 256 with 2 x 4 waves (two
+// waves per SIMD, so one wave's waits are covered by the other's MFMAs), and
+// 128 x 128 with 2 x 2 waves (two workgroups per CU).
+//
+//   * Per 16-k step a wave reads FM + 2 FN fragments (FM = wave rows / 32,
+//     FN = wave columns / 32) for FM x FN MFMAs.
+//   * Loads are the same direct-to-LDS 16-byte copies and XOR swizzles as
+//     gemm_dma, addressed as an SGPR base (the stage's k offset) plus a fixed
+//     32-bit VGPR offset per lane.  Rows and columns past the matrix are
+//     clamped to valid ones (their results are never stored); k has no tail.
+//   * Each stage runs in two phases of FM x FN MFMAs.  Phase 1 computes k step
+//     0 while reading the fragments of k step 1.  Then this wave waits for its
+//     loads of the next stage and the workgroup meets at a barrier: every
+//     wave's loads of stage kt + 1 are then in LDS and every wave has finished
+//     reading stage kt - 1.  Phase 2 computes k step 1 while reading the
+//     fragments of stage kt + 1 (k step 0) and loading stage kt + S - 1 into
+//     the slot stage kt - 1 used.  The MFMA unit thus never waits for a
+//     fragment read at a stage boundary.
+//   * Fragment reads go 2 per MFMA from the first MFMA of a phase; the DMA
+//     instructions are spread evenly over phase 2.  sched_barrier fixes that
+//     order against the compiler's scheduler.
+//   * The k walk (16-k MFMA steps in increasing k, same operand roles) is the
+//     one every other kernel here uses, so results are bitwise identical to
+//     theirs.
+template <int BM, int BN, int S, int WM, int WN, int KIND>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_ring(GemmParams p) {
+    constexpr int BK = 32, NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE = A_BYTES + B_BYTES;
+    constexpr int APW = A_BYTES / 1024 / NW, BPW = B_BYTES / 1024 / NW, DPW = APW + BPW;
+    constexpr int BROW = BN / 8;   // 16-byte chunks per weight k-row
+    constexpr int KPI = 64 / BROW; // weight k-rows per load instruction
+    constexpr int NMM = FM * FN, NRD = FM + 2 * FN;
+    constexpr int OUT_DT = (KIND == GK_BF16) ? COC_BF16 : COC_F16;
+    static_assert((A_BYTES / 1024) % NW == 0 && (B_BYTES / 1024) % NW == 0, "loads split over the waves");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32 x 32 MFMA blocks");
+    static_assert(BROW >= 16 && BROW <= 64, "weight swizzle works on 16-chunk groups");
+    static_assert(S >= 3 && S * STAGE <= 160 * 1024, "LDS ring");
+    __shared__ __attribute__((aligned(1024))) uint8_t sm[S * STAGE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const uint32_t lds0 = lds_u32(sm);
+
+    // load offsets from the stage's global base (bytes)
+    uint32_t aof[APW], bof[BPW];
+#pragma unroll
+    for (int i = 0; i < APW; ++i) {
+        const int row = (wave * APW + i) * 16 + (lane >> 2);
+        const int r = m0 + row < p.rows ? m0 + row : p.rows - 1;
+        const int64_t gr = map_row(r, p.rpb, p.base, p.stride);
+        aof[i] = (uint32_t)(gr * p.k * 2) + (((lane & 3) ^ gA<32>(row)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+        const int K = (wave * BPW + i) * KPI + lane / BROW;
+        const int col = n0 + (((lane % BROW) ^ gB(K)) << 3);
+        bof[i] = (uint32_t)K * (uint32_t)p.n * 2u + (uint32_t)(col < p.n ? col : 0) * 2u;
+    }
+    // fragment offsets within a stage (the rest are immediates)
+    int ard[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int row = wm * WTM + (lane & 31);
+        ard[ks] = row * (BK * 2) + (((ks * 2 + (lane >> 5)) ^ gA<32>(row)) << 4);
+    }
+    int brd[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int r = lane & 15, K = (lane >> 5) * 8 + (r >> 2);
+        const int col = wn * WTN + j * 32 + ((lane >> 4) & 1) * 16 + 4 * (r & 3);
+        brd[j] = A_BYTES + K * BN * 2 + (((col >> 3) ^ gB(K)) << 4) + (col & 7) * 2;
+    }
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const int KT = p.k / BK;   // >= 1 (the launcher sends k == 0 elsewhere)
+    const int64_t bstep = (int64_t)BK * p.n * 2;
+    auto dma = [&](int d, int kt, int slot) {
+        const uint32_t l = lds0 + slot * STAGE;
+        if (d < APW)
+            dma16_sbase(aof[d], p.a + (int64_t)kt * BK * 2, l + (wave * APW + d) * 1024);
+        else
+            dma16_sbase(bof[d - APW], p.b + (int64_t)kt * bstep, l + A_BYTES + (wave * BPW + d - APW) * 1024);
+    };
+    u32x4 af[2][FM], bf[2][FN];
+    // fragment r of k step ks of a slot: r < 2 FN are weight halves, then activation rows
+    auto rdf = [&](int r, int slot, int ks, int buf) {
+        const COC_LDS uint8_t* st = (const COC_LDS uint8_t*)sm + slot * STAGE;
+        if (r < 2 * FN) {
+            const int j = r >> 1, h = r & 1;
+            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (COC_LDS s16x4*)(st + brd[j] + (ks * 16 + h * 4) * BN * 2));
+            const u32x2 v2 = __builtin_bit_cast(u32x2, v);
+            bf[buf][j][2 * h] = v2[0];
+            bf[buf][j][2 * h + 1] = v2[1];
+        } else {
+            af[buf][r - 2 * FN] = *(const COC_LDS u32x4*)(st + ard[ks] + (r - 2 * FN) * 32 * BK * 2);
+        }
+    };
+    auto reads_at = [&](int s, int slot, int ks, int buf) {
+        if (2 * s < NRD) rdf(2 * s, slot, ks, buf);
+        if (2 * s + 1 < NRD) rdf(2 * s + 1, slot, ks, buf);
+    };
+    auto dmas_at = [&](int s, int kt, int slot) {
+#pragma unroll
+        for (int d = 0; d < DPW; ++d)
+            if ((d * NMM) / DPW == s) dma(d, kt, slot);
+    };
+
+    // prologue: stages 0 .. S-2 in flight, stage 0 visible, its k step 0 read
+    for (int s = 0; s < S - 1; ++s)
+        if (s < KT)
+            for (int d = 0; d < DPW; ++d) dma(d, s, s);
+    if (KT >= S - 1) wait_vmcnt<(S - 2) * DPW>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    for (int r = 0; r < NRD; ++r) rdf(r, 0, 0, 0);
+
+    auto stage = [&](int kt, auto LOAD, auto MORE, auto WAITN) {
+        constexpr bool load = decltype(LOAD)::value, more = decltype(MORE)::value;
+        const int slot = kt % S;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < NMM; ++s) {
+            acc[s / FN][s % FN] = mfma32<KIND>(bf[0][s % FN], af[0][s / FN], acc[s / FN][s % FN]);
+            reads_at(s, slot, 1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (more) {
+            wait_vmcnt<decltype(WAITN)::value>();
+            block_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int nslot = (kt + 1) % S, dslot = (kt + S - 1) % S;
+#pragma unroll
+        for (int s = 0; s < NMM; ++s) {
+            acc[s / FN][s % FN] = mfma32<KIND>(bf[1][s % FN], af[1][s / FN], acc[s / FN][s % FN]);
+            if constexpr (more) reads_at(s, nslot, 0, 0);
+            if constexpr (load) dmas_at(s, kt + S - 1, dslot);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    int kt = 0;
+    // steady state: stages kt+2 .. kt+S-2 may stay in flight at the wait
+    for (; kt + S - 1 < KT; ++kt) stage(kt, yes{}, yes{}, std::integral_constant<int, (S - 3) * DPW>{});
+    for (; kt + 1 < KT; ++kt) stage(kt, no{}, yes{}, std::integral_constant<int, 0>{});
+    stage(kt, no{}, no{}, std::integral_constant<int, 0>{});
+
+    // epilogue: lane holds n = q*8 + (lane/32)*4 + {0..3} of row m = lane%32
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int r = m0 + wm * WTM + i * 32 + (lane & 31);
+        if (r >= p.rows) continue;
+        uint8_t* crow = p.c + map_row(r, p.rpb, p.base, p.stride) * (int64_t)p.n * 2;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
+                if (col < p.n) {
+                    u32x2 v;
+                    v[0] = pack2<OUT_DT>(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+                    v[1] = pack2<OUT_DT>(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+                    *(u32x2*)(crow + (int64_t)col * 2) = v;
+                }
+            }
+    }
+}
+
 // ------------------------------------------------------------------ fp32 GEMM
 // 64 x 64 x 16 tiles, 256 threads, 4 x 4 outputs per thread, fused
 // multiply-add in k order (binary32 throughout).
@@ -840,17 +1019,30 @@ hipError_t launch_dma(GemmParams p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int BM, int BN, int S, int WM, int WN, int KIND>
+hipError_t launch_ring(GemmParams p, hipStream_t s) {
+    p.tiles_m = (p.rows + BM - 1) / BM;
+    p.tiles_n = (p.n + BN - 1) / BN;
+    hipLaunchKernelGGL((gemm_ring<BM, BN, S, WM, WN, KIND>), dim3(p.tiles_m * p.tiles_n), dim3(64 * WM * WN), 0,
+                       s, p);
+    return hipGetLastError();
+}
+
 template <int KIND>
-hipError_t launch_dma_kind(GemmParams p, hipStream_t s) {
-    // Tile shape: the largest tile that still gives at least ~100 workgroups
-    // (two chunk matmuls run side by side on 256 compute units in the
-    // pipeline).  All shapes share the k loop, so the choice never changes the
-    // result bits.
-    const int64_t t256 = ((p.rows + 255) / 256) * ((p.n + 255) / 256);
-    const int64_t t256x128 = ((p.rows + 255) / 256) * ((p.n + 127) / 128);
-    if (t256 >= COC_TILE256_MIN)
-        return launch_dma<256, 256, COC_T256_WM, 8 / COC_T256_WM, 2, 64, KIND, COC_SC1_256 != 0>(p, s);
-    if (t256x128 >= COC_TILE256x128_MIN) return launch_dma<256, 128, 4, 2, 3, 64, KIND, COC_SC1_128 != 0>(p, s);
+hipError_t launch_dma_kind(GemmParams p, int concurrent, hipStream_t s) {
+    // k a positive multiple of 32: the ring kernel with the largest tile that
+    // still gives COC_RING_MIN_TILES workgroups across the chunk matmuls that
+    // run side by side.  Otherwise the 128 x 128 direct-to-LDS kernel, which
+    // zero-fills the k tail.  Every choice walks k the same way, so it never
+    // changes the result bits.
+    if (p.k >= 32 && p.k % 32 == 0) {
+        const int64_t want = COC_RING_MIN_TILES / (concurrent > 1 ? concurrent : 1);
+        const int64_t tm256 = (p.rows + 255) / 256, tm128 = (p.rows + 127) / 128;
+        const int64_t tn256 = (p.n + 255) / 256;
+        if (tm256 * tn256 >= want) return launch_ring<256, 256, 4, 2, 4, KIND>(p, s);
+        if (tm128 * tn256 >= want) return launch_ring<128, 256, 4, 2, 4, KIND>(p, s);
+        return launch_ring<128, 128, 4, 2, 2, KIND>(p, s);
+    }
     return launch_dma<128, 128, 2, 2, 4, 32, KIND, false>(p, s);
 }
 
@@ -880,8 +1072,8 @@ int launch_gemm(const GemmLaunch& g, void* stream) {
             hipLaunchKernelGGL(gemm_f32, dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
             return hipGetLastError();
         }
-        case GK_F16: return launch_dma_kind<GK_F16>(p, s);
-        case GK_BF16: return launch_dma_kind<GK_BF16>(p, s);
+        case GK_F16: return launch_dma_kind<GK_F16>(p, g.concurrent, s);
+        case GK_BF16: return launch_dma_kind<GK_BF16>(p, g.concurrent, s);
         case GK_W8_F16: return launch_w8_any(p, s);
     }
     return hipErrorInvalidValue;

@@ -51,12 +51,13 @@ def test_toy_fp32_all_reduce_equals_unsplit_layer(split, det):
 
 # ------------------------------------------------------------------ exact integer GEMM
 GEMM_SHAPES = [
-    (300, 200, 136),     # ragged in m, n and k
+    (300, 200, 136),     # k % 32 != 0: 128x128 kernel with a zero-filled k tail; ragged m, n
     (1, 8, 8),
     (64, 8, 520),
     (517, 1032, 72),
-    (2048 + 40, 8192, 64),   # 256x256 tiles, ragged m
-    (1024, 8192, 72),        # 256x128 tiles
+    (2088, 8200, 64),    # ring kernel, 256x256 tiles, ragged m and n
+    (1000, 6152, 96),    # ring kernel, 128x256 tiles, ragged m and n
+    (300, 1032, 160),    # ring kernel, 128x128 tiles, ragged m and n
 ]
 
 
@@ -76,6 +77,31 @@ def test_gemm_integer_inputs_bit_exact(dtype, m, n, k):
     assert_bits_equal(p, encode_dtype(exact, dtype), "partial_out")
     y_ref = oracle.reduce_fixed_order([oracle.round_dtype(exact, dtype), f64(peers[1], dtype)], dtype)
     assert_bits_equal(y, encode_dtype(y_ref, dtype), "y")
+
+
+def test_gemm_bits_independent_of_kernel_and_tile():
+    """Rows 0..127 of X @ W through the 256x256, 128x256 and 128x128 ring tiles
+    and through the any-k kernel (k padded with zeros) are the same bits: every
+    kernel walks k in the same 16-k MFMA steps."""
+    log("GEMM bits across kernels and tiles")
+    k, n = 512, 8192
+    x = synth.normal(WID_TEST + 12, synth.T_X, 0, (2048, k), 1.0, "bf16")
+    w = synth.normal(WID_TEST + 12, synth.T_W, 0, (k, n), 0.02, "bf16")
+    xd, wd = dev(x), dev(w)
+    outs = []
+    for rows in (2048, 1024, 128):      # 256 tiles of 256x256, 256 of 128x256, 32 of 128x128
+        _, p = tgc.matmul_all_reduce(xd[:rows].contiguous(), wd, [None], 0, split=1)
+        outs.append(p[:128])
+    xpad = torch.zeros((128, k + 8), dtype=torch.bfloat16, device="cuda")
+    xpad[:, :k] = xd[:128]
+    wpad = torch.zeros((k + 8, n), dtype=torch.bfloat16, device="cuda")
+    wpad[:k] = wd
+    _, p = tgc.matmul_all_reduce(xpad, wpad, [None], 0, split=1)
+    outs.append(p)
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs[1:], 1):
+        assert_bits_equal(o, raw(outs[0]), f"variant {i} vs 256x256 tiles")
+    assert_close(outs[0], oracle.matmul(f64(x[:128], "bf16"), f64(w, "bf16")), "bf16", "rows 0..127")
 
 
 def test_gemm_k_zero_gives_zero_partial():
@@ -114,9 +140,10 @@ def test_all_reduce_random(dtype, split):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-def test_deterministic_bits_independent_of_split_and_run(dtype):
-    log(f"AR det invariance {dtype}")
-    m, n, k, world, rank = 256, 512, 264, 8, 6
+@pytest.mark.parametrize("k", [264, 256])
+def test_deterministic_bits_independent_of_split_and_run(dtype, k):
+    log(f"AR det invariance {dtype} k={k}")
+    m, n, world, rank = 256, 512, 8, 6
     x = synth.normal(WID_TEST + 4, synth.T_X, rank, (m, k), 1.0, dtype)
     w = synth.normal(WID_TEST + 4, synth.T_W, rank, (k, n), 0.02, dtype)
     peers = [dev(q) for q in synth.peers_random(WID_TEST + 4, world, rank, (m, n), 0.33, dtype)]
@@ -136,9 +163,10 @@ def test_deterministic_bits_independent_of_split_and_run(dtype):
 # ------------------------------------------------------------------ reduce-scatter
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("split", [1, 2, 4, 8])
-def test_reduce_scatter(dtype, split):
-    log(f"RS {dtype} split={split}")
-    m, n, k, world, rank = 1024, 520, 264, 8, 5
+@pytest.mark.parametrize("k", [264, 256])
+def test_reduce_scatter(dtype, split, k):
+    log(f"RS {dtype} split={split} k={k}")
+    m, n, world, rank = 1024, 520, 8, 5
     b = m // world
     x = synth.normal(WID_TEST + 5, synth.T_X, rank, (m, k), 1.0, dtype)
     w = synth.normal(WID_TEST + 5, synth.T_W, rank, (k, n), 0.02, dtype)
@@ -172,9 +200,10 @@ def test_reduce_scatter(dtype, split):
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("split", [1, 2, 4, 8])
 @pytest.mark.parametrize("rank", [0, 5])
-def test_allgather_matmul(dtype, split, rank):
-    log(f"AG {dtype} split={split} rank={rank}")
-    world, shard, k, n = 8, 64, 264, 392
+@pytest.mark.parametrize("k", [264, 256])
+def test_allgather_matmul(dtype, split, rank, k):
+    log(f"AG {dtype} split={split} rank={rank} k={k}")
+    world, shard, n = 8, 64, 392
     m = world * shard
     shards = [synth.normal(WID_TEST + 6, synth.T_PEER, r, (shard, k), 1.0, dtype) for r in range(world)]
     w = synth.normal(WID_TEST + 6, synth.T_W, 0, (k, n), 0.02, dtype)
