@@ -32,6 +32,12 @@
 #ifndef COC_COMPUTE_STREAMS
 #define COC_COMPUTE_STREAMS 2
 #endif
+// 1: bf16 / fp16 pipelines with k a multiple of 32 run all chunk matmuls of an
+// op in one chunk-walking launch (hand-over through device counters); 0: one
+// launch per chunk on the two compute streams.
+#ifndef COC_ONE_LAUNCH
+#define COC_ONE_LAUNCH 1
+#endif
 
 namespace coc {
 namespace {
@@ -63,6 +69,13 @@ struct StreamCtx {
     hipEvent_t fork = nullptr;
     hipEvent_t join = nullptr;
     hipEvent_t join2 = nullptr;
+    // Chunk hand-over counters of the one-launch pipeline (device memory):
+    // sync[c] = tiles of chunk c stored, sync[COC_MAX_SPLIT + c] = gather
+    // workgroups of chunk c done.  They only grow; *_sent hold the values all
+    // work enqueued so far brings them to.
+    uint32_t* sync = nullptr;
+    uint32_t done_sent[COC_MAX_SPLIT] = {};
+    uint32_t ready_sent[COC_MAX_SPLIT] = {};
 };
 
 std::mutex g_ctx_mu;
@@ -85,6 +98,9 @@ coc_status get_ctx(hipStream_t main, StreamCtx** out) {
     COC_HIP(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming));
     COC_HIP(hipEventCreateWithFlags(&c->join, hipEventDisableTiming));
     COC_HIP(hipEventCreateWithFlags(&c->join2, hipEventDisableTiming));
+    COC_HIP(hipMalloc(&c->sync, 2 * COC_MAX_SPLIT * sizeof(uint32_t)));
+    COC_HIP(hipMemset(c->sync, 0, 2 * COC_MAX_SPLIT * sizeof(uint32_t)));
+    COC_HIP(hipDeviceSynchronize());
     g_ctx[key] = c;
     *out = c;
     return COC_OK;
@@ -199,6 +215,104 @@ double gemm_flops(const Plan& P, const coc_chunk& c) {
     return 2.0 * double(c.rows_per_blk) * double(c.nblk) * double(P.n) * double(P.k);
 }
 
+ChunksLaunch chunks_for(const Plan& P, const GemmLaunch& g0) {
+    ChunksLaunch L{};
+    L.kind = g0.kind;
+    L.a = g0.a;
+    L.b = g0.b;
+    L.c = g0.c;
+    L.n = g0.n;
+    L.k = g0.k;
+    L.nchunks = P.nchunks;
+    for (int i = 0; i < P.nchunks; ++i) {
+        L.base[i] = P.chunk[i].base;
+        L.stride[i] = P.chunk[i].stride;
+        L.rpb[i] = P.chunk[i].rows_per_blk;
+        L.nblk[i] = P.chunk[i].nblk;
+    }
+    return L;
+}
+
+bool one_launch(const Plan& P, const GemmLaunch& g0) {
+    return COC_ONE_LAUNCH != 0 && P.split > 1 && chunks_supported(g0.kind, g0.k);
+}
+
+// The one-launch all-gather reads gathered rows through the L2, which needs
+// every chunk to start on a 128-byte line (see gemm_ring_chunks).
+bool one_launch_gather(const Plan& P, const GemmLaunch& g0) {
+    return one_launch(P, g0) && (uintptr_t)g0.a % 128 == 0 && (g0.k * (int64_t)elem_size(P.dt)) % 128 == 0;
+}
+
+double total_flops(const Plan& P) {
+    double f = 0;
+    for (int i = 0; i < P.nchunks; ++i) f += gemm_flops(P, P.chunk[i]);
+    return f;
+}
+
+// One-launch pipeline, compute first: the matmul walks the chunks in order on
+// the caller's stream and counts finished tiles per chunk; the reduce of chunk
+// i, on the side stream from the start, waits for chunk i's count.  The host
+// enqueues the matmul before the reduces, so if both streams shared one
+// hardware queue the matmul would simply finish first.
+coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const ReduceLaunch& r0,
+                                    hipStream_t main) {
+    StreamCtx* c = nullptr;
+    COC_TRY(get_ctx(main, &c));
+    const size_t es = elem_size(P.dt);
+    COC_HIP(hipEventRecord(c->fork, main));
+    COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
+    ChunksLaunch L = chunks_for(P, g0);
+    L.done = c->sync;
+    int32_t tiles[COC_MAX_SPLIT];
+    COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
+    uint32_t target[COC_MAX_SPLIT];
+    for (int i = 0; i < P.nchunks; ++i) target[i] = c->done_sent[i] += (uint32_t)tiles[i];
+    for (int i = 0; i < P.nchunks; ++i) {
+        ReduceLaunch r = r0;
+        r.src_row0 = P.chunk[i].red_base;
+        r.dst_row0 = P.chunk[i].out_base;
+        r.rows = P.chunk[i].red_rows;
+        r.wait = c->sync + i;
+        r.wait_target = target[i];
+        r.own = P.rank;
+        const double bytes = double(r.nsrc + 1) * double(r.rows) * double(P.n) * double(es);
+        COC_TRY(launch(KC_REDUCE, bytes, c->side, [&] { return launch_reduce(r, c->side); }));
+    }
+    COC_HIP(hipEventRecord(c->join, c->side));
+    COC_HIP(hipStreamWaitEvent(main, c->join, 0));
+    return COC_OK;
+}
+
+// One-launch pipeline, communicate first: the gathers of all chunks go to the
+// side stream first, each workgroup counting itself done; the matmul then
+// walks the chunks on the caller's stream and waits for chunk i's count
+// before its first tile of chunk i.
+coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const GatherLaunch& a0,
+                                 hipStream_t main) {
+    StreamCtx* c = nullptr;
+    COC_TRY(get_ctx(main, &c));
+    const size_t es = elem_size(P.dt);
+    COC_HIP(hipEventRecord(c->fork, main));
+    COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
+    ChunksLaunch L = chunks_for(P, g0);
+    L.ready = c->sync + COC_MAX_SPLIT;
+    for (int i = 0; i < P.nchunks; ++i) {
+        GatherLaunch a = a0;
+        a.row0 = P.chunk[i].red_base;
+        a.rows = P.chunk[i].red_rows;
+        a.signal = c->sync + COC_MAX_SPLIT + i;
+        int32_t groups = 0;
+        const double bytes = 2.0 * double(a.rows) * double(P.k) * double(es);
+        COC_TRY(launch(KC_GATHER, bytes, c->side, [&] { return launch_gather(a, c->side, &groups); }));
+        L.ready_target[i] = c->ready_sent[i] += (uint32_t)groups;
+    }
+    int32_t tiles[COC_MAX_SPLIT];
+    COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
+    COC_HIP(hipEventRecord(c->join, c->side));
+    COC_HIP(hipStreamWaitEvent(main, c->join, 0));
+    return COC_OK;
+}
+
 // Compute first, then reduce: all-reduce, reduce-scatter, w8a16 all-reduce.
 coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLaunch& r0,
                              hipStream_t main) {
@@ -219,6 +333,7 @@ coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLa
         COC_TRY(gemm(0, main));
         return reduce(0, main);
     }
+    if (one_launch(P, g0)) return run_compute_first_chunks(P, g0, r0, main);
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
     COC_HIP(hipEventRecord(c->fork, main));
@@ -256,6 +371,7 @@ coc_status run_comm_first(const Plan& P, const GemmLaunch& g0, const GatherLaunc
         COC_TRY(gather(0, main));
         return gemm(0, main);
     }
+    if (one_launch_gather(P, g0)) return run_comm_first_chunks(P, g0, a0, main);
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
     COC_HIP(hipEventRecord(c->fork, main));

@@ -68,6 +68,9 @@ struct ReduceLaunch {
     int32_t nsrc;
     void* dst;
     int64_t src_row0, dst_row0, rows, n;
+    const uint32_t* wait;    // if set, the kernel first waits for *wait >= wait_target
+    uint32_t wait_target;
+    int32_t own;             // with wait: index of the source being written meanwhile
 };
 
 // Bit copy of gathered rows: dst[row] = shard (row / shard_rows), local row
@@ -79,12 +82,36 @@ struct GatherLaunch {
     int64_t shard_rows;
     void* dst;
     int64_t row0, rows, k;
+    uint32_t* signal;        // if set, each workgroup adds 1 once its rows are stored
+};
+
+// Matmul over every chunk of an op in one launch (bf16 / fp16, k a positive
+// multiple of 32): chunk c's rows come from its row map.  Before its first
+// tile of chunk c a workgroup waits for ready[c] >= ready_target[c] (if ready
+// is set); after each tile of chunk c it adds 1 to done[c] (if done is set).
+struct ChunksLaunch {
+    GemmKind kind;
+    const void* a;
+    const void* b;
+    void* c;
+    int64_t n, k;
+    int32_t nchunks;
+    int64_t base[COC_MAX_SPLIT], stride[COC_MAX_SPLIT], rpb[COC_MAX_SPLIT];
+    int32_t nblk[COC_MAX_SPLIT];
+    uint32_t* done;
+    const uint32_t* ready;
+    uint32_t ready_target[COC_MAX_SPLIT];
 };
 
 // Launchers (kernels.hip).  Return a hipError_t value (0 = success).  The
 // caller guarantees that every size and pointer has been validated.
 int launch_gemm(const GemmLaunch& g, void* stream);
 int launch_reduce(const ReduceLaunch& r, void* stream);
-int launch_gather(const GatherLaunch& g, void* stream);
+// *groups (if given) receives the number of workgroups launched (signals sent).
+int launch_gather(const GatherLaunch& g, void* stream, int32_t* groups = nullptr);
+
+bool chunks_supported(GemmKind kind, int64_t k);
+// tiles[c] receives the tile count of chunk c (the completions done[c] gets).
+int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[COC_MAX_SPLIT]);
 
 }  // namespace coc

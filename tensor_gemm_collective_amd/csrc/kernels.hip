@@ -115,15 +115,92 @@ __device__ __forceinline__ int xcd_tile(int b, int total) {
     return x * q + (x < r ? x : r) + local;
 }
 
-__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int* tm, int* tn) {
+__device__ __forceinline__ void grouped_coords(int t, int tiles_m, int tiles_n, int* tm, int* tn) {
     constexpr int GM = 4;
-    const int t = xcd_tile(b, tiles_m * tiles_n);
     const int per_group = GM * tiles_n;
     const int g = t / per_group;
     const int rows_in_group = (tiles_m - g * GM) < GM ? (tiles_m - g * GM) : GM;
     const int in_g = t - g * per_group;
     *tm = g * GM + in_g % rows_in_group;
     *tn = in_g / rows_in_group;
+}
+
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int* tm, int* tn) {
+    grouped_coords(xcd_tile(b, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
+}
+
+// ------------------------------------------------------------------ cross-kernel sync
+// Counters in device memory let one chunk-walking matmul kernel and the
+// reduce / gather kernels beside it on another stream hand chunks over without
+// a kernel boundary.  The data handed over is written with system-scope
+// (write-through, sc0 sc1) stores, and the reduce reads the matmul's partials
+// with system-scope loads, so no L2 writeback or invalidate is needed: a
+// producer waits for its stores to complete, then bumps the counter; a
+// consumer polls the counter, then loads.  (Device-scope fences here would
+// write back or invalidate a whole XCD L2 per workgroup, dropping the cached
+// weight tiles of the matmul running beside.)  Counters only grow (mod 2^32);
+// the host tracks the value each wait must reach.  Waits are bounded: on
+// time-out the waiting kernel writes NaN instead of results and carries on,
+// so a lost signal shows up in the output instead of hanging the GPU.
+constexpr uint32_t kSpinLimit = 1u << 19;   // polls, ~2 s at the longest sleep
+// Scope of the counter loads and adds (the data itself is always written and
+// read at system scope).
+#ifndef COC_SYNC_SYSTEM
+#define COC_SYNC_SYSTEM 0
+#endif
+constexpr int kSyncScope = COC_SYNC_SYSTEM ? __HIP_MEMORY_SCOPE_SYSTEM : __HIP_MEMORY_SCOPE_AGENT;
+
+// Polls back off from ~0.1 us to ~4 us between loads: hundreds of workgroups
+// polling one counter at a fixed short interval load its HBM channel enough to
+// slow every other stream through it.
+__device__ __forceinline__ bool spin_until(const uint32_t* p, uint32_t target) {
+    for (uint32_t i = 0; i < kSpinLimit; ++i) {
+        const uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, kSyncScope);
+        if ((int32_t)(v - target) >= 0) return true;
+        if (i < 4) __builtin_amdgcn_s_sleep(2);
+        else if (i < 8) __builtin_amdgcn_s_sleep(16);
+        else __builtin_amdgcn_s_sleep(127);
+    }
+    return false;
+}
+
+// Workgroup-wide wait for *p >= target: thread 0 polls and the outcome goes to
+// every wave through LDS.  The barrier orders every later load after the
+// poll.  Two calls must be separated by a workgroup barrier (the flag is
+// reused).
+__device__ __forceinline__ bool wg_wait(const uint32_t* p, uint32_t target) {
+    __shared__ int ok;
+    if (threadIdx.x == 0) ok = spin_until(p, target) ? 1 : 0;
+    __syncthreads();
+    return ok != 0;
+}
+
+// Workgroup-wide signal after system-scope stores: every wave waits for its
+// stores to complete, then one thread adds 1 to the counter.
+__device__ __forceinline__ void wg_signal(uint32_t* p) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, kSyncScope);
+}
+
+// 16-byte system-scope stores go through a buffer resource over the whole
+// output (byte offsets < 4 GiB: every matrix has fewer than 2^31 elements):
+// one buffer_store_dwordx4 with sc0 sc1 (cache-policy bits 0 and 4), measured
+// as fast as a plain store, where two 8-byte atomic stores run at ~60 %.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sys_rsrc(uint8_t* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)0xffffffff, 0x00020000);
+}
+__device__ __forceinline__ void store16_sys(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, 17);
+}
+
+__device__ __forceinline__ u32x4 load16_sys(const uint8_t* src) {
+    const u32x2 lo = __builtin_bit_cast(u32x2, __hip_atomic_load((const uint64_t*)src, __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_SYSTEM));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __hip_atomic_load((const uint64_t*)(src + 8), __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_SYSTEM));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
 // ------------------------------------------------------------------ MFMA GEMMs
@@ -655,8 +732,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
 //   * The k walk (16-k MFMA steps in increasing k, same operand roles) is the
 //     one every other kernel here uses, so results are bitwise identical to
 //     theirs.
-template <int BM, int BN, int S, int WM, int WN, int KIND>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_ring(GemmParams p) {
+template <int BM, int BN, int S, int WM, int WN>
+constexpr int ring_lds_bytes() { return S * (BM * 32 * 2 + 32 * BN * 2); }
+
+// One BM x BN output tile at (m0, n0) of a chunk with row map (rows, rpb,
+// base, stride).  `sm` is the workgroup's LDS ring; the caller guarantees that
+// every wave has finished with it and has no stores outstanding.  poison:
+// store NaN instead of the products (a wait for the tile's inputs timed out).
+// SYS: system-scope (write-through) stores, for a tile another kernel reads
+// while this one runs.
+template <int BM, int BN, int S, int WM, int WN, int KIND, bool SYS = false>
+__device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb, int64_t base, int64_t stride,
+                                          int m0, int n0, uint8_t* sm, bool poison) {
     constexpr int BK = 32, NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE = A_BYTES + B_BYTES;
@@ -669,14 +756,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring(GemmParams p) {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32 x 32 MFMA blocks");
     static_assert(BROW >= 16 && BROW <= 64, "weight swizzle works on 16-chunk groups");
     static_assert(S >= 3 && S * STAGE <= 160 * 1024, "LDS ring");
-    __shared__ __attribute__((aligned(1024))) uint8_t sm[S * STAGE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
-    const int m0 = tm * BM, n0 = tn * BN;
     const uint32_t lds0 = lds_u32(sm);
 
     // load offsets from the stage's global base (bytes)
@@ -684,8 +767,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < APW; ++i) {
         const int row = (wave * APW + i) * 16 + (lane >> 2);
-        const int r = m0 + row < p.rows ? m0 + row : p.rows - 1;
-        const int64_t gr = map_row(r, p.rpb, p.base, p.stride);
+        const int r = m0 + row < rows ? m0 + row : rows - 1;
+        const int64_t gr = map_row(r, rpb, base, stride);
         aof[i] = (uint32_t)(gr * p.k * 2) + (((lane & 3) ^ gA<32>(row)) << 4);
     }
 #pragma unroll
@@ -792,24 +875,123 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring(GemmParams p) {
     for (; kt + 1 < KT; ++kt) stage(kt, no{}, yes{}, std::integral_constant<int, 0>{});
     stage(kt, no{}, no{}, std::integral_constant<int, 0>{});
 
-    // epilogue: lane holds n = q*8 + (lane/32)*4 + {0..3} of row m = lane%32
+    if (poison) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int r = m0 + wm * WTM + i * 32 + (lane & 31);
-        if (r >= p.rows) continue;
-        uint8_t* crow = p.c + map_row(r, p.rpb, p.base, p.stride) * (int64_t)p.n * 2;
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_nanf("");
+    }
+
+    // Epilogue through LDS.  A lane holds n = q*8 + (lane/32)*4 + {0..3} of row
+    // m = lane%32 in each 32 x 32 block; stored directly that gives 16-byte
+    // pieces of 32 rows per instruction.  Instead each wave (once the whole
+    // workgroup is off the ring) writes its WTM x WTN tile, in the storage
+    // dtype, into its own LDS region (rows of WTN*2 bytes, 16-byte chunk c of
+    // row r at c ^ (r & 7)) and reads it back 16 bytes per lane, WTN/8 lanes
+    // per row: every store instruction then writes whole rows of WTN*2
+    // contiguous bytes (whole 128-byte lines).
+    constexpr int RP = WTN * 2;     // staged row pitch (bytes)
+    constexpr int CPR = WTN / 8;    // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;   // rows per store instruction
+    static_assert(CPR % 8 == 0 && 64 % CPR == 0 && WTM % RPI == 0, "staging layout");
+    static_assert(NW * WTM * RP <= S * STAGE, "staging fits in the ring");
+    block_barrier();
+    // An opaque copy of the lane index: in the chunk-walking kernel the
+    // compiler would otherwise hoist these lane-only LDS addresses out of the
+    // tile loop and hold them in registers through the main loop.
+    int el;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
+    COC_LDS uint8_t* stg = (COC_LDS uint8_t*)sm + wave * (WTM * RP);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
-                if (col < p.n) {
-                    u32x2 v;
-                    v[0] = pack2<OUT_DT>(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-                    v[1] = pack2<OUT_DT>(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-                    *(u32x2*)(crow + (int64_t)col * 2) = v;
-                }
+                const int row = i * 32 + (el & 31);
+                u32x2 v;
+                v[0] = pack2<OUT_DT>(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+                v[1] = pack2<OUT_DT>(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+                *(COC_LDS u32x2*)(stg + row * RP + (((j * 4 + q) ^ (row & 7)) << 4) + (el >> 5) * 8) = v;
             }
+    // (keeps the store addresses below from being computed while the
+    // accumulators are still live)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < WTM / RPI; ++t) {
+        const int row = t * RPI + el / CPR, ch = el % CPR;
+        const u32x4 v = *(const COC_LDS u32x4*)(stg + row * RP + ((ch ^ (row & 7)) << 4));
+        const int r = m0 + wm * WTM + row, col = n0 + wn * WTN + ch * 8;
+        if (r < rows && col < p.n) {
+            const int64_t off = map_row(r, rpb, base, stride) * (int64_t)p.n * 2 + (int64_t)col * 2;
+            if constexpr (SYS)
+                store16_sys(sys_rsrc(p.c), (uint32_t)off, v);
+            else
+                *(u32x4*)(p.c + off) = v;
+        }
+    }
+}
+
+template <int BM, int BN, int S, int WM, int WN, int KIND>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_ring(GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t sm[ring_lds_bytes<BM, BN, S, WM, WN>()];
+    int tm, tn;
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
+    ring_tile<BM, BN, S, WM, WN, KIND>(p, p.rows, p.rpb, p.base, p.stride, tm * BM, tn * BN, sm, false);
+}
+
+// Chunk-walking form of the ring kernel: one launch covers every chunk of an
+// op.  8 * per_xcd workgroups (one per CU for the 256-wide tiles, two for
+// 128 x 128); workgroup b runs on XCD b % 8 and walks that XCD's tile list:
+// chunk by chunk in pipeline order, within a chunk the XCD's run of
+// xcd_tile's split in grouped order, taking every per_xcd-th item.  Chunk c
+// can wait for ready[c] (gathered rows in place) before its first tile; with
+// SIGNAL, tiles are stored write-through and each adds 1 to done[c].  The
+// gathered rows are read through the L2 as usual: no line of chunk c can be
+// cached before its wait (rows are whole 128-byte lines and nothing reads
+// them earlier in this launch), and the gather writes them through.
+struct PersistParams {
+    GemmParams g;   // a, b, c, n, k, tiles_n (row map fields unused)
+    int64_t base[COC_MAX_SPLIT], stride[COC_MAX_SPLIT];
+    int32_t rpb[COC_MAX_SPLIT], rows[COC_MAX_SPLIT], tiles_m[COC_MAX_SPLIT];
+    int32_t nchunks, per_xcd;
+    uint32_t* done;
+    const uint32_t* ready;
+    uint32_t ready_target[COC_MAX_SPLIT];
+};
+
+template <int BM, int BN, int S, int WM, int WN, int KIND, bool SIGNAL>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P) {
+    __shared__ __attribute__((aligned(1024))) uint8_t sm[ring_lds_bytes<BM, BN, S, WM, WN>()];
+    constexpr int NX = 8;
+    const int x = blockIdx.x % NX, w = blockIdx.x / NX;
+    const int tn_all = P.g.tiles_n;
+    int waited = -1;
+    bool ok = true;
+    for (int j = w;; j += P.per_xcd) {
+        int c = 0, jj = j;
+        for (; c < P.nchunks; ++c) {
+            const int T = P.tiles_m[c] * tn_all;
+            const int cnt = T / NX + (x < T % NX ? 1 : 0);
+            if (jj < cnt) break;
+            jj -= cnt;
+        }
+        if (c >= P.nchunks) break;
+        const int T = P.tiles_m[c] * tn_all;
+        int tm, tn;
+        grouped_coords(x * (T / NX) + (x < T % NX ? x : T % NX) + jj, P.tiles_m[c], tn_all, &tm, &tn);
+        if (P.ready != nullptr && c != waited) {
+            ok = wg_wait(P.ready + c, P.ready_target[c]);
+            waited = c;
+        }
+        // the previous tile's stores are done and every wave is off the LDS ring
+        wait_vmcnt<0>();
+        block_barrier();
+        ring_tile<BM, BN, S, WM, WN, KIND, SIGNAL>(P.g, P.rows[c], P.rpb[c], P.base[c], P.stride[c], tm * BM,
+                                                   tn * BN, sm, !ok);
+        if constexpr (SIGNAL) wg_signal(P.done + c);
     }
 }
 
@@ -886,6 +1068,9 @@ struct ReduceParams {
     int32_t nsrc;
     int32_t vpr;         // 16-byte vectors per row
     int32_t total;       // rows * vpr
+    const uint32_t* wait;   // if set, first wait for *wait >= wait_target
+    uint32_t wait_target;
+    int32_t own;            // with wait: the source written while this kernel waits
 };
 
 // Two sources are loaded at a time and added in rank order before the next
@@ -958,6 +1143,54 @@ __global__ __launch_bounds__(256) void reduce_rows(ReduceParams p) {
     }
 }
 
+// The reduce that runs beside the one-launch matmul and waits for its chunk's
+// tiles; the partial written meanwhile (source `own`) is read with
+// system-scope loads.  It is launched with at most one workgroup per CU, so
+// however the hardware orders the two launches, every CU keeps room for the
+// matmul's workgroup (the wait could otherwise hold slots the matmul needs).
+// To keep HBM busy with that few waves, each thread loads all sources of a
+// 16-byte vector before adding them (same rank order, same binary32 sums).
+template <int DT>
+__global__ __launch_bounds__(256) void reduce_rows_wait(ReduceParams p) {
+    constexpr int E = (DT == COC_F32) ? 4 : 8;
+    const bool ok = p.wait == nullptr || wg_wait(p.wait, p.wait_target);
+    const int stride = gridDim.x * 256;
+    for (int v = blockIdx.x * 256 + threadIdx.x; v < p.total; v += stride) {
+        const int row = v / p.vpr;
+        const int cv = v - row * p.vpr;
+        const int64_t so = (p.src_row0 + row) * p.row_bytes + (int64_t)cv * 16;
+        const int64_t dof = (p.dst_row0 + row) * p.row_bytes + (int64_t)cv * 16;
+        u32x4 x[COC_MAX_WORLD];
+#pragma unroll
+        for (int s = 0; s < COC_MAX_WORLD; ++s)
+            if (s < p.nsrc) x[s] = s == p.own ? load16_sys(p.src[s] + so) : *(const u32x4*)(p.src[s] + so);
+        float acc[E];
+        if constexpr (DT == COC_F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __uint_as_float(x[0][e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = unpack_lo<DT>(x[0][e]);
+                acc[2 * e + 1] = unpack_hi<DT>(x[0][e]);
+            }
+        }
+#pragma unroll
+        for (int s = 1; s < COC_MAX_WORLD; ++s)
+            if (s < p.nsrc) acc_add<DT>(acc, x[s]);
+        u32x4 out;
+        if constexpr (DT == COC_F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = __float_as_uint(acc[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = pack2<DT>(acc[2 * e], acc[2 * e + 1]);
+        }
+        if (!ok) out = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};   // NaN in every format
+        *(u32x4*)(p.dst + dof) = out;
+    }
+}
+
 // ------------------------------------------------------------------ gather
 // dst row g (g in [row0, row0 + rows)) = row g % shard_rows of shard
 // g / shard_rows; 16-byte vector copies.
@@ -969,6 +1202,7 @@ struct GatherParams {
     int32_t row0;
     int32_t vpr;
     int32_t total;
+    uint32_t* signal;    // if set, each workgroup adds 1 when its rows are stored
 };
 
 __global__ __launch_bounds__(256) void gather_rows(GatherParams p) {
@@ -984,8 +1218,13 @@ __global__ __launch_bounds__(256) void gather_rows(GatherParams p) {
         for (int i = 1; i < COC_MAX_WORLD; ++i)
             if (s == i) sp = p.src[i];
         const u32x4 x = *(const u32x4*)(sp + (int64_t)local * p.row_bytes + (int64_t)cv * 16);
-        *(u32x4*)(p.dst + (int64_t)g * p.row_bytes + (int64_t)cv * 16) = x;
+        const int64_t off = (int64_t)g * p.row_bytes + (int64_t)cv * 16;
+        if (p.signal != nullptr)
+            store16_sys(sys_rsrc(p.dst), (uint32_t)off, x);   // read by a matmul already running
+        else
+            *(u32x4*)(p.dst + off) = x;
     }
+    if (p.signal != nullptr) wg_signal(p.signal);
 }
 
 int grid_for(int64_t total_vec) {
@@ -1090,7 +1329,20 @@ int launch_reduce(const ReduceLaunch& r, void* stream) {
     p.nsrc = r.nsrc;
     p.vpr = (int32_t)(p.row_bytes / 16);
     p.total = (int32_t)(r.rows * p.vpr);
+    p.wait = r.wait;
+    p.wait_target = r.wait_target;
+    p.own = r.wait != nullptr ? r.own : -1;
     hipStream_t s = (hipStream_t)stream;
+    if (p.wait != nullptr) {
+        const int grid = grid_for(p.total) < 256 ? grid_for(p.total) : 256;   // at most one per CU
+        switch (r.dt) {
+            case COC_F32: hipLaunchKernelGGL(reduce_rows_wait<COC_F32>, dim3(grid), dim3(256), 0, s, p); break;
+            case COC_F16: hipLaunchKernelGGL(reduce_rows_wait<COC_F16>, dim3(grid), dim3(256), 0, s, p); break;
+            case COC_BF16: hipLaunchKernelGGL(reduce_rows_wait<COC_BF16>, dim3(grid), dim3(256), 0, s, p); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     const int grid = grid_for(p.total);
     switch (r.dt) {
         case COC_F32: hipLaunchKernelGGL(reduce_rows<COC_F32>, dim3(grid), dim3(256), 0, s, p); break;
@@ -1101,7 +1353,8 @@ int launch_reduce(const ReduceLaunch& r, void* stream) {
     return hipGetLastError();
 }
 
-int launch_gather(const GatherLaunch& g, void* stream) {
+int launch_gather(const GatherLaunch& g, void* stream, int32_t* groups) {
+    if (groups != nullptr) *groups = 0;
     if (g.rows == 0 || g.k == 0) return hipSuccess;
     GatherParams p{};
     for (int i = 0; i < COC_MAX_WORLD; ++i) p.src[i] = (const uint8_t*)(i < g.nsrc ? g.src[i] : g.src[0]);
@@ -1111,9 +1364,82 @@ int launch_gather(const GatherLaunch& g, void* stream) {
     p.row0 = (int32_t)g.row0;
     p.vpr = (int32_t)(p.row_bytes / 16);
     p.total = (int32_t)(g.rows * p.vpr);
+    p.signal = g.signal;
     hipStream_t s = (hipStream_t)stream;
-    hipLaunchKernelGGL(gather_rows, dim3(grid_for(p.total)), dim3(256), 0, s, p);
+    // with a signal, at most 256 workgroups: their adds to the one counter
+    // are serialised (~8 ns each)
+    const int grid = g.signal != nullptr && grid_for(p.total) > 256 ? 256 : grid_for(p.total);
+    hipLaunchKernelGGL(gather_rows, dim3(grid), dim3(256), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess && groups != nullptr) *groups = grid;
+    return e;
+}
+
+bool chunks_supported(GemmKind kind, int64_t k) {
+    return (kind == GK_BF16 || kind == GK_F16) && k >= 32 && k % 32 == 0;
+}
+
+namespace {
+
+template <int BM, int BN, int S, int WM, int WN, int KIND>
+hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s, int32_t* tiles) {
+    PersistParams P{};
+    P.g.a = (const uint8_t*)L.a;
+    P.g.b = (const uint8_t*)L.b;
+    P.g.c = (uint8_t*)L.c;
+    P.g.n = (int32_t)L.n;
+    P.g.k = (int32_t)L.k;
+    P.g.tiles_n = (int32_t)((L.n + BN - 1) / BN);
+    P.nchunks = L.nchunks;
+    int64_t longest = 0;   // XCD 0's list: ceil(T_c / 8) summed over chunks
+    for (int c = 0; c < L.nchunks; ++c) {
+        const int64_t rows = L.rpb[c] * L.nblk[c];
+        P.base[c] = L.base[c];
+        P.stride[c] = L.stride[c];
+        P.rpb[c] = (int32_t)(L.rpb[c] > 0 ? L.rpb[c] : 1);
+        P.rows[c] = (int32_t)rows;
+        P.tiles_m[c] = (int32_t)((rows + BM - 1) / BM);
+        tiles[c] = P.tiles_m[c] * P.g.tiles_n;
+        longest += (tiles[c] + 7) / 8;
+        P.ready_target[c] = L.ready_target[c];
+    }
+    P.done = L.done;
+    P.ready = L.ready;
+    const int64_t cap = 32 * per_cu;   // 256 CUs / 8 XCDs, times workgroups per CU
+    P.per_xcd = (int32_t)(longest < cap ? (longest > 0 ? longest : 1) : cap);
+    if (P.done != nullptr)
+        hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true>), dim3(8 * P.per_xcd), dim3(64 * WM * WN),
+                           0, s, P);
+    else
+        hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, false>), dim3(8 * P.per_xcd),
+                           dim3(64 * WM * WN), 0, s, P);
     return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* tiles) {
+    // largest tile that still fills the 256 CUs once over the whole op
+    int64_t t256 = 0, t128x256 = 0;
+    for (int c = 0; c < L.nchunks; ++c) {
+        const int64_t rows = L.rpb[c] * L.nblk[c];
+        t256 += ((rows + 255) / 256) * ((L.n + 255) / 256);
+        t128x256 += ((rows + 127) / 128) * ((L.n + 255) / 256);
+    }
+    if (t256 >= 256) return launch_chunks_shape<256, 256, 4, 2, 4, KIND>(L, 1, s, tiles);
+    if (t128x256 >= 256) return launch_chunks_shape<128, 256, 4, 2, 4, KIND>(L, 1, s, tiles);
+    return launch_chunks_shape<128, 128, 4, 2, 2, KIND>(L, 2, s, tiles);
+}
+
+}  // namespace
+
+int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[COC_MAX_SPLIT]) {
+    for (int c = 0; c < COC_MAX_SPLIT; ++c) tiles[c] = 0;
+    hipStream_t s = (hipStream_t)stream;
+    switch (L.kind) {
+        case GK_F16: return launch_chunks_kind<GK_F16>(L, s, tiles);
+        case GK_BF16: return launch_chunks_kind<GK_BF16>(L, s, tiles);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace coc

@@ -347,3 +347,44 @@ def test_stream_order_without_host_sync():
     s.synchronize()
     for o in outs:
         assert_bits_equal(o, y_ref, "consumer on caller stream")
+
+
+# ------------------------------------------------------------------ one-launch pipeline hand-over
+@pytest.mark.parametrize("split", [2, 4, 8])
+def test_pipeline_handover_reuses_buffers_without_stale_rows(split):
+    """Two input sets alternate through the same output / gathered buffers, so
+    any row the matmul read or the reduce saw from the previous call would show
+    up.  Results must match split 1 (one serial matmul, no hand-over) bit for
+    bit, and the gathered rows the shards exactly."""
+    log(f"pipeline hand-over, split={split}")
+    world, rank, shard, k, n = 8, 2, 512, 1024, 2048
+    m = world * shard
+    sets = []
+    for tag in (13, 14):
+        shards = [synth.normal(WID_TEST + tag, synth.T_PEER, r, (shard, k), 1.0, "bf16") for r in range(world)]
+        x = synth.normal(WID_TEST + tag, synth.T_X, rank, (m, k), 1.0, "bf16")
+        peers = synth.peers_random(WID_TEST + tag, world, rank, (m, n), 0.3, "bf16")
+        sets.append(([dev(s) for s in shards], dev(x), [dev(q) for q in peers]))
+    w = dev(synth.normal(WID_TEST + 13, synth.T_W, 0, (k, n), 0.02, "bf16"))
+    refs = []
+    for shards, x, peers in sets:
+        ag = tgc.allgather_matmul(shards[rank], [None if r == rank else shards[r] for r in range(world)], w, rank,
+                                  split=1)
+        ar, part = tgc.matmul_all_reduce(x, w, peers, rank, split=1, deterministic=1)
+        refs.append((ag, ar, part))
+    torch.cuda.synchronize()
+    y_ag = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    y_ar = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    p_ar = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    for it in range(4):
+        shards, x, peers = sets[it % 2]
+        ref_ag, ref_ar, ref_p = refs[it % 2]
+        tgc.allgather_matmul(shards[rank], [None if r == rank else shards[r] for r in range(world)], w, rank,
+                             y=y_ag, gathered_out=g, v2=True, split=split)
+        tgc.matmul_all_reduce(x, w, peers, rank, y=y_ar, partial_out=p_ar, split=split, deterministic=1)
+        torch.cuda.synchronize()
+        assert_bits_equal(g, torch.cat(shards), f"gathered rows, call {it}")
+        assert_bits_equal(y_ag, ref_ag, f"all-gather matmul, call {it}")
+        assert_bits_equal(p_ar, ref_p, f"partial, call {it}")
+        assert_bits_equal(y_ar, ref_ar, f"all-reduce, call {it}")
