@@ -69,10 +69,10 @@ struct StreamCtx {
     hipEvent_t fork = nullptr;
     hipEvent_t join = nullptr;
     hipEvent_t join2 = nullptr;
-    // Chunk hand-over counters of the one-launch pipeline (device memory):
-    // sync[c] = tiles of chunk c stored, sync[COC_MAX_SPLIT + c] = gather
-    // workgroups of chunk c done.  They only grow; *_sent hold the values all
-    // work enqueued so far brings them to.
+    // Chunk hand-over counters of the one-launch pipeline (device memory,
+    // layout in coc_internal.h): tiles of chunk c stored, gather workgroups
+    // of chunk c done.  They only grow; *_sent hold the values all work
+    // enqueued so far brings them to.
     uint32_t* sync = nullptr;
     uint32_t done_sent[COC_MAX_SPLIT] = {};
     uint32_t ready_sent[COC_MAX_SPLIT] = {};
@@ -98,8 +98,8 @@ coc_status get_ctx(hipStream_t main, StreamCtx** out) {
     COC_HIP(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming));
     COC_HIP(hipEventCreateWithFlags(&c->join, hipEventDisableTiming));
     COC_HIP(hipEventCreateWithFlags(&c->join2, hipEventDisableTiming));
-    COC_HIP(hipMalloc(&c->sync, 2 * COC_MAX_SPLIT * sizeof(uint32_t)));
-    COC_HIP(hipMemset(c->sync, 0, 2 * COC_MAX_SPLIT * sizeof(uint32_t)));
+    COC_HIP(hipMalloc(&c->sync, kSyncLines * kSyncWords * sizeof(uint32_t)));
+    COC_HIP(hipMemset(c->sync, 0, kSyncLines * kSyncWords * sizeof(uint32_t)));
     COC_HIP(hipDeviceSynchronize());
     g_ctx[key] = c;
     *out = c;
@@ -215,22 +215,39 @@ double gemm_flops(const Plan& P, const coc_chunk& c) {
     return 2.0 * double(c.rows_per_blk) * double(c.nblk) * double(P.n) * double(P.k);
 }
 
+// One piece per chunk, A and output rows by the chunk's row map.
 ChunksLaunch chunks_for(const Plan& P, const GemmLaunch& g0) {
     ChunksLaunch L{};
     L.kind = g0.kind;
-    L.a = g0.a;
     L.b = g0.b;
     L.c = g0.c;
     L.n = g0.n;
     L.k = g0.k;
-    L.nchunks = P.nchunks;
+    L.npieces = P.nchunks;
     for (int i = 0; i < P.nchunks; ++i) {
+        L.a[i] = g0.a;
+        L.ashift[i] = 0;
         L.base[i] = P.chunk[i].base;
         L.stride[i] = P.chunk[i].stride;
         L.rpb[i] = P.chunk[i].rows_per_blk;
         L.nblk[i] = P.chunk[i].nblk;
+        L.wait[i] = -1;
+        L.signal[i] = -1;
     }
     return L;
+}
+
+void add_piece(ChunksLaunch* L, const void* a, int64_t ashift, int64_t row0, int64_t rows, int32_t wait) {
+    if (rows <= 0) return;
+    const int i = L->npieces++;
+    L->a[i] = a;
+    L->ashift[i] = ashift;
+    L->base[i] = row0;
+    L->stride[i] = 0;
+    L->rpb[i] = rows;
+    L->nblk[i] = 1;
+    L->wait[i] = wait;
+    L->signal[i] = -1;
 }
 
 bool one_launch(const Plan& P, const GemmLaunch& g0) {
@@ -262,22 +279,24 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
     COC_HIP(hipEventRecord(c->fork, main));
     COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
     ChunksLaunch L = chunks_for(P, g0);
+    for (int i = 0; i < P.nchunks; ++i) L.signal[i] = i;
     L.done = c->sync;
-    int32_t tiles[COC_MAX_SPLIT];
+    int32_t tiles[kMaxPieces];
     COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
-    uint32_t target[COC_MAX_SPLIT];
-    for (int i = 0; i < P.nchunks; ++i) target[i] = c->done_sent[i] += (uint32_t)tiles[i];
+    ReduceChunksLaunch R{};
+    R.r = r0;
+    R.nchunks = P.nchunks;
+    R.done = c->sync;
+    R.own = P.rank;
+    double bytes = 0;
     for (int i = 0; i < P.nchunks; ++i) {
-        ReduceLaunch r = r0;
-        r.src_row0 = P.chunk[i].red_base;
-        r.dst_row0 = P.chunk[i].out_base;
-        r.rows = P.chunk[i].red_rows;
-        r.wait = c->sync + i;
-        r.wait_target = target[i];
-        r.own = P.rank;
-        const double bytes = double(r.nsrc + 1) * double(r.rows) * double(P.n) * double(es);
-        COC_TRY(launch(KC_REDUCE, bytes, c->side, [&] { return launch_reduce(r, c->side); }));
+        R.target[i] = c->done_sent[i] += (uint32_t)tiles[i];
+        R.src_row0[i] = P.chunk[i].red_base;
+        R.dst_row0[i] = P.chunk[i].out_base;
+        R.rows[i] = P.chunk[i].red_rows;
+        bytes += double(r0.nsrc + 1) * double(R.rows[i]) * double(P.n) * double(es);
     }
+    COC_TRY(launch(KC_REDUCE, bytes, c->side, [&] { return launch_reduce_chunks(R, c->side); }));
     COC_HIP(hipEventRecord(c->join, c->side));
     COC_HIP(hipStreamWaitEvent(main, c->join, 0));
     return COC_OK;
@@ -285,8 +304,10 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
 
 // One-launch pipeline, communicate first: the gathers of all chunks go to the
 // side stream first, each workgroup counting itself done; the matmul then
-// walks the chunks on the caller's stream and waits for chunk i's count
-// before its first tile of chunk i.
+// walks the chunks on the caller's stream.  It starts with this rank's own
+// shard, read straight from x_shard (nothing to wait for), then each chunk's
+// other rows from the gathered matrix once that chunk's gather is counted
+// complete.
 coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const GatherLaunch& a0,
                                  hipStream_t main) {
     StreamCtx* c = nullptr;
@@ -294,19 +315,31 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
     const size_t es = elem_size(P.dt);
     COC_HIP(hipEventRecord(c->fork, main));
     COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
-    ChunksLaunch L = chunks_for(P, g0);
-    L.ready = c->sync + COC_MAX_SPLIT;
+    const int64_t shard = P.m / P.world;
+    const int64_t own0 = P.rank * shard, own1 = own0 + shard;
+    ChunksLaunch L{};
+    L.kind = g0.kind;
+    L.b = g0.b;
+    L.c = g0.c;
+    L.n = g0.n;
+    L.k = g0.k;
+    L.ready = c->sync + COC_MAX_SPLIT * kSyncWords;
+    add_piece(&L, a0.src[P.rank], -own0, own0, shard, -1);
     for (int i = 0; i < P.nchunks; ++i) {
         GatherLaunch a = a0;
         a.row0 = P.chunk[i].red_base;
         a.rows = P.chunk[i].red_rows;
-        a.signal = c->sync + COC_MAX_SPLIT + i;
+        a.signal = c->sync + (COC_MAX_SPLIT + i * kReadyLines) * kSyncWords;
         int32_t groups = 0;
         const double bytes = 2.0 * double(a.rows) * double(P.k) * double(es);
         COC_TRY(launch(KC_GATHER, bytes, c->side, [&] { return launch_gather(a, c->side, &groups); }));
         L.ready_target[i] = c->ready_sent[i] += (uint32_t)groups;
+        // the chunk's rows outside the own shard (AG chunks are contiguous)
+        const int64_t r0 = P.chunk[i].base, r1 = r0 + P.chunk[i].rows_per_blk * P.chunk[i].nblk;
+        add_piece(&L, g0.a, 0, r0, (r1 < own0 ? r1 : own0) - r0, i);
+        add_piece(&L, g0.a, 0, r0 > own1 ? r0 : own1, r1 - (r0 > own1 ? r0 : own1), i);
     }
-    int32_t tiles[COC_MAX_SPLIT];
+    int32_t tiles[kMaxPieces];
     COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
     COC_HIP(hipEventRecord(c->join, c->side));
     COC_HIP(hipStreamWaitEvent(main, c->join, 0));

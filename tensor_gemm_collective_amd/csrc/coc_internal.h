@@ -68,9 +68,6 @@ struct ReduceLaunch {
     int32_t nsrc;
     void* dst;
     int64_t src_row0, dst_row0, rows, n;
-    const uint32_t* wait;    // if set, the kernel first waits for *wait >= wait_target
-    uint32_t wait_target;
-    int32_t own;             // with wait: index of the source being written meanwhile
 };
 
 // Bit copy of gathered rows: dst[row] = shard (row / shard_rows), local row
@@ -82,36 +79,65 @@ struct GatherLaunch {
     int64_t shard_rows;
     void* dst;
     int64_t row0, rows, k;
-    uint32_t* signal;        // if set, each workgroup adds 1 once its rows are stored
+    uint32_t* signal;        // if set: ready lines of the chunk; each workgroup adds 1 to one
 };
 
 // Matmul over every chunk of an op in one launch (bf16 / fp16, k a positive
-// multiple of 32): chunk c's rows come from its row map.  Before its first
-// tile of chunk c a workgroup waits for ready[c] >= ready_target[c] (if ready
-// is set); after each tile of chunk c it adds 1 to done[c] (if done is set).
+// multiple of 32), as a list of pieces walked in order.  Piece i covers the
+// output rows of its row map { base + b*stride + j : b < nblk, j < rpb } and
+// reads A row (output row + ashift) from a[i].  Before its first tile of
+// piece i a workgroup waits for the sum of ready group wait[i]'s lines to
+// reach ready_target[wait[i]] (wait[i] >= 0, ready set); after each tile of
+// piece i it adds 1 to done[signal[i]] (signal[i] >= 0, done set).  Counter
+// layout as below.
+constexpr int kMaxPieces = 16;
 struct ChunksLaunch {
     GemmKind kind;
-    const void* a;
     const void* b;
     void* c;
     int64_t n, k;
-    int32_t nchunks;
-    int64_t base[COC_MAX_SPLIT], stride[COC_MAX_SPLIT], rpb[COC_MAX_SPLIT];
-    int32_t nblk[COC_MAX_SPLIT];
+    int32_t npieces;
+    const void* a[kMaxPieces];
+    int64_t ashift[kMaxPieces];
+    int64_t base[kMaxPieces], stride[kMaxPieces], rpb[kMaxPieces];
+    int32_t nblk[kMaxPieces];
+    int32_t wait[kMaxPieces];
+    int32_t signal[kMaxPieces];
     uint32_t* done;
     const uint32_t* ready;
     uint32_t ready_target[COC_MAX_SPLIT];
+};
+
+// Layout of the chunk hand-over counters (device memory, 32-bit words): each
+// counter on its own 128-byte line.  done[c] at line c; ready[c] is spread
+// over kReadyLines lines from line COC_MAX_SPLIT + c * kReadyLines (gather
+// workgroup b adds to line b % kReadyLines, so its adds do not queue on one
+// address) and a waiter sums them.
+constexpr int kSyncWords = 32;
+constexpr int kReadyLines = 16;
+constexpr int kSyncLines = COC_MAX_SPLIT + COC_MAX_SPLIT * kReadyLines;
+
+// The reduce that waits beside the one-launch matmul: every chunk in one
+// launch, chunk c's rows once done[c] reaches target[c].
+struct ReduceChunksLaunch {
+    ReduceLaunch r;          // sources, destination, n, dtype; rows fields unused
+    int32_t nchunks;
+    int64_t src_row0[COC_MAX_SPLIT], dst_row0[COC_MAX_SPLIT], rows[COC_MAX_SPLIT];
+    const uint32_t* done;    // counter lines as above
+    uint32_t target[COC_MAX_SPLIT];
+    int32_t own;             // index of the source the matmul is writing meanwhile
 };
 
 // Launchers (kernels.hip).  Return a hipError_t value (0 = success).  The
 // caller guarantees that every size and pointer has been validated.
 int launch_gemm(const GemmLaunch& g, void* stream);
 int launch_reduce(const ReduceLaunch& r, void* stream);
+int launch_reduce_chunks(const ReduceChunksLaunch& r, void* stream);
 // *groups (if given) receives the number of workgroups launched (signals sent).
 int launch_gather(const GatherLaunch& g, void* stream, int32_t* groups = nullptr);
 
 bool chunks_supported(GemmKind kind, int64_t k);
-// tiles[c] receives the tile count of chunk c (the completions done[c] gets).
-int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[COC_MAX_SPLIT]);
+// tiles[i] receives the tile count of piece i (the adds its signal gets).
+int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[kMaxPieces]);
 
 }  // namespace coc

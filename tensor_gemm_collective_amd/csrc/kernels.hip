@@ -153,9 +153,11 @@ constexpr int kSyncScope = COC_SYNC_SYSTEM ? __HIP_MEMORY_SCOPE_SYSTEM : __HIP_M
 // Polls back off from ~0.1 us to ~4 us between loads: hundreds of workgroups
 // polling one counter at a fixed short interval load its HBM channel enough to
 // slow every other stream through it.
-__device__ __forceinline__ bool spin_until(const uint32_t* p, uint32_t target) {
+// Waits until the sum of `lines` counters (kSyncWords apart) reaches target.
+__device__ __forceinline__ bool spin_until(const uint32_t* p, int lines, uint32_t target) {
     for (uint32_t i = 0; i < kSpinLimit; ++i) {
-        const uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, kSyncScope);
+        uint32_t v = 0;
+        for (int l = 0; l < lines; ++l) v += __hip_atomic_load(p + l * kSyncWords, __ATOMIC_RELAXED, kSyncScope);
         if ((int32_t)(v - target) >= 0) return true;
         if (i < 4) __builtin_amdgcn_s_sleep(2);
         else if (i < 8) __builtin_amdgcn_s_sleep(16);
@@ -164,13 +166,13 @@ __device__ __forceinline__ bool spin_until(const uint32_t* p, uint32_t target) {
     return false;
 }
 
-// Workgroup-wide wait for *p >= target: thread 0 polls and the outcome goes to
+// Workgroup-wide wait for the counters: thread 0 polls and the outcome goes to
 // every wave through LDS.  The barrier orders every later load after the
 // poll.  Two calls must be separated by a workgroup barrier (the flag is
 // reused).
-__device__ __forceinline__ bool wg_wait(const uint32_t* p, uint32_t target) {
+__device__ __forceinline__ bool wg_wait(const uint32_t* p, int lines, uint32_t target) {
     __shared__ int ok;
-    if (threadIdx.x == 0) ok = spin_until(p, target) ? 1 : 0;
+    if (threadIdx.x == 0) ok = spin_until(p, lines, target) ? 1 : 0;
     __syncthreads();
     return ok != 0;
 }
@@ -736,14 +738,14 @@ template <int BM, int BN, int S, int WM, int WN>
 constexpr int ring_lds_bytes() { return S * (BM * 32 * 2 + 32 * BN * 2); }
 
 // One BM x BN output tile at (m0, n0) of a chunk with row map (rows, rpb,
-// base, stride).  `sm` is the workgroup's LDS ring; the caller guarantees that
+// base, stride); A row = output row + ashift.  `sm` is the workgroup's LDS ring; the caller guarantees that
 // every wave has finished with it and has no stores outstanding.  poison:
 // store NaN instead of the products (a wait for the tile's inputs timed out).
 // SYS: system-scope (write-through) stores, for a tile another kernel reads
 // while this one runs.
 template <int BM, int BN, int S, int WM, int WN, int KIND, bool SYS = false>
 __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb, int64_t base, int64_t stride,
-                                          int m0, int n0, uint8_t* sm, bool poison) {
+                                          int64_t ashift, int m0, int n0, uint8_t* sm, bool poison) {
     constexpr int BK = 32, NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE = A_BYTES + B_BYTES;
@@ -768,7 +770,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     for (int i = 0; i < APW; ++i) {
         const int row = (wave * APW + i) * 16 + (lane >> 2);
         const int r = m0 + row < rows ? m0 + row : rows - 1;
-        const int64_t gr = map_row(r, rpb, base, stride);
+        const int64_t gr = map_row(r, rpb, base, stride) + ashift;
         aof[i] = (uint32_t)(gr * p.k * 2) + (((lane & 3) ^ gA<32>(row)) << 4);
     }
 #pragma unroll
@@ -939,27 +941,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t sm[ring_lds_bytes<BM, BN, S, WM, WN>()];
     int tm, tn;
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
-    ring_tile<BM, BN, S, WM, WN, KIND>(p, p.rows, p.rpb, p.base, p.stride, tm * BM, tn * BN, sm, false);
+    ring_tile<BM, BN, S, WM, WN, KIND>(p, p.rows, p.rpb, p.base, p.stride, 0, tm * BM, tn * BN, sm, false);
 }
 
 // Chunk-walking form of the ring kernel: one launch covers every chunk of an
-// op.  8 * per_xcd workgroups (one per CU for the 256-wide tiles, two for
-// 128 x 128); workgroup b runs on XCD b % 8 and walks that XCD's tile list:
-// chunk by chunk in pipeline order, within a chunk the XCD's run of
-// xcd_tile's split in grouped order, taking every per_xcd-th item.  Chunk c
-// can wait for ready[c] (gathered rows in place) before its first tile; with
-// SIGNAL, tiles are stored write-through and each adds 1 to done[c].  The
-// gathered rows are read through the L2 as usual: no line of chunk c can be
-// cached before its wait (rows are whole 128-byte lines and nothing reads
-// them earlier in this launch), and the gather writes them through.
+// op, as a list of pieces (see ChunksLaunch).  8 * per_xcd workgroups (one per
+// CU for the 256-wide tiles, two for 128 x 128); workgroup b runs on XCD b % 8
+// and walks that XCD's tile list: piece by piece in order, within a piece the
+// XCD's run of xcd_tile's split in grouped order, taking every per_xcd-th
+// item.  A piece can wait for a group of ready counters before its first tile;
+// with SIGNAL, tiles are stored write-through and add 1 to their piece's done
+// counter.  Gathered rows are read through the L2 as usual: no line of a piece
+// can be cached before its wait (rows are whole 128-byte lines and nothing
+// reads them earlier in this launch), and the gather writes them through.
 struct PersistParams {
-    GemmParams g;   // a, b, c, n, k, tiles_n (row map fields unused)
-    int64_t base[COC_MAX_SPLIT], stride[COC_MAX_SPLIT];
-    int32_t rpb[COC_MAX_SPLIT], rows[COC_MAX_SPLIT], tiles_m[COC_MAX_SPLIT];
-    int32_t nchunks, per_xcd;
+    GemmParams g;   // b, c, n, k, tiles_n (a and the row map fields unused)
+    const uint8_t* a[kMaxPieces];
+    int64_t ashift[kMaxPieces], base[kMaxPieces], stride[kMaxPieces];
+    int32_t rpb[kMaxPieces], rows[kMaxPieces], tiles_m[kMaxPieces];
+    int32_t wait[kMaxPieces], signal[kMaxPieces];
+    uint32_t ready_target[COC_MAX_SPLIT];
+    int32_t npieces, per_xcd;
     uint32_t* done;
     const uint32_t* ready;
-    uint32_t ready_target[COC_MAX_SPLIT];
 };
 
 template <int BM, int BN, int S, int WM, int WN, int KIND, bool SIGNAL>
@@ -972,26 +976,31 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P
     bool ok = true;
     for (int j = w;; j += P.per_xcd) {
         int c = 0, jj = j;
-        for (; c < P.nchunks; ++c) {
+        for (; c < P.npieces; ++c) {
             const int T = P.tiles_m[c] * tn_all;
             const int cnt = T / NX + (x < T % NX ? 1 : 0);
             if (jj < cnt) break;
             jj -= cnt;
         }
-        if (c >= P.nchunks) break;
+        if (c >= P.npieces) break;
         const int T = P.tiles_m[c] * tn_all;
         int tm, tn;
         grouped_coords(x * (T / NX) + (x < T % NX ? x : T % NX) + jj, P.tiles_m[c], tn_all, &tm, &tn);
-        if (P.ready != nullptr && c != waited) {
-            ok = wg_wait(P.ready + c, P.ready_target[c]);
-            waited = c;
+        const int wi = P.wait[c];
+        if (P.ready != nullptr && wi >= 0 && wi != waited) {
+            ok = wg_wait(P.ready + wi * kReadyLines * kSyncWords, kReadyLines, P.ready_target[wi]);
+            waited = wi;
         }
         // the previous tile's stores are done and every wave is off the LDS ring
         wait_vmcnt<0>();
         block_barrier();
-        ring_tile<BM, BN, S, WM, WN, KIND, SIGNAL>(P.g, P.rows[c], P.rpb[c], P.base[c], P.stride[c], tm * BM,
-                                                   tn * BN, sm, !ok);
-        if constexpr (SIGNAL) wg_signal(P.done + c);
+        GemmParams g = P.g;
+        g.a = P.a[c];
+        ring_tile<BM, BN, S, WM, WN, KIND, SIGNAL>(g, P.rows[c], P.rpb[c], P.base[c], P.stride[c], P.ashift[c],
+                                                   tm * BM, tn * BN, sm, wi >= 0 && !ok);
+        if constexpr (SIGNAL) {
+            if (P.signal[c] >= 0) wg_signal(P.done + P.signal[c] * kSyncWords);
+        }
     }
 }
 
@@ -1068,9 +1077,15 @@ struct ReduceParams {
     int32_t nsrc;
     int32_t vpr;         // 16-byte vectors per row
     int32_t total;       // rows * vpr
-    const uint32_t* wait;   // if set, first wait for *wait >= wait_target
-    uint32_t wait_target;
-    int32_t own;            // with wait: the source written while this kernel waits
+};
+
+// Chunk list of the waiting reduce, in pipeline order.
+struct ReduceChunks {
+    int64_t src_row0[COC_MAX_SPLIT], dst_row0[COC_MAX_SPLIT];
+    int32_t total[COC_MAX_SPLIT];     // rows * vpr
+    uint32_t target[COC_MAX_SPLIT];
+    const uint32_t* done;
+    int32_t nchunks, own;
 };
 
 // Two sources are loaded at a time and added in rank order before the next
@@ -1143,51 +1158,73 @@ __global__ __launch_bounds__(256) void reduce_rows(ReduceParams p) {
     }
 }
 
-// The reduce that runs beside the one-launch matmul and waits for its chunk's
-// tiles; the partial written meanwhile (source `own`) is read with
-// system-scope loads.  It is launched with at most one workgroup per CU, so
-// however the hardware orders the two launches, every CU keeps room for the
-// matmul's workgroup (the wait could otherwise hold slots the matmul needs).
-// To keep HBM busy with that few waves, each thread loads all sources of a
-// 16-byte vector before adding them (same rank order, same binary32 sums).
+// The reduce that runs beside the one-launch matmul: one launch walks the
+// chunks in pipeline order, each workgroup waiting for chunk c's tiles before
+// its share of chunk c's rows.  The partial written meanwhile (source `own`)
+// is read with system-scope loads.  At most one workgroup per CU, so however
+// the hardware orders the two launches every CU keeps room for the matmul's
+// workgroup (the waits could otherwise hold slots the matmul needs).  To keep
+// HBM busy with that few waves, each thread loads all sources of two 16-byte
+// vectors before adding them (same rank order, same binary32 sums).
 template <int DT>
-__global__ __launch_bounds__(256) void reduce_rows_wait(ReduceParams p) {
+__device__ __forceinline__ void load_sources(const ReduceParams& p, int own, int64_t so, u32x4* x) {
+#pragma unroll
+    for (int s = 0; s < COC_MAX_WORLD; ++s)
+        if (s < p.nsrc) x[s] = s == own ? load16_sys(p.src[s] + so) : *(const u32x4*)(p.src[s] + so);
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 sum_sources(const ReduceParams& p, const u32x4* x) {
     constexpr int E = (DT == COC_F32) ? 4 : 8;
-    const bool ok = p.wait == nullptr || wg_wait(p.wait, p.wait_target);
+    float acc[E];
+    if constexpr (DT == COC_F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __uint_as_float(x[0][e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = unpack_lo<DT>(x[0][e]);
+            acc[2 * e + 1] = unpack_hi<DT>(x[0][e]);
+        }
+    }
+#pragma unroll
+    for (int s = 1; s < COC_MAX_WORLD; ++s)
+        if (s < p.nsrc) acc_add<DT>(acc, x[s]);
+    u32x4 out;
+    if constexpr (DT == COC_F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = __float_as_uint(acc[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = pack2<DT>(acc[2 * e], acc[2 * e + 1]);
+    }
+    return out;
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void reduce_chunks_wait(ReduceParams p, ReduceChunks C) {
     const int stride = gridDim.x * 256;
-    for (int v = blockIdx.x * 256 + threadIdx.x; v < p.total; v += stride) {
-        const int row = v / p.vpr;
-        const int cv = v - row * p.vpr;
-        const int64_t so = (p.src_row0 + row) * p.row_bytes + (int64_t)cv * 16;
-        const int64_t dof = (p.dst_row0 + row) * p.row_bytes + (int64_t)cv * 16;
-        u32x4 x[COC_MAX_WORLD];
-#pragma unroll
-        for (int s = 0; s < COC_MAX_WORLD; ++s)
-            if (s < p.nsrc) x[s] = s == p.own ? load16_sys(p.src[s] + so) : *(const u32x4*)(p.src[s] + so);
-        float acc[E];
-        if constexpr (DT == COC_F32) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = __uint_as_float(x[0][e]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = unpack_lo<DT>(x[0][e]);
-                acc[2 * e + 1] = unpack_hi<DT>(x[0][e]);
+    for (int c = 0; c < C.nchunks; ++c) {
+        if (c > 0) __syncthreads();   // wg_wait's flag is reused
+        const bool ok = wg_wait(C.done + c * kSyncWords, 1, C.target[c]);
+        const int total = C.total[c];
+        for (int v = blockIdx.x * 256 + threadIdx.x; v < total; v += 2 * stride) {
+            const int v2 = v + stride;
+            const bool two = v2 < total;
+            const int row = v / p.vpr, row2 = v2 / p.vpr;
+            const int64_t so = (C.src_row0[c] + row) * p.row_bytes + (int64_t)(v - row * p.vpr) * 16;
+            const int64_t so2 = (C.src_row0[c] + row2) * p.row_bytes + (int64_t)(v2 - row2 * p.vpr) * 16;
+            u32x4 x[COC_MAX_WORLD], y[COC_MAX_WORLD];
+            load_sources<DT>(p, C.own, so, x);
+            if (two) load_sources<DT>(p, C.own, so2, y);
+            const u32x4 nan = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};   // NaN in every format
+            const u32x4 o = ok ? sum_sources<DT>(p, x) : nan;
+            *(u32x4*)(p.dst + (C.dst_row0[c] + row) * p.row_bytes + (int64_t)(v - row * p.vpr) * 16) = o;
+            if (two) {
+                const u32x4 o2 = ok ? sum_sources<DT>(p, y) : nan;
+                *(u32x4*)(p.dst + (C.dst_row0[c] + row2) * p.row_bytes + (int64_t)(v2 - row2 * p.vpr) * 16) = o2;
             }
         }
-#pragma unroll
-        for (int s = 1; s < COC_MAX_WORLD; ++s)
-            if (s < p.nsrc) acc_add<DT>(acc, x[s]);
-        u32x4 out;
-        if constexpr (DT == COC_F32) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = __float_as_uint(acc[e]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = pack2<DT>(acc[2 * e], acc[2 * e + 1]);
-        }
-        if (!ok) out = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};   // NaN in every format
-        *(u32x4*)(p.dst + dof) = out;
     }
 }
 
@@ -1205,30 +1242,48 @@ struct GatherParams {
     uint32_t* signal;    // if set, each workgroup adds 1 when its rows are stored
 };
 
-__global__ __launch_bounds__(256) void gather_rows(GatherParams p) {
-    const int stride = gridDim.x * 256;
-    for (int v = blockIdx.x * 256 + threadIdx.x; v < p.total; v += stride) {
-        const int row = v / p.vpr;
-        const int cv = v - row * p.vpr;
-        const int g = p.row0 + row;
-        const int s = g / p.shard_rows;
-        const int local = g - s * p.shard_rows;
-        const uint8_t* sp = p.src[0];
+// Four 16-byte vectors per thread per pass, all loaded before any is stored:
+// beside a running matmul only a few gather waves fit on each CU, and the
+// copy rate is set by the bytes they keep in flight.
+__device__ __forceinline__ const uint8_t* gather_src(const GatherParams& p, int v, int64_t* off) {
+    const int row = v / p.vpr;
+    const int cv = v - row * p.vpr;
+    const int g = p.row0 + row;
+    const int s = g / p.shard_rows;
+    const int local = g - s * p.shard_rows;
+    const uint8_t* sp = p.src[0];
 #pragma unroll
-        for (int i = 1; i < COC_MAX_WORLD; ++i)
-            if (s == i) sp = p.src[i];
-        const u32x4 x = *(const u32x4*)(sp + (int64_t)local * p.row_bytes + (int64_t)cv * 16);
-        const int64_t off = (int64_t)g * p.row_bytes + (int64_t)cv * 16;
-        if (p.signal != nullptr)
-            store16_sys(sys_rsrc(p.dst), (uint32_t)off, x);   // read by a matmul already running
-        else
-            *(u32x4*)(p.dst + off) = x;
-    }
-    if (p.signal != nullptr) wg_signal(p.signal);
+    for (int i = 1; i < COC_MAX_WORLD; ++i)
+        if (s == i) sp = p.src[i];
+    *off = (int64_t)g * p.row_bytes + (int64_t)cv * 16;
+    return sp + (int64_t)local * p.row_bytes + (int64_t)cv * 16;
 }
 
-int grid_for(int64_t total_vec) {
-    const int64_t want = (total_vec + 255) / 256;
+__global__ __launch_bounds__(256) void gather_rows(GatherParams p) {
+    constexpr int U = 4;
+    const int stride = gridDim.x * 256;
+    for (int v0 = blockIdx.x * 256 + threadIdx.x; v0 < p.total; v0 += U * stride) {
+        u32x4 x[U];
+        int64_t off[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * stride;
+            if (v < p.total) x[u] = *(const u32x4*)gather_src(p, v, &off[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (v0 + u * stride >= p.total) break;
+            if (p.signal != nullptr)
+                store16_sys(sys_rsrc(p.dst), (uint32_t)off[u], x[u]);   // read by a matmul already running
+            else
+                *(u32x4*)(p.dst + off[u]) = x[u];
+        }
+    }
+    if (p.signal != nullptr) wg_signal(p.signal + (blockIdx.x % kReadyLines) * kSyncWords);
+}
+
+int grid_for(int64_t total_vec, int per_thread = 1) {
+    const int64_t want = (total_vec + 256 * per_thread - 1) / (256 * per_thread);
     const int64_t cap = 256 * 8;
     return (int)(want < cap ? (want > 0 ? want : 1) : cap);
 }
@@ -1268,6 +1323,9 @@ hipError_t launch_ring(GemmParams p, hipStream_t s) {
 }
 
 template <int KIND>
+hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* tiles);
+
+template <int KIND>
 hipError_t launch_dma_kind(GemmParams p, int concurrent, hipStream_t s) {
     // k a positive multiple of 32: the ring kernel with the largest tile that
     // still gives COC_RING_MIN_TILES workgroups across the chunk matmuls that
@@ -1275,6 +1333,26 @@ hipError_t launch_dma_kind(GemmParams p, int concurrent, hipStream_t s) {
     // zero-fills the k tail.  Every choice walks k the same way, so it never
     // changes the result bits.
     if (p.k >= 32 && p.k % 32 == 0) {
+        if (concurrent <= 1) {
+            // a lone matmul: the chunk-walking launch with one chunk (measured
+            // faster than one workgroup per tile: no second dispatch wave)
+            ChunksLaunch L{};
+            L.kind = (GemmKind)KIND;
+            L.b = p.b;
+            L.c = p.c;
+            L.n = p.n;
+            L.k = p.k;
+            L.npieces = 1;
+            L.a[0] = p.a;
+            L.base[0] = p.base;
+            L.stride[0] = p.stride;
+            L.rpb[0] = p.rpb;
+            L.nblk[0] = p.rows / (p.rpb > 0 ? p.rpb : 1);
+            L.wait[0] = -1;
+            L.signal[0] = -1;
+            int32_t tiles[kMaxPieces];
+            return launch_chunks_kind<KIND>(L, s, tiles);
+        }
         const int64_t want = COC_RING_MIN_TILES / (concurrent > 1 ? concurrent : 1);
         const int64_t tm256 = (p.rows + 255) / 256, tm128 = (p.rows + 127) / 128;
         const int64_t tn256 = (p.n + 255) / 256;
@@ -1329,25 +1407,44 @@ int launch_reduce(const ReduceLaunch& r, void* stream) {
     p.nsrc = r.nsrc;
     p.vpr = (int32_t)(p.row_bytes / 16);
     p.total = (int32_t)(r.rows * p.vpr);
-    p.wait = r.wait;
-    p.wait_target = r.wait_target;
-    p.own = r.wait != nullptr ? r.own : -1;
     hipStream_t s = (hipStream_t)stream;
-    if (p.wait != nullptr) {
-        const int grid = grid_for(p.total) < 256 ? grid_for(p.total) : 256;   // at most one per CU
-        switch (r.dt) {
-            case COC_F32: hipLaunchKernelGGL(reduce_rows_wait<COC_F32>, dim3(grid), dim3(256), 0, s, p); break;
-            case COC_F16: hipLaunchKernelGGL(reduce_rows_wait<COC_F16>, dim3(grid), dim3(256), 0, s, p); break;
-            case COC_BF16: hipLaunchKernelGGL(reduce_rows_wait<COC_BF16>, dim3(grid), dim3(256), 0, s, p); break;
-            default: return hipErrorInvalidValue;
-        }
-        return hipGetLastError();
-    }
     const int grid = grid_for(p.total);
     switch (r.dt) {
         case COC_F32: hipLaunchKernelGGL(reduce_rows<COC_F32>, dim3(grid), dim3(256), 0, s, p); break;
         case COC_F16: hipLaunchKernelGGL(reduce_rows<COC_F16>, dim3(grid), dim3(256), 0, s, p); break;
         case COC_BF16: hipLaunchKernelGGL(reduce_rows<COC_BF16>, dim3(grid), dim3(256), 0, s, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+int launch_reduce_chunks(const ReduceChunksLaunch& L, void* stream) {
+    const ReduceLaunch& r = L.r;
+    if (r.n == 0 || L.nchunks == 0) return hipSuccess;
+    ReduceParams p{};
+    for (int i = 0; i < COC_MAX_WORLD; ++i) p.src[i] = (const uint8_t*)(i < r.nsrc ? r.src[i] : r.src[0]);
+    p.dst = (uint8_t*)r.dst;
+    p.row_bytes = r.n * (int64_t)elem_size(r.dt);
+    p.nsrc = r.nsrc;
+    p.vpr = (int32_t)(p.row_bytes / 16);
+    ReduceChunks C{};
+    int64_t most = 0;
+    for (int c = 0; c < L.nchunks; ++c) {
+        C.src_row0[c] = L.src_row0[c];
+        C.dst_row0[c] = L.dst_row0[c];
+        C.total[c] = (int32_t)(L.rows[c] * p.vpr);
+        C.target[c] = L.target[c];
+        most = C.total[c] > most ? C.total[c] : most;
+    }
+    C.done = L.done;
+    C.nchunks = L.nchunks;
+    C.own = L.own;
+    const int grid = grid_for(most) < 256 ? grid_for(most) : 256;   // at most one per CU
+    hipStream_t s = (hipStream_t)stream;
+    switch (r.dt) {
+        case COC_F32: hipLaunchKernelGGL(reduce_chunks_wait<COC_F32>, dim3(grid), dim3(256), 0, s, p, C); break;
+        case COC_F16: hipLaunchKernelGGL(reduce_chunks_wait<COC_F16>, dim3(grid), dim3(256), 0, s, p, C); break;
+        case COC_BF16: hipLaunchKernelGGL(reduce_chunks_wait<COC_BF16>, dim3(grid), dim3(256), 0, s, p, C); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1366,9 +1463,7 @@ int launch_gather(const GatherLaunch& g, void* stream, int32_t* groups) {
     p.total = (int32_t)(g.rows * p.vpr);
     p.signal = g.signal;
     hipStream_t s = (hipStream_t)stream;
-    // with a signal, at most 256 workgroups: their adds to the one counter
-    // are serialised (~8 ns each)
-    const int grid = g.signal != nullptr && grid_for(p.total) > 256 ? 256 : grid_for(p.total);
+    const int grid = grid_for(p.total, 4);
     hipLaunchKernelGGL(gather_rows, dim3(grid), dim3(256), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess && groups != nullptr) *groups = grid;
@@ -1384,30 +1479,35 @@ namespace {
 template <int BM, int BN, int S, int WM, int WN, int KIND>
 hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s, int32_t* tiles) {
     PersistParams P{};
-    P.g.a = (const uint8_t*)L.a;
     P.g.b = (const uint8_t*)L.b;
     P.g.c = (uint8_t*)L.c;
     P.g.n = (int32_t)L.n;
     P.g.k = (int32_t)L.k;
     P.g.tiles_n = (int32_t)((L.n + BN - 1) / BN);
-    P.nchunks = L.nchunks;
-    int64_t longest = 0;   // XCD 0's list: ceil(T_c / 8) summed over chunks
-    for (int c = 0; c < L.nchunks; ++c) {
+    P.npieces = L.npieces;
+    bool signal = false;
+    int64_t longest = 0;   // XCD 0's list: ceil(T_i / 8) summed over pieces
+    for (int c = 0; c < L.npieces; ++c) {
         const int64_t rows = L.rpb[c] * L.nblk[c];
+        P.a[c] = (const uint8_t*)L.a[c];
+        P.ashift[c] = L.ashift[c];
         P.base[c] = L.base[c];
         P.stride[c] = L.stride[c];
         P.rpb[c] = (int32_t)(L.rpb[c] > 0 ? L.rpb[c] : 1);
         P.rows[c] = (int32_t)rows;
         P.tiles_m[c] = (int32_t)((rows + BM - 1) / BM);
+        P.wait[c] = L.wait[c];
+        P.signal[c] = L.signal[c];
+        signal = signal || (L.done != nullptr && L.signal[c] >= 0);
         tiles[c] = P.tiles_m[c] * P.g.tiles_n;
         longest += (tiles[c] + 7) / 8;
-        P.ready_target[c] = L.ready_target[c];
     }
+    for (int i = 0; i < COC_MAX_SPLIT; ++i) P.ready_target[i] = L.ready_target[i];
     P.done = L.done;
     P.ready = L.ready;
     const int64_t cap = 32 * per_cu;   // 256 CUs / 8 XCDs, times workgroups per CU
     P.per_xcd = (int32_t)(longest < cap ? (longest > 0 ? longest : 1) : cap);
-    if (P.done != nullptr)
+    if (signal)
         hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true>), dim3(8 * P.per_xcd), dim3(64 * WM * WN),
                            0, s, P);
     else
@@ -1420,7 +1520,7 @@ template <int KIND>
 hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* tiles) {
     // largest tile that still fills the 256 CUs once over the whole op
     int64_t t256 = 0, t128x256 = 0;
-    for (int c = 0; c < L.nchunks; ++c) {
+    for (int c = 0; c < L.npieces; ++c) {
         const int64_t rows = L.rpb[c] * L.nblk[c];
         t256 += ((rows + 255) / 256) * ((L.n + 255) / 256);
         t128x256 += ((rows + 127) / 128) * ((L.n + 255) / 256);
@@ -1432,8 +1532,8 @@ hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* til
 
 }  // namespace
 
-int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[COC_MAX_SPLIT]) {
-    for (int c = 0; c < COC_MAX_SPLIT; ++c) tiles[c] = 0;
+int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[kMaxPieces]) {
+    for (int c = 0; c < kMaxPieces; ++c) tiles[c] = 0;
     hipStream_t s = (hipStream_t)stream;
     switch (L.kind) {
         case GK_F16: return launch_chunks_kind<GK_F16>(L, s, tiles);
