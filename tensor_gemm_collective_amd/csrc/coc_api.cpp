@@ -223,6 +223,9 @@ ChunksLaunch chunks_for(const Plan& P, const GemmLaunch& g0) {
     L.c = g0.c;
     L.n = g0.n;
     L.k = g0.k;
+    L.scales = g0.scales;
+    L.qmode = g0.qmode;
+    L.group = g0.group;
     L.npieces = P.nchunks;
     for (int i = 0; i < P.nchunks; ++i) {
         L.a[i] = g0.a;
@@ -251,7 +254,7 @@ void add_piece(ChunksLaunch* L, const void* a, int64_t ashift, int64_t row0, int
 }
 
 bool one_launch(const Plan& P, const GemmLaunch& g0) {
-    return COC_ONE_LAUNCH != 0 && P.split > 1 && chunks_supported(g0.kind, g0.k);
+    return COC_ONE_LAUNCH != 0 && P.split > 1 && chunks_supported(g0);
 }
 
 // The one-launch all-gather reads gathered rows through the L2, which needs
@@ -267,8 +270,10 @@ double total_flops(const Plan& P) {
 }
 
 // One-launch pipeline, compute first: the matmul walks the chunks in order on
-// the caller's stream and counts finished tiles per chunk; the reduce of chunk
-// i, on the side stream from the start, waits for chunk i's count.  The host
+// the caller's stream and counts finished tiles per chunk; the reduce of each
+// early chunk, on the side stream from the start, waits for that chunk's
+// count, and the chunks of the matmul's last round reduce after it on the
+// caller's stream.  The host
 // enqueues the matmul before the reduces, so if both streams shared one
 // hardware queue the matmul would simply finish first.
 coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const ReduceLaunch& r0,
@@ -281,22 +286,45 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
     ChunksLaunch L = chunks_for(P, g0);
     for (int i = 0; i < P.nchunks; ++i) L.signal[i] = i;
     L.done = c->sync;
-    int32_t tiles[kMaxPieces];
+    int32_t tiles[kMaxPieces + 1];
     COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
+    // Chunks whose tiles all fall before the matmul's last round of workgroups
+    // reduce beside it (waiting on its counters, at most one workgroup per
+    // CU).  The rest finish with the matmul; their rows (consecutive in every
+    // plan) reduce in one full-grid launch after it on the caller's stream.
+    const int64_t groups = tiles[kMaxPieces] > 0 ? tiles[kMaxPieces] : 1;
+    int64_t total = 0;
+    for (int i = 0; i < P.nchunks; ++i) total += tiles[i];
+    const int64_t last_round = ((total - 1) / groups) * groups;   // first tile index of the last round
+    int early = 0;
+    for (int64_t cum = 0; early < P.nchunks - 1 && cum + tiles[early] <= last_round; ++early) cum += tiles[early];
     ReduceChunksLaunch R{};
     R.r = r0;
-    R.nchunks = P.nchunks;
+    R.nchunks = early;
     R.done = c->sync;
     R.own = P.rank;
+    R.narrow = g0.kind == GK_W8_F16;   // the int8 matmul leaves ~90 VGPRs per SIMD lane
     double bytes = 0;
     for (int i = 0; i < P.nchunks; ++i) {
-        R.target[i] = c->done_sent[i] += (uint32_t)tiles[i];
+        const uint32_t t = c->done_sent[i] += (uint32_t)tiles[i];
+        if (i >= early) continue;
+        R.target[i] = t;
         R.src_row0[i] = P.chunk[i].red_base;
         R.dst_row0[i] = P.chunk[i].out_base;
         R.rows[i] = P.chunk[i].red_rows;
         bytes += double(r0.nsrc + 1) * double(R.rows[i]) * double(P.n) * double(es);
     }
-    COC_TRY(launch(KC_REDUCE, bytes, c->side, [&] { return launch_reduce_chunks(R, c->side); }));
+    if (early > 0)
+        COC_TRY(launch(KC_REDUCE, bytes, c->side, [&] { return launch_reduce_chunks(R, c->side); }));
+    {
+        ReduceLaunch r = r0;
+        r.src_row0 = P.chunk[early].red_base;
+        r.dst_row0 = P.chunk[early].out_base;
+        r.rows = 0;
+        for (int i = early; i < P.nchunks; ++i) r.rows += P.chunk[i].red_rows;
+        const double lb = double(r.nsrc + 1) * double(r.rows) * double(P.n) * double(es);
+        COC_TRY(launch(KC_REDUCE, lb, main, [&] { return launch_reduce(r, main); }));
+    }
     COC_HIP(hipEventRecord(c->join, c->side));
     COC_HIP(hipStreamWaitEvent(main, c->join, 0));
     return COC_OK;
@@ -339,7 +367,7 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
         add_piece(&L, g0.a, 0, r0, (r1 < own0 ? r1 : own0) - r0, i);
         add_piece(&L, g0.a, 0, r0 > own1 ? r0 : own1, r1 - (r0 > own1 ? r0 : own1), i);
     }
-    int32_t tiles[kMaxPieces];
+    int32_t tiles[kMaxPieces + 1];
     COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
     COC_HIP(hipEventRecord(c->join, c->side));
     COC_HIP(hipStreamWaitEvent(main, c->join, 0));

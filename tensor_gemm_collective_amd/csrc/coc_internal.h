@@ -96,6 +96,8 @@ struct ChunksLaunch {
     const void* b;
     void* c;
     int64_t n, k;
+    const void* scales;  // w8a16 only
+    int32_t qmode, group;
     int32_t npieces;
     const void* a[kMaxPieces];
     int64_t ashift[kMaxPieces];
@@ -126,6 +128,7 @@ struct ReduceChunksLaunch {
     const uint32_t* done;    // counter lines as above
     uint32_t target[COC_MAX_SPLIT];
     int32_t own;             // index of the source the matmul is writing meanwhile
+    bool narrow;             // one vector per thread: fits beside a matmul using more registers
 };
 
 // Launchers (kernels.hip).  Return a hipError_t value (0 = success).  The
@@ -136,8 +139,12 @@ int launch_reduce_chunks(const ReduceChunksLaunch& r, void* stream);
 // *groups (if given) receives the number of workgroups launched (signals sent).
 int launch_gather(const GatherLaunch& g, void* stream, int32_t* groups = nullptr);
 
-bool chunks_supported(GemmKind kind, int64_t k);
-// tiles[i] receives the tile count of piece i (the adds its signal gets).
-int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[kMaxPieces]);
+// Whether the ring kernels take this matmul (bf16 / fp16 with k a positive
+// multiple of 32; w8a16 also needs n % 16 == 0 and, per group, group % 32 == 0
+// with the tile's scale rows fitting in LDS).
+bool chunks_supported(const GemmLaunch& g);
+// tiles[i] receives the tile count of piece i (the adds its signal gets) and
+// tiles[kMaxPieces] the number of workgroups launched.
+int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[kMaxPieces + 1]);
 
 }  // namespace coc

@@ -190,6 +190,8 @@ __device__ __forceinline__ void wg_signal(uint32_t* p) {
 // one buffer_store_dwordx4 with sc0 sc1 (cache-policy bits 0 and 4), measured
 // as fast as a plain store, where two 8-byte atomic stores run at ~60 %.
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t sys_rsrc(uint8_t* base) {
     return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)0xffffffff, 0x00020000);
 }
@@ -734,8 +736,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
 //   * The k walk (16-k MFMA steps in increasing k, same operand roles) is the
 //     one every other kernel here uses, so results are bitwise identical to
 //     theirs.
-template <int BM, int BN, int S, int WM, int WN>
-constexpr int ring_lds_bytes() { return S * (BM * 32 * 2 + 32 * BN * 2); }
+// w8A16 ring tiles keep the tile's per-group fp16 scales in LDS: at most this
+// many bytes (k / group rows of BN scales).
+constexpr int kW8TableBytes = 32768;
+
+template <int BM, int BN, int S, int WM, int WN, int KIND = GK_BF16>
+constexpr int ring_lds_bytes() {
+    const int ring = S * (BM * 32 * 2 + 32 * BN * (KIND == GK_W8_F16 ? 1 : 2)) + (KIND == GK_W8_F16 ? kW8TableBytes : 0);
+    return ring > BM * BN * 2 ? ring : BM * BN * 2;   // the epilogue stages the tile in the same LDS
+}
 
 // One BM x BN output tile at (m0, n0) of a chunk with row map (rows, rpb,
 // base, stride); A row = output row + ashift.  `sm` is the workgroup's LDS ring; the caller guarantees that
@@ -747,17 +756,20 @@ template <int BM, int BN, int S, int WM, int WN, int KIND, bool SYS = false>
 __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb, int64_t base, int64_t stride,
                                           int64_t ashift, int m0, int n0, uint8_t* sm, bool poison) {
     constexpr int BK = 32, NW = WM * WN;
+    constexpr bool W8 = KIND == GK_W8_F16;   // int8 weights, fp16 activations
+    constexpr int BE = W8 ? 1 : 2;            // weight bytes per element
     constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
-    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE = A_BYTES + B_BYTES;
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * BE, STAGE = A_BYTES + B_BYTES;
     constexpr int APW = A_BYTES / 1024 / NW, BPW = B_BYTES / 1024 / NW, DPW = APW + BPW;
-    constexpr int BROW = BN / 8;   // 16-byte chunks per weight k-row
-    constexpr int KPI = 64 / BROW; // weight k-rows per load instruction
-    constexpr int NMM = FM * FN, NRD = FM + 2 * FN;
+    constexpr int BROW = BN * BE / 16;   // 16-byte chunks per weight k-row
+    constexpr int KPI = 64 / BROW;       // weight k-rows per load instruction
+    constexpr int NMM = FM * FN, NRD = FM + (W8 ? 1 : 2) * FN;
     constexpr int OUT_DT = (KIND == GK_BF16) ? COC_BF16 : COC_F16;
+    constexpr int TBL = S * STAGE;       // w8: scale table offset in LDS
     static_assert((A_BYTES / 1024) % NW == 0 && (B_BYTES / 1024) % NW == 0, "loads split over the waves");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32 x 32 MFMA blocks");
-    static_assert(BROW >= 16 && BROW <= 64, "weight swizzle works on 16-chunk groups");
-    static_assert(S >= 3 && S * STAGE <= 160 * 1024, "LDS ring");
+    static_assert(W8 ? (BROW >= 8 && BROW <= 64) : (BROW >= 16 && BROW <= 64), "weight swizzle");
+    static_assert(S >= 3 && ring_lds_bytes<BM, BN, S, WM, WN, KIND>() <= 160 * 1024, "LDS ring");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -776,8 +788,10 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
         const int K = (wave * BPW + i) * KPI + lane / BROW;
-        const int col = n0 + (((lane % BROW) ^ gB(K)) << 3);
-        bof[i] = (uint32_t)K * (uint32_t)p.n * 2u + (uint32_t)(col < p.n ? col : 0) * 2u;
+        // chunk c of weight k-row K sits at c ^ gB(K) (bf16 / fp16: 8 columns per
+        // chunk) or c ^ (K & 7) (int8: 16 columns per chunk)
+        const int col = W8 ? n0 + (((lane % BROW) ^ (K & 7)) << 4) : n0 + (((lane % BROW) ^ gB(K)) << 3);
+        bof[i] = (uint32_t)K * (uint32_t)p.n * BE + (uint32_t)(col < p.n ? col : 0) * BE;
     }
     // fragment offsets within a stage (the rest are immediates)
     int ard[2];
@@ -789,9 +803,20 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     int brd[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-        const int r = lane & 15, K = (lane >> 5) * 8 + (r >> 2);
-        const int col = wn * WTN + j * 32 + ((lane >> 4) & 1) * 16 + 4 * (r & 3);
-        brd[j] = A_BYTES + K * BN * 2 + (((col >> 3) ^ gB(K)) << 4) + (col & 7) * 2;
+        const int r = lane & 15;
+        if constexpr (W8) {
+            // ds_read_b64_tr_b8: in each 16-lane group, lane i gets byte i % 8 of
+            // the 8-byte chunks addressed by lanes 2j' + i / 8 (j' = 0..7); lane
+            // 2j' + h points at k-row K0 + j', columns n0 + 8h .. + 7, so lane i
+            // receives column n0 + i at k-rows K0 .. K0 + 7
+            const int K = (lane >> 5) * 8 + (r >> 1);
+            const int col = wn * WTN + j * 32 + ((lane >> 4) & 1) * 16 + 8 * (r & 1);
+            brd[j] = A_BYTES + K * BN + (((col >> 4) ^ (K & 7)) << 4) + (col & 15);
+        } else {
+            const int K = (lane >> 5) * 8 + (r >> 2);
+            const int col = wn * WTN + j * 32 + ((lane >> 4) & 1) * 16 + 4 * (r & 3);
+            brd[j] = A_BYTES + K * BN * 2 + (((col >> 3) ^ gB(K)) << 4) + (col & 7) * 2;
+        }
     }
 
     f32x16 acc[FM][FN];
@@ -803,7 +828,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     const int KT = p.k / BK;   // >= 1 (the launcher sends k == 0 elsewhere)
-    const int64_t bstep = (int64_t)BK * p.n * 2;
+    const int64_t bstep = (int64_t)BK * p.n * BE;
     auto dma = [&](int d, int kt, int slot) {
         const uint32_t l = lds0 + slot * STAGE;
         if (d < APW)
@@ -812,9 +837,20 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             dma16_sbase(bof[d - APW], p.b + (int64_t)kt * bstep, l + A_BYTES + (wave * BPW + d - APW) * 1024);
     };
     u32x4 af[2][FM], bf[2][FN];
-    // fragment r of k step ks of a slot: r < 2 FN are weight halves, then activation rows
+    u32x2 bq[2][FN];   // w8: raw int8 weight fragments, dequantised right before use
+    // fragment r of k step ks of a slot: weight fragments (two halves each, or
+    // one int8 read each), then activation rows
     auto rdf = [&](int r, int slot, int ks, int buf) {
         const COC_LDS uint8_t* st = (const COC_LDS uint8_t*)sm + slot * STAGE;
+        if constexpr (W8) {
+            if (r < FN) {
+                bq[buf][r] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((COC_LDS i32x2*)(st + brd[r] + ks * 16 * BN)));
+            } else {
+                af[buf][r - FN] = *(const COC_LDS u32x4*)(st + ard[ks] + (r - FN) * 32 * BK * 2);
+            }
+            return;
+        }
         if (r < 2 * FN) {
             const int j = r >> 1, h = r & 1;
             const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -836,6 +872,69 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             if ((d * NMM) / DPW == s) dma(d, kt, slot);
     };
 
+    // w8A16 scales: spk[j] = this lane's scale (packed twice) for weight
+    // fragment j at the current stage.  Per tensor / per channel they are fixed
+    // for the tile; per group (group a multiple of 32, so one k-group per stage)
+    // the tile's k / group rows of BN scales sit in LDS and spn prefetches the
+    // next stage's.
+    uint32_t spk[FN] = {}, spn[FN] = {};
+    const bool grouped = W8 && p.qmode == COC_PER_GROUP;
+    auto scales_of = [&](int kt, uint32_t* out) {
+        const COC_LDS uint16_t* tbl = (const COC_LDS uint16_t*)((const COC_LDS uint8_t*)sm + TBL);
+        const int row = kt * BK / p.group;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const uint32_t s = tbl[row * BN + wn * WTN + j * 32 + (lane & 31)];
+            out[j] = s | (s << 16);
+        }
+    };
+    // int8 fragment -> fp16: 0x6400 | (q ^ 0x80) is 1024 + q + 128 exactly, so
+    // subtracting 1152 gives q; one fp16 multiply by the scale then rounds
+    // q * scale to nearest even, the dequantised weight.
+    auto deq = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const uint32_t x0 = bq[buf][j][0] ^ 0x80808080u, x1 = bq[buf][j][1] ^ 0x80808080u;
+            const uint32_t d[4] = {__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u),
+                                   __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u),
+                                   __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u),
+                                   __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)};
+            const f16x2 sc = __builtin_bit_cast(f16x2, spk[j]);
+            const f16x2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bf[buf][j][e] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, d[e]) + off) * sc);
+        }
+    };
+    if constexpr (W8) {
+        const uint16_t* sg = (const uint16_t*)p.scales;
+        if (p.qmode == COC_PER_TENSOR) {
+            const uint32_t s = sg[0];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) spk[j] = s | (s << 16);
+        } else if (p.qmode == COC_PER_CHANNEL) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+                const uint32_t s = sg[col < p.n ? col : 0];
+                spk[j] = s | (s << 16);
+            }
+        } else {
+            // the tile's scale rows into LDS: rows of BN fp16, 8 per 16-byte vector
+            uint8_t* tbl = sm + TBL;
+            const int rows_t = (p.k + p.group - 1) / p.group;
+            for (int v = threadIdx.x; v < rows_t * (BN / 8); v += 64 * NW) {
+                const int r = v / (BN / 8), c = (v % (BN / 8)) * 8;
+                const int col = n0 + c < p.n ? n0 + c : 0;
+                *(u32x4*)(tbl + (r * BN + c) * 2) = *(const u32x4*)(sg + (int64_t)r * p.n + col);
+            }
+            __syncthreads();
+            scales_of(0, spn);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" :: "v"(spk[j]), "v"(spn[j]));   // loads done before the DMA
+    }
+
     // prologue: stages 0 .. S-2 in flight, stage 0 visible, its k step 0 read
     for (int s = 0; s < S - 1; ++s)
         if (s < KT)
@@ -848,6 +947,13 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     auto stage = [&](int kt, auto LOAD, auto MORE, auto WAITN) {
         constexpr bool load = decltype(LOAD)::value, more = decltype(MORE)::value;
         const int slot = kt % S;
+        if constexpr (W8) {
+            if (grouped) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) spk[j] = spn[j];
+            }
+            deq(0);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < NMM; ++s) {
@@ -859,6 +965,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             wait_vmcnt<decltype(WAITN)::value>();
             block_barrier();
         }
+        if constexpr (W8) deq(1);
         __builtin_amdgcn_sched_barrier(0);
         const int nslot = (kt + 1) % S, dslot = (kt + S - 1) % S;
 #pragma unroll
@@ -867,6 +974,9 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             if constexpr (more) reads_at(s, nslot, 0, 0);
             if constexpr (load) dmas_at(s, kt + S - 1, dslot);
             __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (W8) {
+            if (grouped && kt + 1 < KT) scales_of(kt + 1, spn);
         }
     };
     using yes = std::true_type;
@@ -898,7 +1008,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     constexpr int CPR = WTN / 8;    // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;   // rows per store instruction
     static_assert(CPR % 8 == 0 && 64 % CPR == 0 && WTM % RPI == 0, "staging layout");
-    static_assert(NW * WTM * RP <= S * STAGE, "staging fits in the ring");
+    static_assert(NW * WTM * RP <= ring_lds_bytes<BM, BN, S, WM, WN, KIND>(), "staging fits in the LDS");
     block_barrier();
     // An opaque copy of the lane index: in the chunk-walking kernel the
     // compiler would otherwise hoist these lane-only LDS addresses out of the
@@ -938,7 +1048,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
 
 template <int BM, int BN, int S, int WM, int WN, int KIND>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_ring(GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t sm[ring_lds_bytes<BM, BN, S, WM, WN>()];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm[ring_lds_bytes<BM, BN, S, WM, WN, KIND>()];
     int tm, tn;
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
     ring_tile<BM, BN, S, WM, WN, KIND>(p, p.rows, p.rpb, p.base, p.stride, 0, tm * BM, tn * BN, sm, false);
@@ -968,7 +1078,7 @@ struct PersistParams {
 
 template <int BM, int BN, int S, int WM, int WN, int KIND, bool SIGNAL>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P) {
-    __shared__ __attribute__((aligned(1024))) uint8_t sm[ring_lds_bytes<BM, BN, S, WM, WN>()];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm[ring_lds_bytes<BM, BN, S, WM, WN, KIND>()];
     constexpr int NX = 8;
     const int x = blockIdx.x % NX, w = blockIdx.x / NX;
     const int tn_all = P.g.tiles_n;
@@ -1201,16 +1311,18 @@ __device__ __forceinline__ u32x4 sum_sources(const ReduceParams& p, const u32x4*
     return out;
 }
 
-template <int DT>
+// U = 2: two vectors per thread (~100 VGPRs); U = 1 (~50 VGPRs) beside a
+// matmul that leaves less room.
+template <int DT, int U>
 __global__ __launch_bounds__(256) void reduce_chunks_wait(ReduceParams p, ReduceChunks C) {
     const int stride = gridDim.x * 256;
     for (int c = 0; c < C.nchunks; ++c) {
         if (c > 0) __syncthreads();   // wg_wait's flag is reused
         const bool ok = wg_wait(C.done + c * kSyncWords, 1, C.target[c]);
         const int total = C.total[c];
-        for (int v = blockIdx.x * 256 + threadIdx.x; v < total; v += 2 * stride) {
+        for (int v = blockIdx.x * 256 + threadIdx.x; v < total; v += U * stride) {
             const int v2 = v + stride;
-            const bool two = v2 < total;
+            const bool two = U == 2 && v2 < total;
             const int row = v / p.vpr, row2 = v2 / p.vpr;
             const int64_t so = (C.src_row0[c] + row) * p.row_bytes + (int64_t)(v - row * p.vpr) * 16;
             const int64_t so2 = (C.src_row0[c] + row2) * p.row_bytes + (int64_t)(v2 - row2 * p.vpr) * 16;
@@ -1333,7 +1445,7 @@ hipError_t launch_dma_kind(GemmParams p, int concurrent, hipStream_t s) {
     // zero-fills the k tail.  Every choice walks k the same way, so it never
     // changes the result bits.
     if (p.k >= 32 && p.k % 32 == 0) {
-        if (concurrent <= 1) {
+        if (concurrent <= 1 || KIND == GK_W8_F16) {
             // a lone matmul: the chunk-walking launch with one chunk (measured
             // faster than one workgroup per tile: no second dispatch wave)
             ChunksLaunch L{};
@@ -1343,6 +1455,9 @@ hipError_t launch_dma_kind(GemmParams p, int concurrent, hipStream_t s) {
             L.n = p.n;
             L.k = p.k;
             L.npieces = 1;
+            L.scales = p.scales;
+            L.qmode = p.qmode;
+            L.group = p.group;
             L.a[0] = p.a;
             L.base[0] = p.base;
             L.stride[0] = p.stride;
@@ -1350,7 +1465,7 @@ hipError_t launch_dma_kind(GemmParams p, int concurrent, hipStream_t s) {
             L.nblk[0] = p.rows / (p.rpb > 0 ? p.rpb : 1);
             L.wait[0] = -1;
             L.signal[0] = -1;
-            int32_t tiles[kMaxPieces];
+            int32_t tiles[kMaxPieces + 1];
             return launch_chunks_kind<KIND>(L, s, tiles);
         }
         const int64_t want = COC_RING_MIN_TILES / (concurrent > 1 ? concurrent : 1);
@@ -1391,7 +1506,9 @@ int launch_gemm(const GemmLaunch& g, void* stream) {
         }
         case GK_F16: return launch_dma_kind<GK_F16>(p, g.concurrent, s);
         case GK_BF16: return launch_dma_kind<GK_BF16>(p, g.concurrent, s);
-        case GK_W8_F16: return launch_w8_any(p, s);
+        case GK_W8_F16:
+            if (chunks_supported(g)) return launch_dma_kind<GK_W8_F16>(p, 1, s);
+            return launch_w8_any(p, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1441,10 +1558,17 @@ int launch_reduce_chunks(const ReduceChunksLaunch& L, void* stream) {
     C.own = L.own;
     const int grid = grid_for(most) < 256 ? grid_for(most) : 256;   // at most one per CU
     hipStream_t s = (hipStream_t)stream;
+    auto go = [&](auto DTC) {
+        constexpr int DT = decltype(DTC)::value;
+        if (L.narrow)
+            hipLaunchKernelGGL((reduce_chunks_wait<DT, 1>), dim3(grid), dim3(256), 0, s, p, C);
+        else
+            hipLaunchKernelGGL((reduce_chunks_wait<DT, 2>), dim3(grid), dim3(256), 0, s, p, C);
+    };
     switch (r.dt) {
-        case COC_F32: hipLaunchKernelGGL(reduce_chunks_wait<COC_F32>, dim3(grid), dim3(256), 0, s, p, C); break;
-        case COC_F16: hipLaunchKernelGGL(reduce_chunks_wait<COC_F16>, dim3(grid), dim3(256), 0, s, p, C); break;
-        case COC_BF16: hipLaunchKernelGGL(reduce_chunks_wait<COC_BF16>, dim3(grid), dim3(256), 0, s, p, C); break;
+        case COC_F32: go(std::integral_constant<int, COC_F32>{}); break;
+        case COC_F16: go(std::integral_constant<int, COC_F16>{}); break;
+        case COC_BF16: go(std::integral_constant<int, COC_BF16>{}); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1470,8 +1594,12 @@ int launch_gather(const GatherLaunch& g, void* stream, int32_t* groups) {
     return e;
 }
 
-bool chunks_supported(GemmKind kind, int64_t k) {
-    return (kind == GK_BF16 || kind == GK_F16) && k >= 32 && k % 32 == 0;
+bool chunks_supported(const GemmLaunch& g) {
+    if (g.k < 32 || g.k % 32 != 0) return false;
+    if (g.kind == GK_BF16 || g.kind == GK_F16) return true;
+    if (g.kind != GK_W8_F16 || g.n % 16 != 0) return false;   // whole 16-byte int8 chunks
+    if (g.qmode != COC_PER_GROUP) return true;
+    return g.group % 32 == 0 && ((g.k + g.group - 1) / g.group) * 256 * 2 <= kW8TableBytes;
 }
 
 namespace {
@@ -1483,6 +1611,9 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     P.g.c = (uint8_t*)L.c;
     P.g.n = (int32_t)L.n;
     P.g.k = (int32_t)L.k;
+    P.g.scales = (const uint16_t*)L.scales;
+    P.g.qmode = L.qmode;
+    P.g.group = L.group > 0 ? L.group : 1;
     P.g.tiles_n = (int32_t)((L.n + BN - 1) / BN);
     P.npieces = L.npieces;
     bool signal = false;
@@ -1507,6 +1638,7 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     P.ready = L.ready;
     const int64_t cap = 32 * per_cu;   // 256 CUs / 8 XCDs, times workgroups per CU
     P.per_xcd = (int32_t)(longest < cap ? (longest > 0 ? longest : 1) : cap);
+    tiles[kMaxPieces] = 8 * P.per_xcd;
     if (signal)
         hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true>), dim3(8 * P.per_xcd), dim3(64 * WM * WN),
                            0, s, P);
@@ -1532,12 +1664,13 @@ hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* til
 
 }  // namespace
 
-int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[kMaxPieces]) {
-    for (int c = 0; c < kMaxPieces; ++c) tiles[c] = 0;
+int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[kMaxPieces + 1]) {
+    for (int c = 0; c <= kMaxPieces; ++c) tiles[c] = 0;
     hipStream_t s = (hipStream_t)stream;
     switch (L.kind) {
         case GK_F16: return launch_chunks_kind<GK_F16>(L, s, tiles);
         case GK_BF16: return launch_chunks_kind<GK_BF16>(L, s, tiles);
+        case GK_W8_F16: return launch_chunks_kind<GK_W8_F16>(L, s, tiles);
         default: return hipErrorInvalidValue;
     }
 }

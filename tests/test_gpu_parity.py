@@ -226,12 +226,16 @@ def test_allgather_matmul(dtype, split, rank, k):
 # ------------------------------------------------------------------ w8a16
 @pytest.mark.parametrize("mode", ["per_tensor", "per_channel", "per_group"])
 @pytest.mark.parametrize("split", [1, 4])
-def test_w8a16_exact_with_power_of_two_scales(mode, split):
+@pytest.mark.parametrize("n,g", [(520, 128), (1040, 128), (1040, 32), (528, 16)])
+def test_w8a16_exact_with_power_of_two_scales(mode, split, n, g):
     """X in {-2..2}, q in {-15..15}, scales 2^-6..2^-2 differing per channel and
     group: every product and the binary32 sums are exact, so partial_out is the
-    correctly rounded exact result, bit for bit, whatever the scale index."""
-    log(f"w8a16 exact {mode} split={split}")
-    m, n, k, g, world, rank = 256, 520, 512, 128, 4, 1
+    correctly rounded exact result, bit for bit, whatever the scale index.
+    n % 16 == 0 with group a multiple of 32 takes the ring kernel (int8
+    transpose reads, in-register dequantisation); the others the
+    register-staged kernel."""
+    log(f"w8a16 exact {mode} split={split} n={n} g={g}")
+    m, k, world, rank = 256, 512, 4, 1
     x = _ints(7, (m, k), -2, 2, "f16")
     q = synth.integers(WID_TEST + 7, synth.T_W, 0, (k, n), -15, 15, "i8")
     shape = {"per_tensor": (1,), "per_channel": (n,), "per_group": (k // g, n)}[mode]
@@ -247,7 +251,7 @@ def test_w8a16_exact_with_power_of_two_scales(mode, split):
 
 
 @pytest.mark.parametrize("mode,group", [("per_tensor", 0), ("per_channel", 0), ("per_group", 128),
-                                        ("per_group", 64)])
+                                        ("per_group", 64), ("per_group", 16)])
 def test_w8a16_random(mode, group):
     log(f"w8a16 random {mode} g={group}")
     m, n, k, world, rank = 384, 1024, 512, 8, 2
