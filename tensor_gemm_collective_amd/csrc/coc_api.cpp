@@ -353,20 +353,23 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
     L.k = g0.k;
     L.ready = c->sync + COC_MAX_SPLIT * kSyncWords;
     add_piece(&L, a0.src[P.rank], -own0, own0, shard, -1);
+    int64_t grow0[COC_MAX_SPLIT], grows[COC_MAX_SPLIT];
+    double bytes = 0;
     for (int i = 0; i < P.nchunks; ++i) {
-        GatherLaunch a = a0;
-        a.row0 = P.chunk[i].red_base;
-        a.rows = P.chunk[i].red_rows;
-        a.signal = c->sync + (COC_MAX_SPLIT + i * kReadyLines) * kSyncWords;
-        int32_t groups = 0;
-        const double bytes = 2.0 * double(a.rows) * double(P.k) * double(es);
-        COC_TRY(launch(KC_GATHER, bytes, c->side, [&] { return launch_gather(a, c->side, &groups); }));
-        L.ready_target[i] = c->ready_sent[i] += (uint32_t)groups;
+        grow0[i] = P.chunk[i].red_base;
+        grows[i] = P.chunk[i].red_rows;
+        bytes += 2.0 * double(grows[i]) * double(P.k) * double(es);
         // the chunk's rows outside the own shard (AG chunks are contiguous)
         const int64_t r0 = P.chunk[i].base, r1 = r0 + P.chunk[i].rows_per_blk * P.chunk[i].nblk;
         add_piece(&L, g0.a, 0, r0, (r1 < own0 ? r1 : own0) - r0, i);
         add_piece(&L, g0.a, 0, r0 > own1 ? r0 : own1, r1 - (r0 > own1 ? r0 : own1), i);
     }
+    int32_t per_chunk = 0;
+    COC_TRY(launch(KC_GATHER, bytes, c->side, [&] {
+        return launch_gather_chunks(a0, P.nchunks, grow0, grows, c->sync + COC_MAX_SPLIT * kSyncWords, c->side,
+                                    &per_chunk);
+    }));
+    for (int i = 0; i < P.nchunks; ++i) L.ready_target[i] = c->ready_sent[i] += (uint32_t)per_chunk;
     int32_t tiles[kMaxPieces + 1];
     COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
     COC_HIP(hipEventRecord(c->join, c->side));

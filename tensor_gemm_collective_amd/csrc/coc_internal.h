@@ -138,6 +138,11 @@ int launch_reduce(const ReduceLaunch& r, void* stream);
 int launch_reduce_chunks(const ReduceChunksLaunch& r, void* stream);
 // *groups (if given) receives the number of workgroups launched (signals sent).
 int launch_gather(const GatherLaunch& g, void* stream, int32_t* groups = nullptr);
+// Every chunk of an all-gather in one launch (system-scope stores); chunk c's
+// workgroups then add 1 each to its ready lines (at ready + c * kReadyLines
+// lines).  *per_chunk receives the workgroups per chunk (the adds each gets).
+int launch_gather_chunks(const GatherLaunch& g, int nchunks, const int64_t* row0, const int64_t* rows,
+                         uint32_t* ready, void* stream, int32_t* per_chunk);
 
 // Whether the ring kernels take this matmul (bf16 / fp16 with k a positive
 // multiple of 32; w8a16 also needs n % 16 == 0 and, per group, group % 32 == 0

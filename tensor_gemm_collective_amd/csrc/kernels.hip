@@ -1394,6 +1394,41 @@ __global__ __launch_bounds__(256) void gather_rows(GatherParams p) {
     if (p.signal != nullptr) wg_signal(p.signal + (blockIdx.x % kReadyLines) * kSyncWords);
 }
 
+// Every chunk of an all-gather in one launch: workgroups [c*per_chunk,
+// (c+1)*per_chunk) copy chunk c (rows row0[c] .. row0[c] + rows[c]) and then
+// add 1 to that chunk's ready lines.  Workgroups are dispatched in id order,
+// so chunk 0's rows land first, without a kernel boundary between chunks.
+struct GatherChunks {
+    int32_t row0[COC_MAX_SPLIT], total[COC_MAX_SPLIT];   // first row; rows * vpr
+    uint32_t* ready;                                      // chunk c's lines at c * kReadyLines
+    int32_t per_chunk;
+};
+
+__global__ __launch_bounds__(256) void gather_chunks(GatherParams p, GatherChunks C) {
+    constexpr int U = 4;
+    const int c = blockIdx.x / C.per_chunk, lb = blockIdx.x % C.per_chunk;
+    const int total = C.total[c];
+    const int per = (total + C.per_chunk - 1) / C.per_chunk;   // vectors of this workgroup
+    const int v_end = (lb + 1) * per < total ? (lb + 1) * per : total;
+    p.row0 = C.row0[c];
+    p.total = v_end;
+    for (int v0 = lb * per + threadIdx.x; v0 < v_end; v0 += U * 256) {
+        u32x4 x[U];
+        int64_t off[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * 256;
+            if (v < v_end) x[u] = *(const u32x4*)gather_src(p, v, &off[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (v0 + u * 256 >= v_end) break;
+            store16_sys(sys_rsrc(p.dst), (uint32_t)off[u], x[u]);   // read by a matmul already running
+        }
+    }
+    wg_signal(C.ready + (c * kReadyLines + lb % kReadyLines) * kSyncWords);
+}
+
 int grid_for(int64_t total_vec, int per_thread = 1) {
     const int64_t want = (total_vec + 256 * per_thread - 1) / (256 * per_thread);
     const int64_t cap = 256 * 8;
@@ -1591,6 +1626,34 @@ int launch_gather(const GatherLaunch& g, void* stream, int32_t* groups) {
     hipLaunchKernelGGL(gather_rows, dim3(grid), dim3(256), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess && groups != nullptr) *groups = grid;
+    return e;
+}
+
+int launch_gather_chunks(const GatherLaunch& g, int nchunks, const int64_t* row0, const int64_t* rows,
+                         uint32_t* ready, void* stream, int32_t* per_chunk) {
+    *per_chunk = 0;
+    if (g.k == 0 || nchunks == 0) return hipSuccess;
+    GatherParams p{};
+    for (int i = 0; i < COC_MAX_WORLD; ++i) p.src[i] = (const uint8_t*)(i < g.nsrc ? g.src[i] : g.src[0]);
+    p.dst = (uint8_t*)g.dst;
+    p.row_bytes = g.k * (int64_t)elem_size(g.dt);
+    p.shard_rows = (int32_t)g.shard_rows;
+    p.vpr = (int32_t)(p.row_bytes / 16);
+    GatherChunks C{};
+    int64_t most = 0;
+    for (int c = 0; c < nchunks; ++c) {
+        C.row0[c] = (int32_t)row0[c];
+        C.total[c] = (int32_t)(rows[c] * p.vpr);
+        most = C.total[c] > most ? C.total[c] : most;
+    }
+    C.ready = ready;
+    // up to 2048 workgroups in all, each with at least 4 passes of 4 vectors per thread
+    const int64_t want = (most + 4 * 4 * 256 - 1) / (4 * 4 * 256);
+    const int64_t cap = 2048 / nchunks;
+    C.per_chunk = (int32_t)(want < cap ? (want > 0 ? want : 1) : cap);
+    hipLaunchKernelGGL(gather_chunks, dim3(C.per_chunk * nchunks), dim3(256), 0, (hipStream_t)stream, p, C);
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) *per_chunk = C.per_chunk;
     return e;
 }
 
