@@ -8,9 +8,11 @@ A step is one TP8 + sequence-parallel MLP pass of one rank at LLaMA2-70B shapes:
                         reduce-scattered to this rank's 512 x 8192 slice
 both bf16, split into `--split` m-chunks.  The other ranks' shards and partial
 sums are seeded buffers in the same HBM.  Prints one JSON line on stdout
-(progress goes to stderr).
+(progress goes to stderr).  Before the W warmup steps, untimed steps run for
+--prewarm-s seconds (default 0.5) so that the K timed steps see the GPU at its
+steady clocks; the JSON line reports them under "prewarm".
 
-    python bench.py [--steps K] [--warmup W] [--split S] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--split S] [--prewarm-s T] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -207,6 +209,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prewarm-s", type=float, default=0.5,
+                    help="before the warmup steps, run untimed steps for this many seconds so the GPU "
+                         "reaches its steady clocks (0: off)")
     ap.add_argument("--split", type=int, default=4, choices=[1, 2, 4, 8])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frac", type=float, default=1.0)
@@ -264,7 +269,17 @@ def main():
         run_ag()
         run_rs()
 
-    log(f"warmup {args.warmup} steps ...")
+    # The GPU idles while the inputs are generated on the host; a few
+    # milliseconds of warmup steps leave it short of its steady clocks, which
+    # costs about a tenth of the step rate.  Untimed steps for prewarm_s
+    # seconds first (not counted in the K timed steps).
+    prewarm_steps, t_pre = 0, time.perf_counter()
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        prewarm_steps += 20
+    log(f"prewarm {prewarm_steps} steps, then warmup {args.warmup} steps ...")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -354,6 +369,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm": {"seconds": args.prewarm_s, "steps": prewarm_steps},
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

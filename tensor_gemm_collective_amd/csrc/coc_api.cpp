@@ -32,6 +32,12 @@
 #ifndef COC_COMPUTE_STREAMS
 #define COC_COMPUTE_STREAMS 2
 #endif
+// 1: the all-gather pipeline's copy runs inside its chunk-walking matmul
+// launch (by the workgroups with one tile) where the launch allows it; 0: as
+// a separate launch on the side stream.
+#ifndef COC_FUSED_GATHER
+#define COC_FUSED_GATHER 1
+#endif
 // 1: bf16 / fp16 pipelines with k a multiple of 32 run all chunk matmuls of an
 // op in one chunk-walking launch (hand-over through device counters); 0: one
 // launch per chunk on the two compute streams.
@@ -341,8 +347,6 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
     const size_t es = elem_size(P.dt);
-    COC_HIP(hipEventRecord(c->fork, main));
-    COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
     const int64_t shard = P.m / P.world;
     const int64_t own0 = P.rank * shard, own1 = own0 + shard;
     ChunksLaunch L{};
@@ -364,13 +368,32 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
         add_piece(&L, g0.a, 0, r0, (r1 < own0 ? r1 : own0) - r0, i);
         add_piece(&L, g0.a, 0, r0 > own1 ? r0 : own1, r1 - (r0 > own1 ? r0 : own1), i);
     }
+    int32_t tiles[kMaxPieces + 1];
+    L.gather_nchunks = P.nchunks;   // (the plan depends on it)
+    const FusedGatherPlan fp = COC_FUSED_GATHER ? chunks_fused_gather(L) : FusedGatherPlan{};
+    if (fp.gatherers > 0) {
+        // the matmul launch copies the rows itself, chunk by chunk
+        L.gather_plan = fp;
+        for (int r = 0; r < COC_MAX_WORLD; ++r) L.gather_src[r] = a0.src[r < a0.nsrc ? r : 0];
+        L.gather_dst = a0.dst;
+        L.gather_row_bytes = P.k * (int64_t)es;
+        L.gather_shard_rows = shard;
+        for (int i = 0; i < P.nchunks; ++i) {
+            L.gather_row0[i] = grow0[i];
+            L.gather_rows[i] = grows[i];
+            L.ready_target[i] = c->ready_sent[i] += (uint32_t)(i < fp.early ? fp.workgroups : fp.gatherers);
+        }
+        return launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); });
+    }
+    L.gather_nchunks = 0;
+    COC_HIP(hipEventRecord(c->fork, main));
+    COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
     int32_t per_chunk = 0;
     COC_TRY(launch(KC_GATHER, bytes, c->side, [&] {
         return launch_gather_chunks(a0, P.nchunks, grow0, grows, c->sync + COC_MAX_SPLIT * kSyncWords, c->side,
                                     &per_chunk);
     }));
     for (int i = 0; i < P.nchunks; ++i) L.ready_target[i] = c->ready_sent[i] += (uint32_t)per_chunk;
-    int32_t tiles[kMaxPieces + 1];
     COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
     COC_HIP(hipEventRecord(c->join, c->side));
     COC_HIP(hipStreamWaitEvent(main, c->join, 0));

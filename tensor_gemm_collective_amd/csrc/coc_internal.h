@@ -91,6 +91,15 @@ struct GatherLaunch {
 // piece i it adds 1 to done[signal[i]] (signal[i] >= 0, done set).  Counter
 // layout as below.
 constexpr int kMaxPieces = 16;
+// How a chunk-walking launch runs the all-gather itself (see
+// chunks_fused_gather): chunks [0, early) are copied by all `workgroups` of
+// the launch, the rest by `gatherers` of them; each adds 1 per chunk share to
+// that chunk's ready lines.  gatherers == 0: the launch cannot (it needs at
+// least 16 one-tile workgroups and all workgroups resident at once).
+struct FusedGatherPlan {
+    int32_t gatherers, early, workgroups;
+};
+
 struct ChunksLaunch {
     GemmKind kind;
     const void* b;
@@ -106,8 +115,18 @@ struct ChunksLaunch {
     int32_t wait[kMaxPieces];
     int32_t signal[kMaxPieces];
     uint32_t* done;
-    const uint32_t* ready;
+    uint32_t* ready;
     uint32_t ready_target[COC_MAX_SPLIT];
+    // All-gather rows that the launch's one-tile workgroups copy before their
+    // tile (gather_nchunks > 0; see chunks_fused_gatherers): gathered row g of
+    // chunk c's rows [gather_row0[c], + gather_rows[c]) comes from row
+    // g % gather_shard_rows of gather_src[g / gather_shard_rows].
+    int32_t gather_nchunks;
+    FusedGatherPlan gather_plan;   // as chunks_fused_gather returned it (the launch checks it)
+    const void* gather_src[COC_MAX_WORLD];
+    void* gather_dst;
+    int64_t gather_row_bytes, gather_shard_rows;
+    int64_t gather_row0[COC_MAX_SPLIT], gather_rows[COC_MAX_SPLIT];
 };
 
 // Layout of the chunk hand-over counters (device memory, 32-bit words): each
@@ -151,5 +170,8 @@ bool chunks_supported(const GemmLaunch& g);
 // tiles[i] receives the tile count of piece i (the adds its signal gets) and
 // tiles[kMaxPieces] the number of workgroups launched.
 int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[kMaxPieces + 1]);
+// The plan by which L's launch would run the gather itself (L.gather_nchunks
+// set); the caller sets each chunk's ready target from it.
+FusedGatherPlan chunks_fused_gather(const ChunksLaunch& L);
 
 }  // namespace coc

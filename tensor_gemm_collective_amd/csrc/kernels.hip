@@ -1054,16 +1054,56 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring(GemmParams p) {
     ring_tile<BM, BN, S, WM, WN, KIND>(p, p.rows, p.rpb, p.base, p.stride, 0, tm * BM, tn * BN, sm, false);
 }
 
+// ------------------------------------------------------------------ gather
+// dst row g (g in [row0, row0 + rows)) = row g % shard_rows of shard
+// g / shard_rows; 16-byte vector copies.
+struct GatherParams {
+    const uint8_t* src[COC_MAX_WORLD];
+    uint8_t* dst;
+    int64_t row_bytes;   // k * element size
+    int32_t shard_rows;
+    int32_t row0;
+    int32_t vpr;
+    int32_t total;
+    uint32_t* signal;    // if set, each workgroup adds 1 when its rows are stored
+};
+
+// Vector v of the rows from row0 on.  p must be the kernel argument itself
+// (not a copy): src[s] then loads from the argument segment instead of
+// making a private copy of the pointer array.
+__device__ __forceinline__ const uint8_t* gather_src(const GatherParams& p, int row0, int v, int64_t* off) {
+    const int row = v / p.vpr;
+    const int cv = v - row * p.vpr;
+    const int g = row0 + row;
+    const int s = g / p.shard_rows;
+    const int local = g - s * p.shard_rows;
+    *off = (int64_t)g * p.row_bytes + (int64_t)cv * 16;
+    return p.src[s] + (int64_t)local * p.row_bytes + (int64_t)cv * 16;
+}
+
 // Chunk-walking form of the ring kernel: one launch covers every chunk of an
 // op, as a list of pieces (see ChunksLaunch).  8 * per_xcd workgroups (one per
 // CU for the 256-wide tiles, two for 128 x 128); workgroup b runs on XCD b % 8
-// and walks that XCD's tile list: piece by piece in order, within a piece the
-// XCD's run of xcd_tile's split in grouped order, taking every per_xcd-th
-// item.  A piece can wait for a group of ready counters before its first tile;
+// and walks that XCD's tile list (piece by piece in order, within a piece the
+// XCD's run of xcd_tile's split in grouped order) as schedule_item assigns
+// it.  A piece can wait for a group of ready counters before its first tile;
 // with SIGNAL, tiles are stored write-through and add 1 to their piece's done
 // counter.  Gathered rows are read through the L2 as usual: no line of a piece
 // can be cached before its wait (rows are whole 128-byte lines and nothing
 // reads them earlier in this launch), and the gather writes them through.
+//
+// Fused all-gather: the launch copies the chunks' rows into the gathered
+// matrix itself, chunk by chunk, adding 1 to a chunk's ready lines after each
+// share of it.  Chunks [0, early), which the first tiles of the two-tile
+// workgroups (below) read, are copied by every workgroup before its first
+// tile, so those tiles start together; the rest by the workgroups that own a
+// single tile of the last two rounds, which have a tile's time to spare.
+struct FusedGather {
+    GatherParams p;                    // src, dst, row_bytes, shard_rows, vpr (row0 / total per chunk)
+    int32_t row0[COC_MAX_SPLIT], total[COC_MAX_SPLIT];
+    int32_t nchunks, early, gatherers; // gatherers == 0: no fused gather
+};
+
 struct PersistParams {
     GemmParams g;   // b, c, n, k, tiles_n (a and the row map fields unused)
     const uint8_t* a[kMaxPieces];
@@ -1073,8 +1113,84 @@ struct PersistParams {
     uint32_t ready_target[COC_MAX_SPLIT];
     int32_t npieces, per_xcd;
     uint32_t* done;
-    const uint32_t* ready;
+    uint32_t* ready;
+    FusedGather fg;
 };
+
+// Items of XCD x's list (the pieces' tiles split over the 8 XCDs).
+// (A piece has tiles_m[c] * tiles_n tiles.)
+__host__ __device__ inline int xcd_items(const int32_t* tiles_m, int tiles_n, int npieces, int x) {
+    int l = 0;
+    for (int c = 0; c < npieces; ++c) {
+        const int t = tiles_m[c] * tiles_n;
+        l += t / 8 + (x < t % 8 ? 1 : 0);
+    }
+    return l;
+}
+
+// The s-th item of workgroup w among per_xcd on a list of l items, or -1.
+// Whole rounds first (w, w + per_xcd, ...); the last two rounds, with
+// l' items, have d = l' - per_xcd workgroups doing two items and the rest
+// one: the two-item workgroups take the first d items and then the next d,
+// the one-item workgroups the last ones.  List order is chunk order, so the
+// workgroups that must also finish a second tile start on the chunks that
+// are ready first, and those that start last have a whole tile of slack.
+__host__ __device__ inline int schedule_item(int l, int per_xcd, int w, int s) {
+    if (l <= per_xcd) return s == 0 && w < l ? w : -1;
+    const int rounds = (l + per_xcd - 1) / per_xcd;
+    if (s < rounds - 2) return s * per_xcd + w;
+    const int b = (rounds - 2) * per_xcd, d = l - b - per_xcd, t = s - (rounds - 2);
+    if (w < d) return t == 0 ? b + w : (t == 1 ? b + d + w : -1);
+    return t == 0 ? b + 2 * d + (w - d) : -1;
+}
+
+// One-item workgroups of the last two rounds over XCDs 0..x-1, and on XCD x
+// the first such workgroup (-1 if the list has no such last two rounds).
+__host__ __device__ inline int singles_before(const int32_t* tiles_m, int tiles_n, int npieces, int per_xcd, int x,
+                                              int* first) {
+    int n = 0;
+    for (int y = 0; y <= x; ++y) {
+        const int l = xcd_items(tiles_m, tiles_n, npieces, y);
+        int d = -1, singles = 0;
+        if (l > per_xcd) {
+            const int rounds = (l + per_xcd - 1) / per_xcd;
+            d = l - (rounds - 2) * per_xcd - per_xcd;
+            singles = per_xcd - d;
+        }
+        if (y == x) *first = d;
+        else n += singles;
+    }
+    return n;
+}
+
+// Share gi of ng of chunks [c0, c1), 16 vectors per thread in flight (the
+// matmul's registers are free before its first tile), stores written through
+// for the other XCDs' matmul workgroups; then 1 added to the chunk's ready
+// lines.
+__device__ __forceinline__ void fused_gather(const FusedGather& F, int c0, int c1, int gi, int ng, uint32_t* ready) {
+    constexpr int U = 16;
+    const int nt = blockDim.x;
+    const GatherParams& p = F.p;
+    for (int c = c0; c < c1; ++c) {
+        const int row0 = F.row0[c], total = F.total[c];
+        const int v0 = (int)((int64_t)gi * total / ng), v1 = (int)((int64_t)(gi + 1) * total / ng);
+        for (int b = v0 + (int)threadIdx.x; b < v1; b += U * nt) {
+            u32x4 x[U];
+            int64_t off[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = b + u * nt;
+                if (v < v1) x[u] = *(const u32x4*)gather_src(p, row0, v, &off[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (b + u * nt >= v1) break;
+                store16_sys(sys_rsrc(p.dst), (uint32_t)off[u], x[u]);
+            }
+        }
+        wg_signal(ready + (c * kReadyLines + gi % kReadyLines) * kSyncWords);
+    }
+}
 
 template <int BM, int BN, int S, int WM, int WN, int KIND, bool SIGNAL>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P) {
@@ -1082,9 +1198,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P
     constexpr int NX = 8;
     const int x = blockIdx.x % NX, w = blockIdx.x / NX;
     const int tn_all = P.g.tiles_n;
+    const int l = xcd_items(P.tiles_m, tn_all, P.npieces, x);
+    if (P.fg.gatherers > 0) {
+        int first = -1;
+        const int before = singles_before(P.tiles_m, tn_all, P.npieces, P.per_xcd, x, &first);
+        fused_gather(P.fg, 0, P.fg.early, blockIdx.x, gridDim.x, P.ready);
+        if (first >= 0 && w >= first)
+            fused_gather(P.fg, P.fg.early, P.fg.nchunks, before + (w - first), P.fg.gatherers, P.ready);
+    }
     int waited = -1;
     bool ok = true;
-    for (int j = w;; j += P.per_xcd) {
+    for (int s = 0;; ++s) {
+        const int j = schedule_item(l, P.per_xcd, w, s);
+        if (j < 0) break;
         int c = 0, jj = j;
         for (; c < P.npieces; ++c) {
             const int T = P.tiles_m[c] * tn_all;
@@ -1341,36 +1467,10 @@ __global__ __launch_bounds__(256) void reduce_chunks_wait(ReduceParams p, Reduce
 }
 
 // ------------------------------------------------------------------ gather
-// dst row g (g in [row0, row0 + rows)) = row g % shard_rows of shard
-// g / shard_rows; 16-byte vector copies.
-struct GatherParams {
-    const uint8_t* src[COC_MAX_WORLD];
-    uint8_t* dst;
-    int64_t row_bytes;   // k * element size
-    int32_t shard_rows;
-    int32_t row0;
-    int32_t vpr;
-    int32_t total;
-    uint32_t* signal;    // if set, each workgroup adds 1 when its rows are stored
-};
-
-// Four 16-byte vectors per thread per pass, all loaded before any is stored:
-// beside a running matmul only a few gather waves fit on each CU, and the
-// copy rate is set by the bytes they keep in flight.
-__device__ __forceinline__ const uint8_t* gather_src(const GatherParams& p, int v, int64_t* off) {
-    const int row = v / p.vpr;
-    const int cv = v - row * p.vpr;
-    const int g = p.row0 + row;
-    const int s = g / p.shard_rows;
-    const int local = g - s * p.shard_rows;
-    const uint8_t* sp = p.src[0];
-#pragma unroll
-    for (int i = 1; i < COC_MAX_WORLD; ++i)
-        if (s == i) sp = p.src[i];
-    *off = (int64_t)g * p.row_bytes + (int64_t)cv * 16;
-    return sp + (int64_t)local * p.row_bytes + (int64_t)cv * 16;
-}
-
+// (GatherParams and gather_src sit above the chunk-walking matmul, which can
+// also run the copy itself.)  Four 16-byte vectors per thread per pass, all
+// loaded before any is stored: beside a running matmul only a few gather
+// waves fit on each CU, and the copy rate is set by the bytes in flight.
 __global__ __launch_bounds__(256) void gather_rows(GatherParams p) {
     constexpr int U = 4;
     const int stride = gridDim.x * 256;
@@ -1380,7 +1480,7 @@ __global__ __launch_bounds__(256) void gather_rows(GatherParams p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = v0 + u * stride;
-            if (v < p.total) x[u] = *(const u32x4*)gather_src(p, v, &off[u]);
+            if (v < p.total) x[u] = *(const u32x4*)gather_src(p, p.row0, v, &off[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -1410,15 +1510,14 @@ __global__ __launch_bounds__(256) void gather_chunks(GatherParams p, GatherChunk
     const int total = C.total[c];
     const int per = (total + C.per_chunk - 1) / C.per_chunk;   // vectors of this workgroup
     const int v_end = (lb + 1) * per < total ? (lb + 1) * per : total;
-    p.row0 = C.row0[c];
-    p.total = v_end;
+    const int row0 = C.row0[c];
     for (int v0 = lb * per + threadIdx.x; v0 < v_end; v0 += U * 256) {
         u32x4 x[U];
         int64_t off[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = v0 + u * 256;
-            if (v < v_end) x[u] = *(const u32x4*)gather_src(p, v, &off[u]);
+            if (v < v_end) x[u] = *(const u32x4*)gather_src(p, row0, v, &off[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -1667,6 +1766,48 @@ bool chunks_supported(const GemmLaunch& g) {
 
 namespace {
 
+// Tile shape of a chunk-walking launch: the largest tile that still fills the
+// 256 CUs once over the whole op (0: 256 x 256, 1: 128 x 256, 2: 128 x 128).
+int chunks_shape(const ChunksLaunch& L, int* bm, int* bn, int* per_cu) {
+    int64_t t256 = 0, t128x256 = 0;
+    for (int c = 0; c < L.npieces; ++c) {
+        const int64_t rows = L.rpb[c] * L.nblk[c];
+        t256 += ((rows + 255) / 256) * ((L.n + 255) / 256);
+        t128x256 += ((rows + 127) / 128) * ((L.n + 255) / 256);
+    }
+    if (t256 >= 256) { *bm = 256; *bn = 256; *per_cu = 1; return 0; }
+    if (t128x256 >= 256) { *bm = 128; *bn = 256; *per_cu = 1; return 1; }
+    *bm = 128; *bn = 128; *per_cu = 2;
+    return 2;
+}
+
+// Per-piece tiles and workgroups per XCD of a chunk-walking launch.
+int chunks_layout(const ChunksLaunch& L, int32_t* tiles, int* per_cu) {
+    int bm, bn;
+    chunks_shape(L, &bm, &bn, per_cu);
+    const int64_t tiles_n = (L.n + bn - 1) / bn;
+    int64_t longest = 0;   // XCD 0's list: ceil(T_i / 8) summed over pieces
+    for (int c = 0; c < L.npieces; ++c) {
+        const int64_t rows = L.rpb[c] * L.nblk[c];
+        tiles[c] = (int32_t)(((rows + bm - 1) / bm) * tiles_n);
+        longest += (tiles[c] + 7) / 8;
+    }
+    const int64_t cap = 32 * *per_cu;   // 256 CUs / 8 XCDs, times workgroups per CU
+    return (int)(longest < cap ? (longest > 0 ? longest : 1) : cap);
+}
+
+int device_cus() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
 template <int BM, int BN, int S, int WM, int WN, int KIND>
 hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s, int32_t* tiles) {
     PersistParams P{};
@@ -1680,7 +1821,8 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     P.g.tiles_n = (int32_t)((L.n + BN - 1) / BN);
     P.npieces = L.npieces;
     bool signal = false;
-    int64_t longest = 0;   // XCD 0's list: ceil(T_i / 8) summed over pieces
+    int per_cu_chk = 0;
+    P.per_xcd = chunks_layout(L, tiles, &per_cu_chk);
     for (int c = 0; c < L.npieces; ++c) {
         const int64_t rows = L.rpb[c] * L.nblk[c];
         P.a[c] = (const uint8_t*)L.a[c];
@@ -1693,14 +1835,30 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
         P.wait[c] = L.wait[c];
         P.signal[c] = L.signal[c];
         signal = signal || (L.done != nullptr && L.signal[c] >= 0);
-        tiles[c] = P.tiles_m[c] * P.g.tiles_n;
-        longest += (tiles[c] + 7) / 8;
     }
     for (int i = 0; i < COC_MAX_SPLIT; ++i) P.ready_target[i] = L.ready_target[i];
     P.done = L.done;
     P.ready = L.ready;
-    const int64_t cap = 32 * per_cu;   // 256 CUs / 8 XCDs, times workgroups per CU
-    P.per_xcd = (int32_t)(longest < cap ? (longest > 0 ? longest : 1) : cap);
+    if (L.gather_nchunks > 0) {
+        // the caller's ready targets assume this very plan
+        const FusedGatherPlan fp = chunks_fused_gather(L);
+        if (fp.gatherers <= 0 || L.ready == nullptr || fp.gatherers != L.gather_plan.gatherers ||
+            fp.early != L.gather_plan.early || fp.workgroups != L.gather_plan.workgroups)
+            return hipErrorInvalidValue;
+        FusedGather& F = P.fg;
+        for (int i = 0; i < COC_MAX_WORLD; ++i) F.p.src[i] = (const uint8_t*)L.gather_src[i];
+        F.p.dst = (uint8_t*)L.gather_dst;
+        F.p.row_bytes = L.gather_row_bytes;
+        F.p.shard_rows = (int32_t)L.gather_shard_rows;
+        F.p.vpr = (int32_t)(L.gather_row_bytes / 16);
+        F.nchunks = L.gather_nchunks;
+        for (int c = 0; c < L.gather_nchunks; ++c) {
+            F.row0[c] = (int32_t)L.gather_row0[c];
+            F.total[c] = (int32_t)(L.gather_rows[c] * F.p.vpr);
+        }
+        F.gatherers = fp.gatherers;
+        F.early = fp.early;
+    }
     tiles[kMaxPieces] = 8 * P.per_xcd;
     if (signal)
         hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true>), dim3(8 * P.per_xcd), dim3(64 * WM * WN),
@@ -1713,19 +1871,48 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
 
 template <int KIND>
 hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* tiles) {
-    // largest tile that still fills the 256 CUs once over the whole op
-    int64_t t256 = 0, t128x256 = 0;
-    for (int c = 0; c < L.npieces; ++c) {
-        const int64_t rows = L.rpb[c] * L.nblk[c];
-        t256 += ((rows + 255) / 256) * ((L.n + 255) / 256);
-        t128x256 += ((rows + 127) / 128) * ((L.n + 255) / 256);
+    int bm, bn, per_cu;
+    switch (chunks_shape(L, &bm, &bn, &per_cu)) {
+        case 0: return launch_chunks_shape<256, 256, 4, 2, 4, KIND>(L, 1, s, tiles);
+        case 1: return launch_chunks_shape<128, 256, 4, 2, 4, KIND>(L, 1, s, tiles);
+        default: return launch_chunks_shape<128, 128, 4, 2, 2, KIND>(L, 2, s, tiles);
     }
-    if (t256 >= 256) return launch_chunks_shape<256, 256, 4, 2, 4, KIND>(L, 1, s, tiles);
-    if (t128x256 >= 256) return launch_chunks_shape<128, 256, 4, 2, 4, KIND>(L, 1, s, tiles);
-    return launch_chunks_shape<128, 128, 4, 2, 2, KIND>(L, 2, s, tiles);
 }
 
 }  // namespace
+
+FusedGatherPlan chunks_fused_gather(const ChunksLaunch& L) {
+    FusedGatherPlan fp{};
+    int32_t tiles[kMaxPieces];
+    int per_cu = 0;
+    const int per_xcd = chunks_layout(L, tiles, &per_cu);
+    // every workgroup must be resident at once (one per CU): workgroups wait
+    // for rows that others copy
+    if (per_cu != 1 || 8 * per_xcd > device_cus()) return fp;
+    int first = -1;
+    const int g = singles_before(tiles, 1, L.npieces, per_xcd, 8, &first);   // over XCDs 0..7
+    if (g < 16) return fp;
+    // early: one past the last chunk that a two-tile workgroup's first tile reads
+    int early = 0;
+    for (int x = 0; x < 8; ++x) {
+        const int l = xcd_items(tiles, 1, L.npieces, x);
+        for (int w = 0; w < per_xcd; ++w) {
+            const int j = schedule_item(l, per_xcd, w, 0);
+            if (j < 0 || schedule_item(l, per_xcd, w, 1) < 0) continue;   // one-tile workgroup
+            int c = 0, jj = j;
+            for (; c < L.npieces; ++c) {
+                const int cnt = tiles[c] / 8 + (x < tiles[c] % 8 ? 1 : 0);
+                if (jj < cnt) break;
+                jj -= cnt;
+            }
+            if (c < L.npieces && L.wait[c] + 1 > early) early = L.wait[c] + 1;
+        }
+    }
+    fp.gatherers = g;
+    fp.early = early < L.gather_nchunks ? early : L.gather_nchunks;
+    fp.workgroups = 8 * per_xcd;
+    return fp;
+}
 
 int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[kMaxPieces + 1]) {
     for (int c = 0; c <= kMaxPieces; ++c) tiles[c] = 0;
