@@ -287,41 +287,44 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
     const size_t es = elem_size(P.dt);
-    COC_HIP(hipEventRecord(c->fork, main));
-    COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
     ChunksLaunch L = chunks_for(P, g0);
-    for (int i = 0; i < P.nchunks; ++i) L.signal[i] = i;
-    L.done = c->sync;
-    int32_t tiles[kMaxPieces + 1];
-    COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
     // Chunks whose tiles all fall before the matmul's last round of workgroups
     // reduce beside it (waiting on its counters, at most one workgroup per
     // CU).  The rest finish with the matmul; their rows (consecutive in every
     // plan) reduce in one full-grid launch after it on the caller's stream.
+    int32_t tiles[kMaxPieces + 1];
+    chunks_tiles(L, tiles);
     const int64_t groups = tiles[kMaxPieces] > 0 ? tiles[kMaxPieces] : 1;
     int64_t total = 0;
     for (int i = 0; i < P.nchunks; ++i) total += tiles[i];
     const int64_t last_round = ((total - 1) / groups) * groups;   // first tile index of the last round
     int early = 0;
     for (int64_t cum = 0; early < P.nchunks - 1 && cum + tiles[early] <= last_round; ++early) cum += tiles[early];
-    ReduceChunksLaunch R{};
-    R.r = r0;
-    R.nchunks = early;
-    R.done = c->sync;
-    R.own = P.rank;
-    R.narrow = g0.kind == GK_W8_F16;   // the int8 matmul leaves ~90 VGPRs per SIMD lane
-    double bytes = 0;
-    for (int i = 0; i < P.nchunks; ++i) {
-        const uint32_t t = c->done_sent[i] += (uint32_t)tiles[i];
-        if (i >= early) continue;
-        R.target[i] = t;
-        R.src_row0[i] = P.chunk[i].red_base;
-        R.dst_row0[i] = P.chunk[i].out_base;
-        R.rows[i] = P.chunk[i].red_rows;
-        bytes += double(r0.nsrc + 1) * double(R.rows[i]) * double(P.n) * double(es);
+    if (early > 0) {
+        COC_HIP(hipEventRecord(c->fork, main));
+        COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
+        for (int i = 0; i < early; ++i) L.signal[i] = i;   // only the chunks reduced beside the matmul
+        L.done = c->sync;
     }
-    if (early > 0)
+    int32_t launched[kMaxPieces + 1];
+    COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, launched); }));
+    if (early > 0) {
+        ReduceChunksLaunch R{};
+        R.r = r0;
+        R.nchunks = early;
+        R.done = c->sync;
+        R.own = P.rank;
+        R.narrow = g0.kind == GK_W8_F16;   // the int8 matmul leaves ~90 VGPRs per SIMD lane
+        double bytes = 0;
+        for (int i = 0; i < early; ++i) {
+            R.target[i] = c->done_sent[i] += (uint32_t)tiles[i];
+            R.src_row0[i] = P.chunk[i].red_base;
+            R.dst_row0[i] = P.chunk[i].out_base;
+            R.rows[i] = P.chunk[i].red_rows;
+            bytes += double(r0.nsrc + 1) * double(R.rows[i]) * double(P.n) * double(es);
+        }
         COC_TRY(launch(KC_REDUCE, bytes, c->side, [&] { return launch_reduce_chunks(R, c->side); }));
+    }
     {
         ReduceLaunch r = r0;
         r.src_row0 = P.chunk[early].red_base;
@@ -331,8 +334,10 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
         const double lb = double(r.nsrc + 1) * double(r.rows) * double(P.n) * double(es);
         COC_TRY(launch(KC_REDUCE, lb, main, [&] { return launch_reduce(r, main); }));
     }
-    COC_HIP(hipEventRecord(c->join, c->side));
-    COC_HIP(hipStreamWaitEvent(main, c->join, 0));
+    if (early > 0) {
+        COC_HIP(hipEventRecord(c->join, c->side));
+        COC_HIP(hipStreamWaitEvent(main, c->join, 0));
+    }
     return COC_OK;
 }
 
@@ -356,6 +361,7 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
     L.n = g0.n;
     L.k = g0.k;
     L.ready = c->sync + COC_MAX_SPLIT * kSyncWords;
+    L.order = 1;
     add_piece(&L, a0.src[P.rank], -own0, own0, shard, -1);
     int64_t grow0[COC_MAX_SPLIT], grows[COC_MAX_SPLIT];
     double bytes = 0;

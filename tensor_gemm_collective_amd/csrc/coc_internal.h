@@ -117,6 +117,10 @@ struct ChunksLaunch {
     uint32_t* done;
     uint32_t* ready;
     uint32_t ready_target[COC_MAX_SPLIT];
+    // 0: each workgroup walks whole rounds of the list in order, so chunks
+    // finish in order (compute first); 1: workgroups with two tiles of the
+    // last two rounds start on the first chunks (communicate first)
+    int32_t order;
     // All-gather rows that the launch's one-tile workgroups copy before their
     // tile (gather_nchunks > 0; see chunks_fused_gatherers): gathered row g of
     // chunk c's rows [gather_row0[c], + gather_rows[c]) comes from row
@@ -170,6 +174,9 @@ bool chunks_supported(const GemmLaunch& g);
 // tiles[i] receives the tile count of piece i (the adds its signal gets) and
 // tiles[kMaxPieces] the number of workgroups launched.
 int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[kMaxPieces + 1]);
+// Tiles per piece of L's launch, and in tiles[kMaxPieces] its workgroups
+// (what launch_gemm_chunks reports), without launching.
+void chunks_tiles(const ChunksLaunch& L, int32_t tiles[kMaxPieces + 1]);
 // The plan by which L's launch would run the gather itself (L.gather_nchunks
 // set); the caller sets each chunk's ready target from it.
 FusedGatherPlan chunks_fused_gather(const ChunksLaunch& L);

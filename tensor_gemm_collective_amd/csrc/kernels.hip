@@ -1112,6 +1112,7 @@ struct PersistParams {
     int32_t wait[kMaxPieces], signal[kMaxPieces];
     uint32_t ready_target[COC_MAX_SPLIT];
     int32_t npieces, per_xcd;
+    int32_t order;   // 0: whole rounds in list order; 1: two-tile workgroups first (schedule_item)
     uint32_t* done;
     uint32_t* ready;
     FusedGather fg;
@@ -1209,7 +1210,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P
     int waited = -1;
     bool ok = true;
     for (int s = 0;; ++s) {
-        const int j = schedule_item(l, P.per_xcd, w, s);
+        // order 0 finishes the list's chunks in order (a compute-first op
+        // hands each chunk to its reduce as early as possible)
+        const int j = P.order == 0 ? (w + s * P.per_xcd < l ? w + s * P.per_xcd : -1)
+                                   : schedule_item(l, P.per_xcd, w, s);
         if (j < 0) break;
         int c = 0, jj = j;
         for (; c < P.npieces; ++c) {
@@ -1820,6 +1824,7 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     P.g.group = L.group > 0 ? L.group : 1;
     P.g.tiles_n = (int32_t)((L.n + BN - 1) / BN);
     P.npieces = L.npieces;
+    P.order = L.order;
     bool signal = false;
     int per_cu_chk = 0;
     P.per_xcd = chunks_layout(L, tiles, &per_cu_chk);
@@ -1880,6 +1885,12 @@ hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* til
 }
 
 }  // namespace
+
+void chunks_tiles(const ChunksLaunch& L, int32_t tiles[kMaxPieces + 1]) {
+    for (int c = 0; c <= kMaxPieces; ++c) tiles[c] = 0;
+    int per_cu = 0;
+    tiles[kMaxPieces] = 8 * chunks_layout(L, tiles, &per_cu);
+}
 
 FusedGatherPlan chunks_fused_gather(const ChunksLaunch& L) {
     FusedGatherPlan fp{};
