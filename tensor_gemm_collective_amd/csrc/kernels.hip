@@ -21,6 +21,8 @@
 #include <type_traits>
 
 #include "coc_internal.h"
+#define COC_HD __host__ __device__
+#include "coc_schedule.h"
 
 // Build-time tuning knob (default: the measured best): the fewest workgroups
 // the chunk matmuls running side by side should have together before the
@@ -1118,52 +1120,6 @@ struct PersistParams {
     FusedGather fg;
 };
 
-// Items of XCD x's list (the pieces' tiles split over the 8 XCDs).
-// (A piece has tiles_m[c] * tiles_n tiles.)
-__host__ __device__ inline int xcd_items(const int32_t* tiles_m, int tiles_n, int npieces, int x) {
-    int l = 0;
-    for (int c = 0; c < npieces; ++c) {
-        const int t = tiles_m[c] * tiles_n;
-        l += t / 8 + (x < t % 8 ? 1 : 0);
-    }
-    return l;
-}
-
-// The s-th item of workgroup w among per_xcd on a list of l items, or -1.
-// Whole rounds first (w, w + per_xcd, ...); the last two rounds, with
-// l' items, have d = l' - per_xcd workgroups doing two items and the rest
-// one: the two-item workgroups take the first d items and then the next d,
-// the one-item workgroups the last ones.  List order is chunk order, so the
-// workgroups that must also finish a second tile start on the chunks that
-// are ready first, and those that start last have a whole tile of slack.
-__host__ __device__ inline int schedule_item(int l, int per_xcd, int w, int s) {
-    if (l <= per_xcd) return s == 0 && w < l ? w : -1;
-    const int rounds = (l + per_xcd - 1) / per_xcd;
-    if (s < rounds - 2) return s * per_xcd + w;
-    const int b = (rounds - 2) * per_xcd, d = l - b - per_xcd, t = s - (rounds - 2);
-    if (w < d) return t == 0 ? b + w : (t == 1 ? b + d + w : -1);
-    return t == 0 ? b + 2 * d + (w - d) : -1;
-}
-
-// One-item workgroups of the last two rounds over XCDs 0..x-1, and on XCD x
-// the first such workgroup (-1 if the list has no such last two rounds).
-__host__ __device__ inline int singles_before(const int32_t* tiles_m, int tiles_n, int npieces, int per_xcd, int x,
-                                              int* first) {
-    int n = 0;
-    for (int y = 0; y <= x; ++y) {
-        const int l = xcd_items(tiles_m, tiles_n, npieces, y);
-        int d = -1, singles = 0;
-        if (l > per_xcd) {
-            const int rounds = (l + per_xcd - 1) / per_xcd;
-            d = l - (rounds - 2) * per_xcd - per_xcd;
-            singles = per_xcd - d;
-        }
-        if (y == x) *first = d;
-        else n += singles;
-    }
-    return n;
-}
-
 // Share gi of ng of chunks [c0, c1), 16 vectors per thread in flight (the
 // matmul's registers are free before its first tile), stores written through
 // for the other XCDs' matmul workgroups; then 1 added to the chunk's ready
@@ -1212,16 +1168,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P
     for (int s = 0;; ++s) {
         // order 0 finishes the list's chunks in order (a compute-first op
         // hands each chunk to its reduce as early as possible)
-        const int j = P.order == 0 ? (w + s * P.per_xcd < l ? w + s * P.per_xcd : -1)
-                                   : schedule_item(l, P.per_xcd, w, s);
+        const int j = P.order == 0 ? inorder_item(l, P.per_xcd, w, s) : schedule_item(l, P.per_xcd, w, s);
         if (j < 0) break;
-        int c = 0, jj = j;
-        for (; c < P.npieces; ++c) {
-            const int T = P.tiles_m[c] * tn_all;
-            const int cnt = T / NX + (x < T % NX ? 1 : 0);
-            if (jj < cnt) break;
-            jj -= cnt;
-        }
+        int jj = 0;
+        const int c = piece_of_item(P.tiles_m, tn_all, P.npieces, x, j, &jj);
         if (c >= P.npieces) break;
         const int T = P.tiles_m[c] * tn_all;
         int tm, tn;
@@ -1903,22 +1853,7 @@ FusedGatherPlan chunks_fused_gather(const ChunksLaunch& L) {
     int first = -1;
     const int g = singles_before(tiles, 1, L.npieces, per_xcd, 8, &first);   // over XCDs 0..7
     if (g < 16) return fp;
-    // early: one past the last chunk that a two-tile workgroup's first tile reads
-    int early = 0;
-    for (int x = 0; x < 8; ++x) {
-        const int l = xcd_items(tiles, 1, L.npieces, x);
-        for (int w = 0; w < per_xcd; ++w) {
-            const int j = schedule_item(l, per_xcd, w, 0);
-            if (j < 0 || schedule_item(l, per_xcd, w, 1) < 0) continue;   // one-tile workgroup
-            int c = 0, jj = j;
-            for (; c < L.npieces; ++c) {
-                const int cnt = tiles[c] / 8 + (x < tiles[c] % 8 ? 1 : 0);
-                if (jj < cnt) break;
-                jj -= cnt;
-            }
-            if (c < L.npieces && L.wait[c] + 1 > early) early = L.wait[c] + 1;
-        }
-    }
+    const int early = early_chunks(tiles, L.wait, L.npieces, per_xcd);
     fp.gatherers = g;
     fp.early = early < L.gather_nchunks ? early : L.gather_nchunks;
     fp.workgroups = 8 * per_xcd;
