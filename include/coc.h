@@ -58,6 +58,14 @@
  * writes nothing, and coc_last_error() returns a description (per host
  * thread).  COC_ERR_HIP wraps a failing HIP runtime call and carries its
  * message.  No C++ exception crosses this interface.
+ *
+ * Hand-over waits.  The pipelined forms hand chunks between kernels through
+ * device counters; every wait is bounded (about 2 s), and a wait that gives
+ * up writes NaN into the tile or rows it guards instead of hanging.  Two
+ * environment variables, read at each call, exist to test that path:
+ * COC_SPIN_LIMIT=n (polls before giving up) and COC_TEST_UNREACHABLE_WAIT=1
+ * (the calls made meanwhile wait for counts that never arrive; the library's
+ * own counter bookkeeping stays exact, so later calls are unaffected).
  */
 #ifndef COC_H
 #define COC_H

@@ -20,6 +20,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <atomic>
+#include <cstdlib>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -47,6 +48,21 @@
 
 namespace coc {
 namespace {
+
+// Testing hooks (see coc.h): COC_SPIN_LIMIT=n makes every hand-over wait give
+// up after n polls instead of about 2 s; COC_TEST_UNREACHABLE_WAIT=1 puts the
+// targets of the waits of the calls made meanwhile out of reach (the counter
+// bookkeeping itself stays exact, so later calls are unaffected).  The
+// waiting tiles and rows then come out NaN and every kernel still ends.
+uint32_t spin_limit_override() {
+    const char* v = getenv("COC_SPIN_LIMIT");
+    const long n = v ? strtol(v, nullptr, 10) : 0;
+    return n > 0 && n < (1L << 30) ? (uint32_t)n : 0u;
+}
+uint32_t target_offset() {
+    const char* v = getenv("COC_TEST_UNREACHABLE_WAIT");
+    return v && v[0] == '1' ? (1u << 30) : 0u;
+}
 
 coc_status hip_fail(hipError_t e, const char* what) {
     return fail(COC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -316,8 +332,10 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
         R.own = P.rank;
         R.narrow = g0.kind == GK_W8_F16;   // the int8 matmul leaves ~90 VGPRs per SIMD lane
         double bytes = 0;
+        R.spin_limit = spin_limit_override();
+        const uint32_t off = target_offset();
         for (int i = 0; i < early; ++i) {
-            R.target[i] = c->done_sent[i] += (uint32_t)tiles[i];
+            R.target[i] = (c->done_sent[i] += (uint32_t)tiles[i]) + off;
             R.src_row0[i] = P.chunk[i].red_base;
             R.dst_row0[i] = P.chunk[i].out_base;
             R.rows[i] = P.chunk[i].red_rows;
@@ -384,10 +402,12 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
         L.gather_dst = a0.dst;
         L.gather_row_bytes = P.k * (int64_t)es;
         L.gather_shard_rows = shard;
+        L.spin_limit = spin_limit_override();
+        const uint32_t off = target_offset();
         for (int i = 0; i < P.nchunks; ++i) {
             L.gather_row0[i] = grow0[i];
             L.gather_rows[i] = grows[i];
-            L.ready_target[i] = c->ready_sent[i] += (uint32_t)(i < fp.early ? fp.workgroups : fp.gatherers);
+            L.ready_target[i] = (c->ready_sent[i] += (uint32_t)(i < fp.early ? fp.workgroups : fp.gatherers)) + off;
         }
         return launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); });
     }
@@ -399,7 +419,8 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
         return launch_gather_chunks(a0, P.nchunks, grow0, grows, c->sync + COC_MAX_SPLIT * kSyncWords, c->side,
                                     &per_chunk);
     }));
-    for (int i = 0; i < P.nchunks; ++i) L.ready_target[i] = c->ready_sent[i] += (uint32_t)per_chunk;
+    L.spin_limit = spin_limit_override();
+    for (int i = 0; i < P.nchunks; ++i) L.ready_target[i] = (c->ready_sent[i] += (uint32_t)per_chunk) + target_offset();
     COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
     COC_HIP(hipEventRecord(c->join, c->side));
     COC_HIP(hipStreamWaitEvent(main, c->join, 0));

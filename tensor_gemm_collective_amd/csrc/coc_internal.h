@@ -121,6 +121,7 @@ struct ChunksLaunch {
     // finish in order (compute first); 1: workgroups with two tiles of the
     // last two rounds start on the first chunks (communicate first)
     int32_t order;
+    uint32_t spin_limit;     // polls before a wait gives up (0: the default, about 2 s)
     // All-gather rows that the launch's one-tile workgroups copy before their
     // tile (gather_nchunks > 0; see chunks_fused_gatherers): gathered row g of
     // chunk c's rows [gather_row0[c], + gather_rows[c]) comes from row
@@ -152,6 +153,7 @@ struct ReduceChunksLaunch {
     uint32_t target[COC_MAX_SPLIT];
     int32_t own;             // index of the source the matmul is writing meanwhile
     bool narrow;             // one vector per thread: fits beside a matmul using more registers
+    uint32_t spin_limit;     // polls before a wait gives up (0: the default, about 2 s)
 };
 
 // Launchers (kernels.hip).  Return a hipError_t value (0 = success).  The

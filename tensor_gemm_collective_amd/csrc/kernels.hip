@@ -156,8 +156,8 @@ constexpr int kSyncScope = COC_SYNC_SYSTEM ? __HIP_MEMORY_SCOPE_SYSTEM : __HIP_M
 // polling one counter at a fixed short interval load its HBM channel enough to
 // slow every other stream through it.
 // Waits until the sum of `lines` counters (kSyncWords apart) reaches target.
-__device__ __forceinline__ bool spin_until(const uint32_t* p, int lines, uint32_t target) {
-    for (uint32_t i = 0; i < kSpinLimit; ++i) {
+__device__ __forceinline__ bool spin_until(const uint32_t* p, int lines, uint32_t target, uint32_t limit) {
+    for (uint32_t i = 0; i < limit; ++i) {
         uint32_t v = 0;
         for (int l = 0; l < lines; ++l) v += __hip_atomic_load(p + l * kSyncWords, __ATOMIC_RELAXED, kSyncScope);
         if ((int32_t)(v - target) >= 0) return true;
@@ -172,9 +172,9 @@ __device__ __forceinline__ bool spin_until(const uint32_t* p, int lines, uint32_
 // every wave through LDS.  The barrier orders every later load after the
 // poll.  Two calls must be separated by a workgroup barrier (the flag is
 // reused).
-__device__ __forceinline__ bool wg_wait(const uint32_t* p, int lines, uint32_t target) {
+__device__ __forceinline__ bool wg_wait(const uint32_t* p, int lines, uint32_t target, uint32_t limit) {
     __shared__ int ok;
-    if (threadIdx.x == 0) ok = spin_until(p, lines, target) ? 1 : 0;
+    if (threadIdx.x == 0) ok = spin_until(p, lines, target, limit) ? 1 : 0;
     __syncthreads();
     return ok != 0;
 }
@@ -1115,6 +1115,7 @@ struct PersistParams {
     uint32_t ready_target[COC_MAX_SPLIT];
     int32_t npieces, per_xcd;
     int32_t order;   // 0: whole rounds in list order; 1: two-tile workgroups first (schedule_item)
+    uint32_t spin_limit;   // polls before a wait gives up (the tile is then NaN)
     uint32_t* done;
     uint32_t* ready;
     FusedGather fg;
@@ -1178,7 +1179,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P
         grouped_coords(x * (T / NX) + (x < T % NX ? x : T % NX) + jj, P.tiles_m[c], tn_all, &tm, &tn);
         const int wi = P.wait[c];
         if (P.ready != nullptr && wi >= 0 && wi != waited) {
-            ok = wg_wait(P.ready + wi * kReadyLines * kSyncWords, kReadyLines, P.ready_target[wi]);
+            ok = wg_wait(P.ready + wi * kReadyLines * kSyncWords, kReadyLines, P.ready_target[wi], P.spin_limit);
             waited = wi;
         }
         // the previous tile's stores are done and every wave is off the LDS ring
@@ -1276,6 +1277,7 @@ struct ReduceChunks {
     uint32_t target[COC_MAX_SPLIT];
     const uint32_t* done;
     int32_t nchunks, own;
+    uint32_t spin_limit;   // polls before a wait gives up (rows then NaN)
 };
 
 // Two sources are loaded at a time and added in rank order before the next
@@ -1398,7 +1400,7 @@ __global__ __launch_bounds__(256) void reduce_chunks_wait(ReduceParams p, Reduce
     const int stride = gridDim.x * 256;
     for (int c = 0; c < C.nchunks; ++c) {
         if (c > 0) __syncthreads();   // wg_wait's flag is reused
-        const bool ok = wg_wait(C.done + c * kSyncWords, 1, C.target[c]);
+        const bool ok = wg_wait(C.done + c * kSyncWords, 1, C.target[c], C.spin_limit);
         const int total = C.total[c];
         for (int v = blockIdx.x * 256 + threadIdx.x; v < total; v += U * stride) {
             const int v2 = v + stride;
@@ -1644,6 +1646,7 @@ int launch_reduce_chunks(const ReduceChunksLaunch& L, void* stream) {
     C.done = L.done;
     C.nchunks = L.nchunks;
     C.own = L.own;
+    C.spin_limit = L.spin_limit > 0 ? L.spin_limit : kSpinLimit;
     const int grid = grid_for(most) < 256 ? grid_for(most) : 256;   // at most one per CU
     hipStream_t s = (hipStream_t)stream;
     auto go = [&](auto DTC) {
@@ -1775,6 +1778,7 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     P.g.tiles_n = (int32_t)((L.n + BN - 1) / BN);
     P.npieces = L.npieces;
     P.order = L.order;
+    P.spin_limit = L.spin_limit > 0 ? L.spin_limit : kSpinLimit;
     bool signal = false;
     int per_cu_chk = 0;
     P.per_xcd = chunks_layout(L, tiles, &per_cu_chk);

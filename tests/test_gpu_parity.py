@@ -382,6 +382,52 @@ def test_allgather_fused_copy_handover(rank):
         assert_bits_equal(y, refs[it % 2], f"all-gather matmul, call {it} split {split}")
 
 
+def test_bounded_wait_gives_up_to_nan(monkeypatch):
+    """A hand-over wait whose count never arrives gives up after its poll limit
+    (forced from the host: a tiny limit and targets out of reach) and writes
+    NaN where it would have read unready data; every kernel ends, the call
+    succeeds, what needed no wait is exact, and the next normal call is exact
+    again (the counter bookkeeping stayed in step)."""
+    bf = torch.bfloat16
+    g0 = torch.Generator(device="cuda").manual_seed(5)
+    # all-gather matmul whose launch copies the rows itself (rank 0: own rows 0..511)
+    world, shard, k, n, rank = 8, 512, 256, 7168, 0
+    shards = [torch.randn(shard, k, device="cuda", generator=g0).to(bf) for _ in range(world)]
+    w = (torch.randn(k, n, device="cuda", generator=g0) * 0.02).to(bf)
+    peers = [None if r == rank else shards[r] for r in range(world)]
+    ref = tgc.allgather_matmul(shards[rank], peers, w, rank, split=1)
+    # reduce-scatter whose first two chunks reduce beside the matmul (512 tiles, two rounds)
+    m2, n2, k2, rank2 = 4096, 8192, 256, 3
+    x2 = torch.randn(m2, k2, device="cuda", generator=g0).to(bf)
+    w2 = (torch.randn(k2, n2, device="cuda", generator=g0) * 0.02).to(bf)
+    peers2 = [None if r == rank2 else torch.randn(m2, n2, device="cuda", generator=g0).to(bf) for r in range(world)]
+    ref2, _ = tgc.matmul_reduce_scatter(x2, w2, peers2, rank2, split=1, deterministic=1)
+    torch.cuda.synchronize()
+
+    log("hand-over waits forced to give up (COC_SPIN_LIMIT=64, unreachable targets)")
+    monkeypatch.setenv("COC_SPIN_LIMIT", "64")
+    monkeypatch.setenv("COC_TEST_UNREACHABLE_WAIT", "1")
+    y, g = tgc.allgather_matmul(shards[rank], peers, w, rank, split=4, v2=True)
+    y2, p2 = tgc.matmul_reduce_scatter(x2, w2, peers2, rank2, split=4, deterministic=1)
+    torch.cuda.synchronize()
+    assert_bits_equal(g, torch.cat(shards), "the copy itself still completes")
+    assert_bits_equal(y[:shard], ref[:shard], "own-shard rows (no wait)")
+    assert torch.isnan(y[shard:].float()).all(), "rows whose wait gave up must be NaN"
+    q = m2 // world // 4   # rows of each chunk in this rank's slice
+    assert torch.isnan(y2[:2 * q].float()).all(), "chunks reduced beside the matmul must be NaN"
+    assert_bits_equal(y2[2 * q:], ref2[2 * q:], "chunks reduced after the matmul (no wait)")
+    assert torch.isfinite(p2.float()).all()
+
+    monkeypatch.delenv("COC_SPIN_LIMIT")
+    monkeypatch.delenv("COC_TEST_UNREACHABLE_WAIT")
+    log("the next normal calls")
+    y, g = tgc.allgather_matmul(shards[rank], peers, w, rank, split=4, v2=True)
+    y2, _ = tgc.matmul_reduce_scatter(x2, w2, peers2, rank2, split=4, deterministic=1)
+    torch.cuda.synchronize()
+    assert_bits_equal(y, ref, "all-gather matmul after the forced time-out")
+    assert_bits_equal(y2, ref2, "reduce-scatter after the forced time-out")
+
+
 @pytest.mark.parametrize("split", [2, 4, 8])
 def test_pipeline_handover_reuses_buffers_without_stale_rows(split):
     """Two input sets alternate through the same output / gathered buffers, so
