@@ -354,28 +354,29 @@ def test_stream_order_without_host_sync():
 
 
 # ------------------------------------------------------------------ one-launch pipeline hand-over
-@pytest.mark.parametrize("rank", [0, 5])
-def test_allgather_fused_copy_handover(rank):
+@pytest.mark.parametrize("world,rank,dt", [(8, 0, "bf16"), (8, 5, "bf16"), (4, 3, "bf16"), (8, 7, "f16")])
+def test_allgather_fused_copy_handover(world, rank, dt):
     """The all-gather shape where the matmul launch copies the rows itself
     (448 tiles of 256 x 256 on 256 workgroups: some own a single tile).  Two
     input sets alternate through the same buffers over every split, so rows
     read before their copy landed, or counters left out of step by an
     earlier call, would show: each call must match split 1 bit for bit."""
-    world, shard, k, n = 8, 512, 256, 7168
-    m = world * shard
+    k, n = 256, 7168
+    m = 4096
+    shard = m // world
     sets = []
     for tag in (21, 22):
-        shards = [synth.normal(WID_TEST + tag, synth.T_PEER, r, (shard, k), 1.0, "bf16") for r in range(world)]
+        shards = [synth.normal(WID_TEST + tag, synth.T_PEER, r, (shard, k), 1.0, dt) for r in range(world)]
         sets.append([dev(s) for s in shards])
-    w = dev(synth.normal(WID_TEST + 21, synth.T_W, 0, (k, n), 0.02, "bf16"))
+    w = dev(synth.normal(WID_TEST + 21, synth.T_W, 0, (k, n), 0.02, dt))
     peers_of = lambda sh: [None if r == rank else sh[r] for r in range(world)]
     refs = [tgc.allgather_matmul(sh[rank], peers_of(sh), w, rank, split=1) for sh in sets]
     torch.cuda.synchronize()
-    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-    g = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((m, n), dtype=TORCH_DT[dt], device="cuda")
+    g = torch.empty((m, k), dtype=TORCH_DT[dt], device="cuda")
     for it, split in enumerate((4, 8, 2, 4, 8, 2)):
         sh = sets[it % 2]
-        log(f"fused all-gather copy, rank={rank} call {it} split={split}")
+        log(f"fused all-gather copy, world={world} rank={rank} {dt} call {it} split={split}")
         tgc.allgather_matmul(sh[rank], peers_of(sh), w, rank, y=y, gathered_out=g, v2=True, split=split)
         torch.cuda.synchronize()
         assert_bits_equal(g, torch.cat(sh), f"gathered rows, call {it}")
