@@ -202,6 +202,30 @@ def run_configs(torch, tgc, synth, dev, iters=10):
         sc = synth.fp16_scales(wl.wid, 0, shape).to(dev)
         ms = timeit(lambda: tgc.matmul_all_reduce_w8a16(x, q, sc, mode, pr, 0, group_size=wl.group, split=4))
         emit(f"w8a16_ar {mode} split4", 2.0 * wl.m * wl.n * wl.k, ms, ref)
+    del x, q, pr, wf
+
+    # backward of the LLaMA2-70B pair: dX of the down projection (AG(dY) @ W^T,
+    # the 3584 x 8192 forward weight read transposed), dX of the gate/up layer
+    # (dY @ W^T reduce-scattered, W 8192 x 7168 read transposed), and dW of the
+    # gate/up layer from the gathered G
+    wl = W["llama70b_ag"]
+    shard = wl.m // wl.world
+    dys = [synth.normal(wl.wid, synth.T_PEER, 9 + r, (shard, wl.k), 1.0, "bf16").to(dev) for r in range(wl.world)]
+    w_down = synth.normal(wl.wid, synth.T_W, 9, (3584, wl.k), 0.02, "bf16").to(dev)
+    ms = timeit(lambda: tgc.allgather_matmul(dys[0], dys, w_down, 0, split=4, trans_w=True))
+    emit("llama70b backward dX down-proj: AG(dY 8x512x8192) @ W^T (8192 -> 3584) split4",
+         2.0 * wl.m * 3584 * wl.k, ms, timeit(lambda: torch.matmul(torch.cat(dys), w_down.t())))
+    w_up = synth.normal(wl.wid, synth.T_W, 0, (wl.k, wl.n), 0.02, "bf16").to(dev)
+    dy = synth.normal(wl.wid, synth.T_X, 9, (wl.m, wl.n), 1.0, "bf16").to(dev)
+    pr = [None] + [synth.normal(wl.wid, synth.T_PEER, 20 + r, (wl.m, wl.k), 1.0, "bf16").to(dev)
+                   for r in range(1, wl.world)]
+    ms = timeit(lambda: tgc.matmul_reduce_scatter(dy, w_up, pr, 0, split=4, trans_w=True))
+    emit("llama70b backward dX gate/up: dY 4096x7168 @ W^T (7168 -> 8192) reduce-scattered split4",
+         2.0 * wl.m * wl.k * wl.n, ms, timeit(lambda: torch.matmul(dy, w_up.t())))
+    g = torch.cat(dys)
+    ms = timeit(lambda: tgc.weight_grad(g, dy))
+    emit("llama70b backward dW gate/up: G^T (8192x4096) @ dY (4096x7168)", 2.0 * wl.m * wl.k * wl.n, ms,
+         timeit(lambda: torch.matmul(g.t(), dy)))
 
 
 def main():

@@ -41,6 +41,13 @@
  *     (serial, no overlap), 2, 4 or 8 (CoC guide, "Usage": the split count
  *     options; the m dimension must divide by it, CoC guide "Approach" and
  *     Overlap blog, third-layer caveats).
+ *   - `trans_w` != 0 (matmul all-reduce / reduce-scatter / all-gather):
+ *     `w` holds the weights transposed, n rows of k elements, so the
+ *     backward pass of a layer (CoC guide, "Approach": forward / backward
+ *     operator pairs) multiplies by the forward k x n weight read as its
+ *     transpose without copying it: dX = dY @ W^T.  bf16 / fp16 and
+ *     k % 32 == 0; the result bits equal those of trans_w = 0 with the
+ *     transpose stored.
  *   - `deterministic` != 0 selects the deterministic variants (CoC guide,
  *     "Approach", fused-operator list): partial sums are added in ascending
  *     rank order 0..world-1 in binary32 with this rank's own partial taken
@@ -130,7 +137,7 @@ typedef enum coc_op {
 coc_status coc_matmul_all_reduce(const void* x, const void* w, void* y, void* partial_out,
                                  const void* const* peer_bufs, int32_t world, int32_t rank,
                                  int64_t m, int64_t n, int64_t k, coc_dtype dt,
-                                 int32_t split, int32_t deterministic,
+                                 int32_t split, int32_t deterministic, int32_t trans_w,
                                  void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -151,7 +158,7 @@ coc_status coc_matmul_all_reduce(const void* x, const void* w, void* y, void* pa
 coc_status coc_matmul_reduce_scatter(const void* x, const void* w, void* y, void* partial_out,
                                      const void* const* peer_bufs, int32_t world, int32_t rank,
                                      int64_t m, int64_t n, int64_t k, coc_dtype dt,
-                                     int32_t split, int32_t deterministic,
+                                     int32_t split, int32_t deterministic, int32_t trans_w,
                                      void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -175,8 +182,24 @@ coc_status coc_matmul_reduce_scatter(const void* x, const void* w, void* y, void
 coc_status coc_allgather_matmul(const void* x_shard, const void* const* peer_bufs, const void* w,
                                 void* y, void* gathered_out, int32_t world, int32_t rank,
                                 int64_t m, int64_t n, int64_t k, coc_dtype dt,
-                                int32_t split, int32_t deterministic,
+                                int32_t split, int32_t deterministic, int32_t trans_w,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weight gradient of the sequence-parallel pair (CoC guide, "Approach": the
+ * fused operators come in forward / backward pairs, and V2 hands back the
+ * all-gathered G so that the backward pass can reuse it):
+ *
+ *   dw = round_dt(G^T @ dY)        (k x n)
+ *
+ * g: m x k (e.g. the gathered_out of ALL_GATHER_MATMUL_V2), dy: m x n,
+ * dw: k x n, all bf16 or fp16; accumulation in binary32 over m in
+ * increasing order.  Requires m > 0, m % 32 == 0, n and k multiples of 8,
+ * 16-byte aligned pointers, dw not overlapping g or dy.  A plain local
+ * matmul: no collective.
+ */
+coc_status coc_weight_grad(const void* g, const void* dy, void* dw, int64_t m, int64_t n, int64_t k,
+                           coc_dtype dt, void* stream);
 
 /*
  * w8A16 pseudo-quantised MATMUL_ALL_REDUCE (CoC guide, "Approach", last item

@@ -17,6 +17,7 @@ from .coc import (
     matmul_reduce_scatter,
     allgather,
     allgather_matmul,
+    weight_grad,
     dequant_weight,
     matmul_all_reduce_w8a16,
     reduce_fixed_order,
@@ -26,6 +27,6 @@ from .coc import (
 __all__ = [
     "round_to", "encode", "decode", "round_f32", "round_dtype", "decode_dtype",
     "matmul", "matmul_all_reduce", "matmul_reduce_scatter", "allgather",
-    "allgather_matmul", "dequant_weight", "matmul_all_reduce_w8a16",
+    "allgather_matmul", "weight_grad", "dequant_weight", "matmul_all_reduce_w8a16",
     "reduce_fixed_order", "normwise_rel_error",
 ]

@@ -107,6 +107,18 @@ def allgather_matmul(shards, w):
     return matmul(g, w), g
 
 
+def weight_grad(g, dy) -> np.ndarray:
+    """Weight gradient of the sequence-parallel pair (CoC guide, "Approach":
+    the fused operators come in forward / backward pairs, and V2 hands back the
+    all-gathered G so the backward pass can reuse it): dW = G^T @ dY in
+    float64, G m x k, dY m x n, dW k x n."""
+    g = np.asarray(g, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    if g.ndim != 2 or dy.ndim != 2 or g.shape[0] != dy.shape[0]:
+        raise ValueError(f"shape mismatch {g.shape} {dy.shape}")
+    return g.T @ dy
+
+
 def dequant_weight(q, scales, mode: str, group: int = 0) -> np.ndarray:
     """Weight-only int8 dequantisation for w8A16 (CoC guide, last item of the
     fused-operator list: per tensor, per channel, per group).

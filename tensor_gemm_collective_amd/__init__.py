@@ -15,6 +15,7 @@ from .coc import (  # noqa: F401
     matmul_reduce_scatter,
     allgather_matmul,
     matmul_all_reduce_w8a16,
+    weight_grad,
     workspace_bytes,
     plan,
     profile_enable,

@@ -33,7 +33,7 @@ KCLASS = ("gemm", "reduce", "gather")
 # exported symbols, as declared in include/coc.h
 EXPORTS = (
     "coc_matmul_all_reduce", "coc_matmul_reduce_scatter", "coc_allgather_matmul",
-    "coc_matmul_all_reduce_w8a16", "coc_workspace_bytes", "coc_status_string",
+    "coc_matmul_all_reduce_w8a16", "coc_weight_grad", "coc_workspace_bytes", "coc_status_string",
     "coc_last_error", "coc_plan", "coc_profile_enable", "coc_profile_read", "coc_profile_records",
 )
 
@@ -68,15 +68,16 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
     L = ctypes.CDLL(LIB_PATH)
-    common = [_i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _sz, _vp]
+    common = [_i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
     L.coc_matmul_all_reduce.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(_vp)] + common
     L.coc_matmul_reduce_scatter.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(_vp)] + common
     L.coc_allgather_matmul.argtypes = [_vp, ctypes.POINTER(_vp), _vp, _vp, _vp] + common
     L.coc_matmul_all_reduce_w8a16.argtypes = [
         _vp, _vp, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(_vp), _i32, _i32, _i64, _i64, _i64,
         _i32, _i32, _vp, _sz, _vp]
+    L.coc_weight_grad.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]
     for f in ("coc_matmul_all_reduce", "coc_matmul_reduce_scatter", "coc_allgather_matmul",
-              "coc_matmul_all_reduce_w8a16"):
+              "coc_matmul_all_reduce_w8a16", "coc_weight_grad"):
         getattr(L, f).restype = _i32
     L.coc_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64, _i32, _i32, _i32]
     L.coc_workspace_bytes.restype = _sz
@@ -140,43 +141,53 @@ def _empty(shape, like):
 
 
 # ------------------------------------------------------------------ ops
+def _wdims(w, trans_w):
+    """(k, n) of a weight given k x n, or n x k when trans_w."""
+    return (w.shape[1], w.shape[0]) if trans_w else (w.shape[0], w.shape[1])
+
+
 def matmul_all_reduce(x, w, peers, rank, *, y=None, partial_out=None, split=4, deterministic=False,
-                      stream=None):
-    """MATMUL_ALL_REDUCE: returns (y, partial_out).  peers[r] (r != rank) are m x n partials."""
+                      trans_w=False, stream=None):
+    """MATMUL_ALL_REDUCE: returns (y, partial_out).  peers[r] (r != rank) are m x n partials.
+    trans_w: w is n x k (the product uses its transpose)."""
     m, k = x.shape
-    n = w.shape[1]
+    n = _wdims(w, trans_w)[1]
     y = _empty((m, n), x) if y is None else y
     partial_out = _empty((m, n), x) if partial_out is None else partial_out
     _check(lib().coc_matmul_all_reduce(
         _ptr(x), _ptr(w), _ptr(y), _ptr(partial_out), _peer_array(peers, rank), len(peers), rank,
-        m, n, k, _dtype_code(x), split, int(bool(deterministic)), None, 0, _stream(stream, x.device)))
+        m, n, k, _dtype_code(x), split, int(bool(deterministic)), int(bool(trans_w)), None, 0,
+        _stream(stream, x.device)))
     return y, partial_out
 
 
 def matmul_reduce_scatter(x, w, peers, rank, *, y=None, partial_out=None, split=4,
-                          deterministic=False, stream=None):
-    """MATMUL_REDUCE_SCATTER: returns (y, partial_out); y is (m/world) x n."""
+                          deterministic=False, trans_w=False, stream=None):
+    """MATMUL_REDUCE_SCATTER: returns (y, partial_out); y is (m/world) x n.
+    trans_w: w is n x k (the product uses its transpose)."""
     m, k = x.shape
-    n = w.shape[1]
+    n = _wdims(w, trans_w)[1]
     world = len(peers)
     y = _empty((m // world, n), x) if y is None else y
     partial_out = _empty((m, n), x) if partial_out is None else partial_out
     _check(lib().coc_matmul_reduce_scatter(
         _ptr(x), _ptr(w), _ptr(y), _ptr(partial_out), _peer_array(peers, rank), world, rank,
-        m, n, k, _dtype_code(x), split, int(bool(deterministic)), None, 0, _stream(stream, x.device)))
+        m, n, k, _dtype_code(x), split, int(bool(deterministic)), int(bool(trans_w)), None, 0,
+        _stream(stream, x.device)))
     return y, partial_out
 
 
 def allgather_matmul(x_shard, peers, w, rank, *, y=None, gathered_out=None, v2=False, ws=None,
-                     split=4, deterministic=False, stream=None):
+                     split=4, deterministic=False, trans_w=False, stream=None):
     """ALL_GATHER_MATMUL (v2=False) or _V2 (v2=True, also returns the gathered matrix).
 
-    Returns y, or (y, gathered) for V2.  peers[r] (r != rank) are (m/world) x k shards."""
+    Returns y, or (y, gathered) for V2.  peers[r] (r != rank) are (m/world) x k shards.
+    trans_w: w is n x k (the product uses its transpose)."""
     import torch
     world = len(peers)
     shard, k = x_shard.shape
     m = shard * world
-    n = w.shape[1]
+    n = _wdims(w, trans_w)[1]
     y = _empty((m, n), x_shard) if y is None else y
     if v2 and gathered_out is None:
         gathered_out = _empty((m, k), x_shard)
@@ -188,9 +199,19 @@ def allgather_matmul(x_shard, peers, w, rank, *, y=None, gathered_out=None, v2=F
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib().coc_allgather_matmul(
         _ptr(x_shard), _peer_array(peers, rank), _ptr(w), _ptr(y), _ptr(gathered_out) if v2 else None,
-        world, rank, m, n, k, _dtype_code(x_shard), split, int(bool(deterministic)),
+        world, rank, m, n, k, _dtype_code(x_shard), split, int(bool(deterministic)), int(bool(trans_w)),
         _ptr(ws) if not v2 else None, ws_bytes, _stream(stream, x_shard.device)))
     return (y, gathered_out) if v2 else y
+
+
+def weight_grad(g, dy, *, dw=None, stream=None):
+    """dW = G^T @ dY (k x n) for G m x k (e.g. V2's gathered matrix) and dY m x n."""
+    m, k = g.shape
+    n = dy.shape[1]
+    dw = _empty((k, n), g) if dw is None else dw
+    _check(lib().coc_weight_grad(_ptr(g), _ptr(dy), _ptr(dw), m, n, k, _dtype_code(g),
+                                 _stream(stream, g.device)))
+    return dw
 
 
 def matmul_all_reduce_w8a16(x, w_q, scales, mode, peers, rank, *, group_size=128, y=None,

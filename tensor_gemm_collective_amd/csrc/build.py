@@ -59,7 +59,8 @@ def build(verbose: bool = False, defines=(), lib_path: str = LIB_PATH, build_dir
         jobs.append([cc, *COMMON, *DEVICE, *dflags, "-x", "hip", "-c", os.path.join(HERE, s), "-o", obj])
     for s in HOST_SOURCES:
         obj = os.path.join(build_dir, s + ".o")
-        jobs.append([cc, *COMMON, *dflags, "-c", os.path.join(HERE, s), "-o", obj])
+        # host code only: no device pass (it holds no kernels)
+        jobs.append([cc, *COMMON, "--offload-host-only", *dflags, "-c", os.path.join(HERE, s), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     objs = [j[-1] for j in jobs]

@@ -248,6 +248,7 @@ ChunksLaunch chunks_for(const Plan& P, const GemmLaunch& g0) {
     L.scales = g0.scales;
     L.qmode = g0.qmode;
     L.group = g0.group;
+    L.trans_b = g0.trans_b;
     L.npieces = P.nchunks;
     for (int i = 0; i < P.nchunks; ++i) {
         L.a[i] = g0.a;
@@ -380,6 +381,7 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
     L.k = g0.k;
     L.ready = c->sync + COC_MAX_SPLIT * kSyncWords;
     L.order = 1;
+    L.trans_b = g0.trans_b;
     add_piece(&L, a0.src[P.rank], -own0, own0, shard, -1);
     int64_t grow0[COC_MAX_SPLIT], grows[COC_MAX_SPLIT];
     double bytes = 0;
@@ -511,14 +513,25 @@ GemmKind kind_of(coc_dtype dt) {
 }
 
 // Shared body of the all-reduce / reduce-scatter / w8a16 entry points.
+// Weights given transposed (w holds n rows of k elements, the forward
+// layer's k x n weight read as its transpose): bf16 / fp16 and k a multiple
+// of 32 (the matmul then always runs through the ring kernel).
+coc_status check_trans_w(int32_t trans_w, coc_dtype dt, int64_t k) {
+    if (!trans_w) return COC_OK;
+    if (dt != COC_BF16 && dt != COC_F16) return fail(COC_ERR_DTYPE, "transposed weights need bf16 or fp16");
+    if (k % 32 != 0) return fail(COC_ERR_SHAPE, "transposed weights need k %% 32 == 0 (k=%lld)", (long long)k);
+    return COC_OK;
+}
+
 coc_status compute_first_op(coc_op op, const void* x, const void* w, const void* scales,
                             int32_t qmode, int32_t group, void* y, void* partial,
                             const void* const* peers, int32_t world, int32_t rank, int64_t m,
                             int64_t n, int64_t k, coc_dtype dt, int32_t split, int32_t det,
-                            void* stream) {
+                            int32_t trans_w, void* stream) {
     clear_error();
     Plan P;
     COC_TRY(make_plan(op, m, n, k, dt, world, rank, split, det, &P));
+    COC_TRY(check_trans_w(trans_w, P.dt, k));
     const bool w8 = op == COC_OP_MATMUL_ALL_REDUCE_W8A16;
     const int64_t es = (int64_t)elem_size(P.dt);
     const int64_t y_rows = op == COC_OP_MATMUL_REDUCE_SCATTER ? m / world : m;
@@ -560,6 +573,7 @@ coc_status compute_first_op(coc_op op, const void* x, const void* w, const void*
     g0.group = qmode == COC_PER_GROUP ? group : 0;
     g0.n = n;
     g0.k = k;
+    g0.trans_b = trans_w;
 
     ReduceLaunch r0{};
     r0.dt = P.dt;
@@ -580,22 +594,23 @@ extern "C" {
 coc_status coc_matmul_all_reduce(const void* x, const void* w, void* y, void* partial_out,
                                  const void* const* peer_bufs, int32_t world, int32_t rank,
                                  int64_t m, int64_t n, int64_t k, coc_dtype dt, int32_t split,
-                                 int32_t deterministic, void* ws, size_t ws_bytes, void* stream) {
+                                 int32_t deterministic, int32_t trans_w, void* ws, size_t ws_bytes,
+                                 void* stream) {
     (void)ws;
     (void)ws_bytes;
     return compute_first_op(COC_OP_MATMUL_ALL_REDUCE, x, w, nullptr, 0, 0, y, partial_out, peer_bufs,
-                            world, rank, m, n, k, dt, split, deterministic, stream);
+                            world, rank, m, n, k, dt, split, deterministic, trans_w, stream);
 }
 
 coc_status coc_matmul_reduce_scatter(const void* x, const void* w, void* y, void* partial_out,
                                      const void* const* peer_bufs, int32_t world, int32_t rank,
                                      int64_t m, int64_t n, int64_t k, coc_dtype dt, int32_t split,
-                                     int32_t deterministic, void* ws, size_t ws_bytes,
-                                     void* stream) {
+                                     int32_t deterministic, int32_t trans_w, void* ws,
+                                     size_t ws_bytes, void* stream) {
     (void)ws;
     (void)ws_bytes;
     return compute_first_op(COC_OP_MATMUL_REDUCE_SCATTER, x, w, nullptr, 0, 0, y, partial_out,
-                            peer_bufs, world, rank, m, n, k, dt, split, deterministic, stream);
+                            peer_bufs, world, rank, m, n, k, dt, split, deterministic, trans_w, stream);
 }
 
 coc_status coc_matmul_all_reduce_w8a16(const void* x_f16, const int8_t* w_q, const void* scales_f16,
@@ -608,17 +623,19 @@ coc_status coc_matmul_all_reduce_w8a16(const void* x_f16, const int8_t* w_q, con
     (void)ws_bytes;
     return compute_first_op(COC_OP_MATMUL_ALL_REDUCE_W8A16, x_f16, w_q, scales_f16, (int32_t)mode,
                             group_size, y_f16, partial_out, peer_bufs, world, rank, m, n, k, COC_F16,
-                            split, deterministic, stream);
+                            split, deterministic, 0, stream);
 }
 
 coc_status coc_allgather_matmul(const void* x_shard, const void* const* peer_bufs, const void* w,
                                 void* y, void* gathered_out, int32_t world, int32_t rank, int64_t m,
                                 int64_t n, int64_t k, coc_dtype dt, int32_t split,
-                                int32_t deterministic, void* ws, size_t ws_bytes, void* stream) {
+                                int32_t deterministic, int32_t trans_w, void* ws, size_t ws_bytes,
+                                void* stream) {
     clear_error();
     const coc_op op = gathered_out ? COC_OP_ALLGATHER_MATMUL_V2 : COC_OP_ALLGATHER_MATMUL;
     Plan P;
     COC_TRY(make_plan(op, m, n, k, dt, world, rank, split, deterministic, &P));
+    COC_TRY(check_trans_w(trans_w, P.dt, k));
     const int64_t es = (int64_t)elem_size(P.dt);
     const int64_t shard = m / world;
     if (m == 0 || (n == 0 && !gathered_out) || (n == 0 && k == 0)) return COC_OK;
@@ -659,7 +676,52 @@ coc_status coc_allgather_matmul(const void* x_shard, const void* const* peer_buf
     g0.c = y;
     g0.n = n;
     g0.k = k;
+    g0.trans_b = trans_w;
     return run_comm_first(P, g0, a0, (hipStream_t)stream);
+}
+
+coc_status coc_weight_grad(const void* g, const void* dy, void* dw, int64_t m, int64_t n, int64_t k,
+                           coc_dtype dt, void* stream) {
+    clear_error();
+    if (dt != COC_BF16 && dt != COC_F16) return fail(COC_ERR_DTYPE, "weight gradient: bf16 or fp16 only");
+    if (m < 0 || n < 0 || k < 0) return fail(COC_ERR_SHAPE, "negative size");
+    if (n % 8 != 0 || k % 8 != 0) return fail(COC_ERR_SHAPE, "n and k must be multiples of 8 (n=%lld k=%lld)",
+                                              (long long)n, (long long)k);
+    if (m <= 0 || m % 32 != 0) return fail(COC_ERR_SHAPE, "weight gradient needs m > 0, m %% 32 == 0 (m=%lld)",
+                                          (long long)m);
+    const int64_t lim = int64_t(1) << 31;
+    if (m >= lim || n >= lim || k >= lim || m * k >= lim || m * n >= lim || k * n >= lim)
+        return fail(COC_ERR_SHAPE, "a matrix has 2^31 or more elements");
+    if (n == 0 || k == 0) return COC_OK;
+    const int64_t es = 2;
+    std::vector<Range> ins, outs;
+    COC_TRY(check_ptr(g, m * k * es, "g"));
+    COC_TRY(check_ptr(dy, m * n * es, "dy"));
+    COC_TRY(check_ptr(dw, k * n * es, "dw"));
+    ins.push_back(mk(g, m * k * es, "g"));
+    ins.push_back(mk(dy, m * n * es, "dy"));
+    outs.push_back(mk(dw, k * n * es, "dw"));
+    COC_TRY(check_alias(outs, ins));
+    // dw (k x n) = g^T dy: the activation operand is g read transposed (k
+    // output rows, reduction over m), the weight operand dy as stored
+    ChunksLaunch L{};
+    L.kind = kind_of(dt);
+    L.b = dy;
+    L.c = dw;
+    L.n = n;
+    L.k = m;
+    L.trans_a = 1;
+    L.lda = k;
+    L.npieces = 1;
+    L.a[0] = g;
+    L.rpb[0] = k;
+    L.nblk[0] = 1;
+    L.wait[0] = -1;
+    L.signal[0] = -1;
+    int32_t tiles[kMaxPieces + 1];
+    hipStream_t s = (hipStream_t)stream;
+    return launch(KC_GEMM, 2.0 * double(m) * double(n) * double(k), s,
+                  [&] { return launch_gemm_chunks(L, s, tiles); });
 }
 
 void coc_profile_enable(int32_t on) { g_prof_on.store(on ? 1 : 0); }

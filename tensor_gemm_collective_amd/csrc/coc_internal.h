@@ -58,6 +58,7 @@ struct GemmLaunch {
     int64_t base, stride, rpb;
     int32_t nblk;
     int32_t concurrent;  // chunk matmuls expected to run side by side (tile choice only)
+    int32_t trans_b;     // b holds the weights transposed: n rows of k elements (bf16 / fp16, k % 32 == 0)
 };
 
 // Fixed-order sum of nsrc row blocks: dst[dst_row0 + j] = sum_r src[r][src_row0 + j],
@@ -107,6 +108,11 @@ struct ChunksLaunch {
     int64_t n, k;
     const void* scales;  // w8a16 only
     int32_t qmode, group;
+    // trans_b: b holds the weights transposed (n rows of k elements);
+    // trans_a: the single piece's a holds the activations transposed (k rows
+    // of lda elements, one per output row; no row map)
+    int32_t trans_a, trans_b;
+    int64_t lda;
     int32_t npieces;
     const void* a[kMaxPieces];
     int64_t ashift[kMaxPieces];

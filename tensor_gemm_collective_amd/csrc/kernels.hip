@@ -101,6 +101,7 @@ struct GemmParams {
     int32_t rpb, rows, n, k;
     int32_t tiles_m, tiles_n;
     int32_t qmode, group;
+    int32_t lda;   // transposed activations: elements per stored row
 };
 
 // ------------------------------------------------------------------ tile order
@@ -753,8 +754,14 @@ constexpr int ring_lds_bytes() {
 // every wave has finished with it and has no stores outstanding.  poison:
 // store NaN instead of the products (a wait for the tile's inputs timed out).
 // SYS: system-scope (write-through) stores, for a tile another kernel reads
-// while this one runs.
-template <int BM, int BN, int S, int WM, int WN, int KIND, bool SYS = false>
+// while this one runs.  TA: the activation operand is stored transposed
+// (p.a holds its k rows of p.lda elements, m contiguous; one piece, no row
+// map); TB: the weight operand is stored transposed (p.b holds n rows of k
+// elements).  A transposed operand is staged the way the other one is
+// normally (rows of one k step's 64 bytes, or k rows read with the LDS
+// transpose), so both come out in the same MFMA fragments and the result
+// bits do not change.
+template <int BM, int BN, int S, int WM, int WN, int KIND, bool SYS = false, bool TA = false, bool TB = false>
 __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb, int64_t base, int64_t stride,
                                           int64_t ashift, int m0, int n0, uint8_t* sm, bool poison) {
     constexpr int BK = 32, NW = WM * WN;
@@ -765,12 +772,18 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     constexpr int APW = A_BYTES / 1024 / NW, BPW = B_BYTES / 1024 / NW, DPW = APW + BPW;
     constexpr int BROW = BN * BE / 16;   // 16-byte chunks per weight k-row
     constexpr int KPI = 64 / BROW;       // weight k-rows per load instruction
-    constexpr int NMM = FM * FN, NRD = FM + (W8 ? 1 : 2) * FN;
+    constexpr int WRD = (W8 || TB) ? 1 : 2;   // LDS reads per weight fragment
+    constexpr int ARD = TA ? 2 : 1;           // LDS reads per activation fragment
+    constexpr int NMM = FM * FN, NRD = ARD * FM + WRD * FN;
+    constexpr int AROW = BM * 2 / 16;         // TA: 16-byte chunks per activation k-row
+    constexpr int KPA = 64 / AROW;            // TA: activation k-rows per load instruction
     constexpr int OUT_DT = (KIND == GK_BF16) ? COC_BF16 : COC_F16;
     constexpr int TBL = S * STAGE;       // w8: scale table offset in LDS
     static_assert((A_BYTES / 1024) % NW == 0 && (B_BYTES / 1024) % NW == 0, "loads split over the waves");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32 x 32 MFMA blocks");
     static_assert(W8 ? (BROW >= 8 && BROW <= 64) : (BROW >= 16 && BROW <= 64), "weight swizzle");
+    static_assert(!(W8 && (TA || TB)) && !(TA && TB), "transposed operands: bf16 / fp16, one at a time");
+    static_assert(!TA || (AROW >= 16 && AROW <= 64), "activation swizzle");
     static_assert(S >= 3 && ring_lds_bytes<BM, BN, S, WM, WN, KIND>() <= 160 * 1024, "LDS ring");
 
     const int lane = threadIdx.x & 63;
@@ -782,6 +795,13 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     uint32_t aof[APW], bof[BPW];
 #pragma unroll
     for (int i = 0; i < APW; ++i) {
+        if constexpr (TA) {
+            // k-row K of the stage, columns m0 .. m0 + BM: chunk c at c ^ gB(K)
+            const int K = (wave * APW + i) * KPA + lane / AROW;
+            const int col = m0 + (((lane % AROW) ^ gB(K)) << 3);
+            aof[i] = (uint32_t)K * (uint32_t)p.lda * 2 + (uint32_t)(col < rows ? col : 0) * 2;
+            continue;
+        }
         const int row = (wave * APW + i) * 16 + (lane >> 2);
         const int r = m0 + row < rows ? m0 + row : rows - 1;
         const int64_t gr = map_row(r, rpb, base, stride) + ashift;
@@ -789,6 +809,13 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     }
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
+        if constexpr (TB) {
+            // weight row n0 + row (its k elements contiguous), 64 bytes per stage
+            const int row = (wave * BPW + i) * 16 + (lane >> 2);
+            const int nr = n0 + row < p.n ? n0 + row : p.n - 1;
+            bof[i] = (uint32_t)nr * (uint32_t)p.k * 2 + (((lane & 3) ^ gA<32>(row)) << 4);
+            continue;
+        }
         const int K = (wave * BPW + i) * KPI + lane / BROW;
         // chunk c of weight k-row K sits at c ^ gB(K) (bf16 / fp16: 8 columns per
         // chunk) or c ^ (K & 7) (int8: 16 columns per chunk)
@@ -801,6 +828,23 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     for (int ks = 0; ks < 2; ++ks) {
         const int row = wm * WTM + (lane & 31);
         ard[ks] = row * (BK * 2) + (((ks * 2 + (lane >> 5)) ^ gA<32>(row)) << 4);
+    }
+    // TA: activation fragment i read with the LDS transpose, like a weight
+    // fragment (k rows of BM elements)
+    int atr[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int r = lane & 15;
+        const int K = (lane >> 5) * 8 + (r >> 2);
+        const int col = wm * WTM + i * 32 + ((lane >> 4) & 1) * 16 + 4 * (r & 3);
+        atr[i] = K * BM * 2 + (((col >> 3) ^ gB(K)) << 4) + (col & 7) * 2;
+    }
+    // TB: weight fragments read like activation fragments, 16 bytes per lane
+    int brt[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int row = wn * WTN + (lane & 31);
+        brt[ks] = A_BYTES + row * (BK * 2) + (((ks * 2 + (lane >> 5)) ^ gA<32>(row)) << 4);
     }
     int brd[FN];
 #pragma unroll
@@ -830,11 +874,12 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     const int KT = p.k / BK;   // >= 1 (the launcher sends k == 0 elsewhere)
-    const int64_t bstep = (int64_t)BK * p.n * BE;
+    const int64_t astep = TA ? (int64_t)BK * p.lda * 2 : (int64_t)BK * 2;
+    const int64_t bstep = TB ? (int64_t)BK * 2 : (int64_t)BK * p.n * BE;
     auto dma = [&](int d, int kt, int slot) {
         const uint32_t l = lds0 + slot * STAGE;
         if (d < APW)
-            dma16_sbase(aof[d], p.a + (int64_t)kt * BK * 2, l + (wave * APW + d) * 1024);
+            dma16_sbase(aof[d], p.a + (int64_t)kt * astep, l + (wave * APW + d) * 1024);
         else
             dma16_sbase(bof[d - APW], p.b + (int64_t)kt * bstep, l + A_BYTES + (wave * BPW + d - APW) * 1024);
     };
@@ -853,15 +898,26 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             }
             return;
         }
-        if (r < 2 * FN) {
-            const int j = r >> 1, h = r & 1;
+        if (r < WRD * FN) {
+            if constexpr (TB) {
+                bf[buf][r] = *(const COC_LDS u32x4*)(st + brt[ks] + r * 32 * BK * 2);
+            } else {
+                const int j = r >> 1, h = r & 1;
+                const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (COC_LDS s16x4*)(st + brd[j] + (ks * 16 + h * 4) * BN * 2));
+                const u32x2 v2 = __builtin_bit_cast(u32x2, v);
+                bf[buf][j][2 * h] = v2[0];
+                bf[buf][j][2 * h + 1] = v2[1];
+            }
+        } else if constexpr (TA) {
+            const int ra = r - WRD * FN, i = ra >> 1, h = ra & 1;
             const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (COC_LDS s16x4*)(st + brd[j] + (ks * 16 + h * 4) * BN * 2));
+                (COC_LDS s16x4*)(st + atr[i] + (ks * 16 + h * 4) * BM * 2));
             const u32x2 v2 = __builtin_bit_cast(u32x2, v);
-            bf[buf][j][2 * h] = v2[0];
-            bf[buf][j][2 * h + 1] = v2[1];
+            af[buf][i][2 * h] = v2[0];
+            af[buf][i][2 * h + 1] = v2[1];
         } else {
-            af[buf][r - 2 * FN] = *(const COC_LDS u32x4*)(st + ard[ks] + (r - 2 * FN) * 32 * BK * 2);
+            af[buf][r - WRD * FN] = *(const COC_LDS u32x4*)(st + ard[ks] + (r - WRD * FN) * 32 * BK * 2);
         }
     };
     auto reads_at = [&](int s, int slot, int ks, int buf) {
@@ -1150,7 +1206,7 @@ __device__ __forceinline__ void fused_gather(const FusedGather& F, int c0, int c
     }
 }
 
-template <int BM, int BN, int S, int WM, int WN, int KIND, bool SIGNAL>
+template <int BM, int BN, int S, int WM, int WN, int KIND, bool SIGNAL, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P) {
     __shared__ __attribute__((aligned(1024))) uint8_t sm[ring_lds_bytes<BM, BN, S, WM, WN, KIND>()];
     constexpr int NX = 8;
@@ -1187,7 +1243,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P
         block_barrier();
         GemmParams g = P.g;
         g.a = P.a[c];
-        ring_tile<BM, BN, S, WM, WN, KIND, SIGNAL>(g, P.rows[c], P.rpb[c], P.base[c], P.stride[c], P.ashift[c],
+        ring_tile<BM, BN, S, WM, WN, KIND, SIGNAL, TA, TB>(g, P.rows[c], P.rpb[c], P.base[c], P.stride[c], P.ashift[c],
                                                    tm * BM, tn * BN, sm, wi >= 0 && !ok);
         if constexpr (SIGNAL) {
             if (P.signal[c] >= 0) wg_signal(P.done + P.signal[c] * kSyncWords);
@@ -1528,14 +1584,14 @@ template <int KIND>
 hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* tiles);
 
 template <int KIND>
-hipError_t launch_dma_kind(GemmParams p, int concurrent, hipStream_t s) {
+hipError_t launch_dma_kind(GemmParams p, int concurrent, hipStream_t s, bool trans_b = false) {
     // k a positive multiple of 32: the ring kernel with the largest tile that
     // still gives COC_RING_MIN_TILES workgroups across the chunk matmuls that
     // run side by side.  Otherwise the 128 x 128 direct-to-LDS kernel, which
     // zero-fills the k tail.  Every choice walks k the same way, so it never
     // changes the result bits.
     if (p.k >= 32 && p.k % 32 == 0) {
-        if (concurrent <= 1 || KIND == GK_W8_F16) {
+        if (concurrent <= 1 || KIND == GK_W8_F16 || trans_b) {
             // a lone matmul: the chunk-walking launch with one chunk (measured
             // faster than one workgroup per tile: no second dispatch wave)
             ChunksLaunch L{};
@@ -1548,6 +1604,7 @@ hipError_t launch_dma_kind(GemmParams p, int concurrent, hipStream_t s) {
             L.scales = p.scales;
             L.qmode = p.qmode;
             L.group = p.group;
+            L.trans_b = trans_b;
             L.a[0] = p.a;
             L.base[0] = p.base;
             L.stride[0] = p.stride;
@@ -1594,8 +1651,8 @@ int launch_gemm(const GemmLaunch& g, void* stream) {
             hipLaunchKernelGGL(gemm_f32, dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
             return hipGetLastError();
         }
-        case GK_F16: return launch_dma_kind<GK_F16>(p, g.concurrent, s);
-        case GK_BF16: return launch_dma_kind<GK_BF16>(p, g.concurrent, s);
+        case GK_F16: return launch_dma_kind<GK_F16>(p, g.concurrent, s, g.trans_b != 0);
+        case GK_BF16: return launch_dma_kind<GK_BF16>(p, g.concurrent, s, g.trans_b != 0);
         case GK_W8_F16:
             if (chunks_supported(g)) return launch_dma_kind<GK_W8_F16>(p, 1, s);
             return launch_w8_any(p, s);
@@ -1715,6 +1772,7 @@ int launch_gather_chunks(const GatherLaunch& g, int nchunks, const int64_t* row0
 
 bool chunks_supported(const GemmLaunch& g) {
     if (g.k < 32 || g.k % 32 != 0) return false;
+    if (g.trans_b) return g.kind == GK_BF16 || g.kind == GK_F16;
     if (g.kind == GK_BF16 || g.kind == GK_F16) return true;
     if (g.kind != GK_W8_F16 || g.n % 16 != 0) return false;   // whole 16-byte int8 chunks
     if (g.qmode != COC_PER_GROUP) return true;
@@ -1765,7 +1823,7 @@ int device_cus() {
     return cus[dev];
 }
 
-template <int BM, int BN, int S, int WM, int WN, int KIND>
+template <int BM, int BN, int S, int WM, int WN, int KIND, bool TA, bool TB>
 hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s, int32_t* tiles) {
     PersistParams P{};
     P.g.b = (const uint8_t*)L.b;
@@ -1775,6 +1833,7 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     P.g.scales = (const uint16_t*)L.scales;
     P.g.qmode = L.qmode;
     P.g.group = L.group > 0 ? L.group : 1;
+    P.g.lda = (int32_t)L.lda;
     P.g.tiles_n = (int32_t)((L.n + BN - 1) / BN);
     P.npieces = L.npieces;
     P.order = L.order;
@@ -1820,21 +1879,36 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     }
     tiles[kMaxPieces] = 8 * P.per_xcd;
     if (signal)
-        hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true>), dim3(8 * P.per_xcd), dim3(64 * WM * WN),
-                           0, s, P);
+        hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true, TA, TB>), dim3(8 * P.per_xcd),
+                           dim3(64 * WM * WN), 0, s, P);
     else
-        hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, false>), dim3(8 * P.per_xcd),
+        hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, false, TA, TB>), dim3(8 * P.per_xcd),
                            dim3(64 * WM * WN), 0, s, P);
     return hipGetLastError();
 }
 
-template <int KIND>
-hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* tiles) {
+template <int KIND, bool TA, bool TB>
+hipError_t launch_chunks_layout(const ChunksLaunch& L, hipStream_t s, int32_t* tiles) {
     int bm, bn, per_cu;
     switch (chunks_shape(L, &bm, &bn, &per_cu)) {
-        case 0: return launch_chunks_shape<256, 256, 4, 2, 4, KIND>(L, 1, s, tiles);
-        case 1: return launch_chunks_shape<128, 256, 4, 2, 4, KIND>(L, 1, s, tiles);
-        default: return launch_chunks_shape<128, 128, 4, 2, 2, KIND>(L, 2, s, tiles);
+        case 0: return launch_chunks_shape<256, 256, 4, 2, 4, KIND, TA, TB>(L, 1, s, tiles);
+        case 1: return launch_chunks_shape<128, 256, 4, 2, 4, KIND, TA, TB>(L, 1, s, tiles);
+        default: return launch_chunks_shape<128, 128, 4, 2, 2, KIND, TA, TB>(L, 2, s, tiles);
+    }
+}
+
+template <int KIND>
+hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* tiles) {
+    if constexpr (KIND == GK_W8_F16) {
+        if (L.trans_a || L.trans_b) return hipErrorInvalidValue;
+        return launch_chunks_layout<KIND, false, false>(L, s, tiles);
+    } else {
+        if (L.trans_a && L.trans_b) return hipErrorInvalidValue;
+        // a transposed activation operand has no row map: one piece
+        if (L.trans_a && (L.npieces != 1 || L.nblk[0] != 1 || L.ashift[0] != 0)) return hipErrorInvalidValue;
+        if (L.trans_a) return launch_chunks_layout<KIND, true, false>(L, s, tiles);
+        if (L.trans_b) return launch_chunks_layout<KIND, false, true>(L, s, tiles);
+        return launch_chunks_layout<KIND, false, false>(L, s, tiles);
     }
 }
 

@@ -162,12 +162,12 @@ def _peers(world, rank, base=20):
 
 def _ar(**kw):
     args = dict(x=_addr(1), w=_addr(2) * 16, y=_addr(3) * 256, p=_addr(4) * 1024, peers=_peers(8, 0),
-                world=8, rank=0, m=64, n=64, k=64, dt=tgc.COC_BF16, split=4, det=0)
+                world=8, rank=0, m=64, n=64, k=64, dt=tgc.COC_BF16, split=4, det=0, tw=0)
     args.update(kw)
     L = tgc.lib()
     return L.coc_matmul_all_reduce(args["x"], args["w"], args["y"], args["p"], args["peers"],
                                    args["world"], args["rank"], args["m"], args["n"], args["k"],
-                                   args["dt"], args["split"], args["det"], None, 0, None)
+                                   args["dt"], args["split"], args["det"], args["tw"], None, 0, None)
 
 
 @no_gpu_only
@@ -191,6 +191,8 @@ def _ar(**kw):
     (dict(y=_addr(3) * 256 + 2), 6),
     (dict(y=_addr(1)), 9),                   # y overlaps x
     (dict(p=_addr(3) * 256 + 4096), 9),      # partial_out overlaps y
+    (dict(tw=1, dt=0), 5),                    # transposed weights: bf16 / fp16 only
+    (dict(tw=1, k=48), 3),                    # transposed weights: k % 32 == 0
 ])
 def test_all_reduce_rejects(kw, status):
     st = _ar(**kw)
@@ -234,10 +236,26 @@ def test_allgather_rejects():
 
     def call(gathered=None, ws=None, ws_bytes=0, m=64, split=4):
         return L.coc_allgather_matmul(_addr(1), _peers(8, 0), _addr(2) * 16, _addr(3) * 256, gathered,
-                                      8, 0, m, 64, 64, tgc.COC_BF16, split, 0, ws, ws_bytes, None)
+                                      8, 0, m, 64, 64, tgc.COC_BF16, split, 0, 0, ws, ws_bytes, None)
     assert call() == 7                                   # no workspace for the non-V2 form
     assert call(ws=_addr(5) * 512, ws_bytes=100) == 7    # too small
     assert call(ws=_addr(5) * 512 + 8, ws_bytes=1 << 20) == 6
     assert call(m=60) == 3
     assert call(split=5) == 2
     assert call(gathered=_addr(3) * 256) == 9            # gathered_out overlaps y
+
+
+@no_gpu_only
+def test_weight_grad_rejects():
+    L = tgc.lib()
+
+    def call(g=_addr(1), dy=_addr(2) * 16, dw=_addr(3) * 256, m=64, n=64, k=64, dt=tgc.COC_BF16):
+        return L.coc_weight_grad(g, dy, dw, m, n, k, dt, None)
+    assert call(m=48) == 3          # m % 32
+    assert call(m=0) == 3
+    assert call(n=60) == 3
+    assert call(k=12) == 3
+    assert call(dt=tgc.COC_F32) == 5
+    assert call(g=None) == 1
+    assert call(dw=_addr(1) + 16) == 9   # dw overlaps g
+    assert call(dy=_addr(2) * 16 + 8) == 6

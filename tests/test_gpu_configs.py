@@ -104,6 +104,34 @@ def test_llama_allgather_matmul(llama_ag, split, rank):
     assert_close(y[torch.as_tensor(rows)], oracle.matmul(g_rows, f64(w, "bf16")), "bf16", "y (sampled rows)")
 
 
+# ------------------------------------------------------------------ LLaMA2-70B backward of the pair
+def test_llama_backward_pair(llama_ag):
+    """The backward of the sequence-parallel MLP pair at full size: dW of the
+    gate/up layer from V2's gathered G (8192 x 7168), and the dX of the down
+    projection, AG(dY) @ W^T, with the 3584 x 8192 forward weight read
+    transposed (reduction 8192, output 3584)."""
+    wl, shards, w = llama_ag
+    rank = 2
+    log(f"LLaMA2-70B backward: weight_grad {wl.k}x{wl.n} over m={wl.m}; AG dX with transposed weights")
+    sd = [s.to(DEV) for s in shards]
+    peers = [None if r == rank else sd[r] for r in range(wl.world)]
+    _, g = tgc.allgather_matmul(sd[rank], peers, w.to(DEV), rank, split=4, v2=True)
+    dy = synth.normal(wl.wid, synth.T_X, 9, (wl.m, wl.n), 1.0, "bf16")
+    dw = tgc.weight_grad(g, dy.to(DEV))
+    w_down = synth.normal(wl.wid, synth.T_W, 9, (3584, wl.k), 0.02, "bf16")       # forward RS weight, k x n
+    dys = [synth.normal(wl.wid, synth.T_PEER, 9 + r, (wl.m // wl.world, wl.k), 1.0, "bf16") for r in range(wl.world)]
+    dpeers = [None if r == rank else dys[r].to(DEV) for r in range(wl.world)]
+    dx = tgc.allgather_matmul(dys[rank].to(DEV), dpeers, w_down.to(DEV), rank, split=4, trans_w=True)
+    torch.cuda.synchronize()
+    assert dw.shape == (wl.k, wl.n) and dx.shape == (wl.m, 3584)
+    rows = sample_rows(wl.k, 8, n=24, seed=21)
+    G = oracle.allgather([f64(s, "bf16") for s in shards])
+    assert_close(dw[torch.as_tensor(rows)], oracle.weight_grad(G[:, rows], f64(dy, "bf16")), "bf16", "dW rows")
+    rows = sample_rows(wl.m, 4, n=24, seed=22)
+    DY = oracle.allgather([f64(d, "bf16") for d in dys])
+    assert_close(dx[torch.as_tensor(rows)], oracle.matmul(DY[rows], f64(w_down, "bf16").T), "bf16", "dX rows")
+
+
 # ------------------------------------------------------------------ LLaMA2-70B matmul reduce-scatter
 @pytest.fixture(scope="module")
 def llama_rs():

@@ -223,6 +223,95 @@ def test_allgather_matmul(dtype, split, rank, k):
     assert_bits_equal(y1, y_s1, "y independent of split")
 
 
+# ------------------------------------------------------------------ backward pair
+# dX = dY @ W^T with the forward k x n weight read transposed (trans_w), and
+# dW = G^T @ dY (weight_grad).  A transposed operand only changes how the
+# tile is staged, so the bits must equal the plain path on the stored
+# transpose; the oracle checks the values.
+TW_SHAPES = [(528, 392, 256), (2080, 1032, 96), (1024, 8200, 64)]   # m, n (output), k (reduction)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("m,n,k", TW_SHAPES)
+@pytest.mark.parametrize("split", [1, 4])
+def test_transposed_weights_compute_first(dtype, m, n, k, split):
+    log(f"trans_w AR/RS {dtype} m={m} n={n} k={k} split={split}")
+    world, rank = 4, 1
+    x = synth.normal(WID_TEST + 31, synth.T_X, rank, (m, k), 1.0, dtype)
+    w = synth.normal(WID_TEST + 31, synth.T_W, rank, (k, n), 0.02, dtype)   # the product's k x n weight
+    peers = synth.peers_random(WID_TEST + 31, world, rank, (m, n), 0.3, dtype)
+    xd, wd, wtd = dev(x), dev(w), dev(w).t().contiguous()                   # wtd: n x k, as stored
+    pd = [dev(q) for q in peers]
+    y_t, p_t = tgc.matmul_all_reduce(xd, wtd, pd, rank, split=split, deterministic=1, trans_w=True)
+    y_n, p_n = tgc.matmul_all_reduce(xd, wd, pd, rank, split=split, deterministic=1)
+    r_t, _ = tgc.matmul_reduce_scatter(xd, wtd, pd, rank, split=split, deterministic=1, trans_w=True)
+    r_n, _ = tgc.matmul_reduce_scatter(xd, wd, pd, rank, split=split, deterministic=1)
+    torch.cuda.synchronize()
+    assert_bits_equal(p_t, p_n, "partial_out, transposed weights")
+    assert_bits_equal(y_t, y_n, "all-reduce, transposed weights")
+    assert_bits_equal(r_t, r_n, "reduce-scatter, transposed weights")
+    y_ref, p_ref = oracle.matmul_all_reduce(f64(x, dtype), f64(w, dtype),
+                                            [None if q is None else f64(q, dtype) for q in peers], rank)
+    assert_close(p_t, p_ref, dtype, "partial_out")
+    assert_close(y_t, y_ref, dtype, "y")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("split", [1, 4, 8])
+@pytest.mark.parametrize("rank", [0, 5])
+def test_transposed_weights_allgather(dtype, split, rank):
+    log(f"trans_w AG {dtype} split={split} rank={rank}")
+    world, shard, n, k = 8, 64, 392, 256
+    shards = [synth.normal(WID_TEST + 32, synth.T_PEER, r, (shard, k), 1.0, dtype) for r in range(world)]
+    w = synth.normal(WID_TEST + 32, synth.T_W, 0, (k, n), 0.02, dtype)
+    peers = [None if r == rank else dev(shards[r]) for r in range(world)]
+    xs, wd = dev(shards[rank]), dev(w)
+    y_t, g_t = tgc.allgather_matmul(xs, peers, wd.t().contiguous(), rank, split=split, v2=True, trans_w=True)
+    y_n = tgc.allgather_matmul(xs, peers, wd, rank, split=split)
+    torch.cuda.synchronize()
+    assert_bits_equal(g_t, torch.cat(shards), "gathered_out")
+    assert_bits_equal(y_t, y_n, "all-gather matmul, transposed weights")
+    y_ref, _ = oracle.allgather_matmul([f64(s, dtype) for s in shards], f64(w, dtype))
+    assert_close(y_t, y_ref, dtype, "y")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("m,k,n", [(64, 520, 1040), (2048, 264, 392), (96, 1032, 8200), (4096, 256, 512)])
+def test_weight_grad(dtype, m, k, n):
+    log(f"weight_grad {dtype} m={m} k={k} n={n}")
+    g = synth.normal(WID_TEST + 33, synth.T_X, 0, (m, k), 1.0, dtype)
+    dy = synth.normal(WID_TEST + 33, synth.T_W, 0, (m, n), 1.0, dtype)
+    gd, dyd = dev(g), dev(dy)
+    dw = tgc.weight_grad(gd, dyd)
+    # the plain matmul on G^T as stored (world 1: partial_out = G^T @ dY)
+    _, p = tgc.matmul_all_reduce(gd.t().contiguous(), dyd, [None], 0, split=1)
+    torch.cuda.synchronize()
+    assert dw.shape == (k, n)
+    assert_bits_equal(dw, p, "weight_grad vs the plain matmul on G^T")
+    assert_close(dw, oracle.weight_grad(f64(g, dtype), f64(dy, dtype)), dtype, "dW")
+
+
+def test_weight_grad_of_gathered_matrix():
+    """The backward of the sequence-parallel pair at small scale: V2's gathered
+    G reused for dW, and dX = AG(dY) @ W^T through the all-gather op."""
+    world, shard, k, n, rank = 4, 64, 264, 384, 2   # n: the reduction of dX, a multiple of 32
+    dt = "bf16"
+    shards = [synth.normal(WID_TEST + 34, synth.T_PEER, r, (shard, k), 1.0, dt) for r in range(world)]
+    w = synth.normal(WID_TEST + 34, synth.T_W, 0, (k, n), 0.02, dt)
+    dys = [synth.normal(WID_TEST + 34, synth.T_X, r, (shard, n), 1.0, dt) for r in range(world)]
+    peers = [None if r == rank else dev(shards[r]) for r in range(world)]
+    _, g = tgc.allgather_matmul(dev(shards[rank]), peers, dev(w), rank, split=4, v2=True)
+    dy_full = dev(torch.cat(dys))
+    dw = tgc.weight_grad(g, dy_full)
+    dpeers = [None if r == rank else dev(dys[r]) for r in range(world)]
+    dx = tgc.allgather_matmul(dev(dys[rank]), dpeers, dev(w), rank, split=4, trans_w=True)   # (m x n) @ W^T
+    torch.cuda.synchronize()
+    G = oracle.allgather([f64(s, dt) for s in shards])
+    DY = oracle.allgather([f64(d, dt) for d in dys])
+    assert_close(dw, oracle.weight_grad(G, DY), dt, "dW")
+    assert_close(dx, oracle.matmul(DY, f64(w, dt).T), dt, "dX")
+
+
 # ------------------------------------------------------------------ w8a16
 @pytest.mark.parametrize("mode", ["per_tensor", "per_channel", "per_group"])
 @pytest.mark.parametrize("split", [1, 4])

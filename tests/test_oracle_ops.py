@@ -116,6 +116,49 @@ def test_allgather_matmul_equals_unsplit_sequence(T):
     assert np.array_equal(y, to_float(bf_matmul(frac_matrix(xf), frac_matrix(w))))
 
 
+# ----------------------------------------------------------------- backward pair
+def bf_weight_grad(G, D):
+    """dW[i][j] = sum over rows t of G[t][i] * D[t][j], element loops (exact)."""
+    m, k, n = len(G), len(G[0]), len(D[0])
+    out = []
+    for i in range(k):
+        row = []
+        for j in range(n):
+            s = Fraction(0)
+            for t in range(m):
+                s += G[t][i] * D[t][j]
+            row.append(s)
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 1, 1), (5, 3, 2), (7, 4, 6), (3, 6, 5)])
+def test_weight_grad_brute_force(m, k, n):
+    rng = np.random.default_rng(300 + m * 31 + k * 7 + n)
+    g = dyadic(rng, (m, k))
+    dy = dyadic(rng, (m, n))
+    assert np.array_equal(oracle.weight_grad(g, dy), to_float(bf_weight_grad(frac_matrix(g), frac_matrix(dy))))
+
+
+def test_weight_grad_identities():
+    """One-hot rows of dY pick rows of G (dW[:, j] = G[t, :] where dY[t, j] = 1),
+    and the gradient of the gathered sequence is the sum of the shards'."""
+    rng = np.random.default_rng(17)
+    m, k, n = 6, 4, 3
+    g = dyadic(rng, (m, k))
+    dy = np.zeros((m, n))
+    for j, t in enumerate((4, 0, 2)):
+        dy[t, j] = 1.0
+    dw = oracle.weight_grad(g, dy)
+    for j, t in enumerate((4, 0, 2)):
+        assert np.array_equal(dw[:, j], g[t])
+    dy = dyadic(rng, (m, n))
+    parts = [oracle.weight_grad(g[r * 2:(r + 1) * 2], dy[r * 2:(r + 1) * 2]) for r in range(3)]
+    assert np.array_equal(oracle.weight_grad(g, dy), parts[0] + parts[1] + parts[2])
+    with pytest.raises(ValueError):
+        oracle.weight_grad(g, dy[:5])
+
+
 # ----------------------------------------------------------------- w8a16
 def bf_dequant(q, s, mode, group):
     K, N = q.shape
