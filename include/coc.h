@@ -37,6 +37,11 @@
  *     later work on `stream` sees the outputs.  Inputs must stay valid until
  *     that work completes.  Different host threads may use different streams
  *     concurrently; two threads must not use the same stream concurrently.
+ *     The pipelined forms whose workgroups wait on device counters (the
+ *     one-launch pipelines) need their work resident together, so on one
+ *     device the library runs them one after another even when they come
+ *     from different streams: such a call waits on its stream for the
+ *     previous one (unless the stream is being captured into a graph).
  *   - `split` is the number of m-chunks the work is pipelined over: 1
  *     (serial, no overlap), 2, 4 or 8 (CoC guide, "Usage": the split count
  *     options; the m dimension must divide by it, CoC guide "Approach" and

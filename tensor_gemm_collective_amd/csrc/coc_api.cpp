@@ -98,6 +98,7 @@ struct StreamCtx {
     uint32_t* sync = nullptr;
     uint32_t done_sent[COC_MAX_SPLIT] = {};
     uint32_t ready_sent[COC_MAX_SPLIT] = {};
+    hipEvent_t tail = nullptr;     // end of this stream's last counter-waiting call
 };
 
 std::mutex g_ctx_mu;
@@ -120,6 +121,7 @@ coc_status get_ctx(hipStream_t main, StreamCtx** out) {
     COC_HIP(hipEventCreateWithFlags(&c->fork, hipEventDisableTiming));
     COC_HIP(hipEventCreateWithFlags(&c->join, hipEventDisableTiming));
     COC_HIP(hipEventCreateWithFlags(&c->join2, hipEventDisableTiming));
+    COC_HIP(hipEventCreateWithFlags(&c->tail, hipEventDisableTiming));
     COC_HIP(hipMalloc(&c->sync, kSyncLines * kSyncWords * sizeof(uint32_t)));
     COC_HIP(hipMemset(c->sync, 0, kSyncLines * kSyncWords * sizeof(uint32_t)));
     COC_HIP(hipDeviceSynchronize());
@@ -127,6 +129,69 @@ coc_status get_ctx(hipStream_t main, StreamCtx** out) {
     *out = c;
     return COC_OK;
 }
+
+// ------------------------------------------------------------------ waiting calls
+// The one-launch pipelines have workgroups that wait on counters other
+// workgroups (or a launch beside them) bump, which only works while the
+// waiting and the counting work are resident together.  Two such calls
+// running at once from different streams could each hold part of the compute
+// units while waiting on their own work that no longer fits; the bounded
+// waits would then give up and leave NaN.  So, per device, these calls are
+// chained: each waits on the caller's stream for the end of the previous one,
+// whatever stream that came from (calls on one stream are ordered anyway).  A
+// stream being captured into a graph takes no part in the chain.
+struct WaitChain {
+    std::mutex mu;
+    hipEvent_t last = nullptr;       // tail event of the last chained call
+    hipStream_t last_stream = nullptr;
+};
+
+std::mutex g_chain_mu;
+std::map<int, WaitChain*> g_chain;
+
+class ChainedCall {
+  public:
+    // Takes the device's chain (held until finish() or destruction) and makes
+    // `main` wait for the previous chained call on another stream.
+    coc_status begin(StreamCtx* c, hipStream_t main) {
+        int dev = 0;
+        COC_HIP(hipGetDevice(&dev));
+        {
+            std::lock_guard<std::mutex> lk(g_chain_mu);
+            WaitChain*& w = g_chain[dev];
+            if (w == nullptr) w = new WaitChain;
+            chain_ = w;
+        }
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        COC_HIP(hipStreamIsCapturing(main, &cs));
+        if (cs != hipStreamCaptureStatusNone) {
+            chain_ = nullptr;
+            return COC_OK;
+        }
+        lock_ = std::unique_lock<std::mutex>(chain_->mu);
+        if (chain_->last != nullptr && chain_->last_stream != main)
+            COC_HIP(hipStreamWaitEvent(main, chain_->last, 0));
+        ctx_ = c;
+        main_ = main;
+        return COC_OK;
+    }
+    // Marks the end of the call's work on `main` (after every join).
+    coc_status finish() {
+        if (chain_ == nullptr) return COC_OK;
+        COC_HIP(hipEventRecord(ctx_->tail, main_));
+        chain_->last = ctx_->tail;
+        chain_->last_stream = main_;
+        chain_ = nullptr;
+        lock_ = std::unique_lock<std::mutex>();
+        return COC_OK;
+    }
+
+  private:
+    WaitChain* chain_ = nullptr;
+    std::unique_lock<std::mutex> lock_;
+    StreamCtx* ctx_ = nullptr;
+    hipStream_t main_ = nullptr;
+};
 
 // ------------------------------------------------------------------ timing
 struct ProfRec {
@@ -303,6 +368,8 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
                                     hipStream_t main) {
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
+    ChainedCall chain;
+    COC_TRY(chain.begin(c, main));
     const size_t es = elem_size(P.dt);
     ChunksLaunch L = chunks_for(P, g0);
     // Chunks whose tiles all fall before the matmul's last round of workgroups
@@ -357,7 +424,7 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
         COC_HIP(hipEventRecord(c->join, c->side));
         COC_HIP(hipStreamWaitEvent(main, c->join, 0));
     }
-    return COC_OK;
+    return chain.finish();
 }
 
 // One-launch pipeline, communicate first: the gathers of all chunks go to the
@@ -370,6 +437,8 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
                                  hipStream_t main) {
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
+    ChainedCall chain;
+    COC_TRY(chain.begin(c, main));
     const size_t es = elem_size(P.dt);
     const int64_t shard = P.m / P.world;
     const int64_t own0 = P.rank * shard, own1 = own0 + shard;
@@ -411,7 +480,8 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
             L.gather_rows[i] = grows[i];
             L.ready_target[i] = (c->ready_sent[i] += (uint32_t)(i < fp.early ? fp.workgroups : fp.gatherers)) + off;
         }
-        return launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); });
+        COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
+        return chain.finish();
     }
     L.gather_nchunks = 0;
     COC_HIP(hipEventRecord(c->fork, main));
@@ -426,7 +496,7 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
     COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
     COC_HIP(hipEventRecord(c->join, c->side));
     COC_HIP(hipStreamWaitEvent(main, c->join, 0));
-    return COC_OK;
+    return chain.finish();
 }
 
 // Compute first, then reduce: all-reduce, reduce-scatter, w8a16 all-reduce.

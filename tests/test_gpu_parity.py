@@ -518,6 +518,63 @@ def test_bounded_wait_gives_up_to_nan(monkeypatch):
     assert_bits_equal(y2, ref2, "reduce-scatter after the forced time-out")
 
 
+def test_waiting_calls_from_two_streams_at_once():
+    """Two host threads, each on a stream of its own, issue the one-launch
+    pipelines at the same time: the all-gather matmul whose launch copies the
+    rows itself (its workgroups wait on one another) and the reduce-scatter
+    whose early chunks reduce beside the matmul (the reduce waits on it).  The
+    library keeps such calls from running at once on the device, so none of
+    their waits can run out for lack of room: every result matches the serial
+    form (split 1) bit for bit."""
+    import threading
+    bf = torch.bfloat16
+    g0 = torch.Generator(device="cuda").manual_seed(9)
+    world, shard, k, n, rank = 8, 512, 256, 7168, 5
+    shards = [torch.randn(shard, k, device="cuda", generator=g0).to(bf) for _ in range(world)]
+    w = (torch.randn(k, n, device="cuda", generator=g0) * 0.02).to(bf)
+    peers = [None if r == rank else shards[r] for r in range(world)]
+    m2, n2, k2, rank2 = 4096, 8192, 256, 3
+    x2 = torch.randn(m2, k2, device="cuda", generator=g0).to(bf)
+    w2 = (torch.randn(k2, n2, device="cuda", generator=g0) * 0.02).to(bf)
+    peers2 = [None if r == rank2 else torch.randn(m2, n2, device="cuda", generator=g0).to(bf) for r in range(world)]
+    ref = tgc.allgather_matmul(shards[rank], peers, w, rank, split=1)
+    ref2, _ = tgc.matmul_reduce_scatter(x2, w2, peers2, rank2, split=1, deterministic=1)
+    torch.cuda.synchronize()
+
+    calls = 6
+    outs = [[None] * calls for _ in range(2)]
+    errors = []
+    start = threading.Barrier(2)
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                start.wait()
+                for i in range(calls):
+                    if (i + t) % 2 == 0:
+                        outs[t][i] = tgc.allgather_matmul(shards[rank], peers, w, rank, split=4, v2=True)[0]
+                    else:
+                        outs[t][i] = tgc.matmul_reduce_scatter(x2, w2, peers2, rank2, split=4,
+                                                               deterministic=1)[0]
+            s.synchronize()
+        except Exception as e:   # reported on the main thread
+            errors.append(e)
+
+    log("one-launch pipelines from two threads / two streams at once")
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for t in range(2):
+        for i in range(calls):
+            want = ref if (i + t) % 2 == 0 else ref2
+            assert_bits_equal(outs[t][i], want, f"thread {t} call {i}")
+
+
 @pytest.mark.parametrize("split", [2, 4, 8])
 def test_pipeline_handover_reuses_buffers_without_stale_rows(split):
     """Two input sets alternate through the same output / gathered buffers, so
