@@ -23,10 +23,21 @@ from .coc import (
     reduce_fixed_order,
     normwise_rel_error,
 )
+from .moe import (
+    received_order,
+    alltoall_dispatch,
+    group_rows,
+    grouped_matmul,
+    alltoall_grouped_matmul,
+    alltoall_combine,
+    grouped_matmul_alltoall,
+)
 
 __all__ = [
     "round_to", "encode", "decode", "round_f32", "round_dtype", "decode_dtype",
     "matmul", "matmul_all_reduce", "matmul_reduce_scatter", "allgather",
     "allgather_matmul", "weight_grad", "dequant_weight", "matmul_all_reduce_w8a16",
     "reduce_fixed_order", "normwise_rel_error",
+    "received_order", "alltoall_dispatch", "group_rows", "grouped_matmul",
+    "alltoall_grouped_matmul", "alltoall_combine", "grouped_matmul_alltoall",
 ]
