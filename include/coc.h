@@ -207,6 +207,65 @@ coc_status coc_weight_grad(const void* g, const void* dy, void* dw, int64_t m, i
                            coc_dtype dt, void* stream);
 
 /*
+ * MoE expert all-to-all + grouped matmul, one expert-parallel rank's share
+ * (Ampipe page, "Problem analysis": an all-to-all before and one after the
+ * expert MLP exchange tokens between the ranks of the expert-parallel group;
+ * "Solution": the input is cut along the sequence into independent pieces
+ * whose communication and compute are pipelined; the Overlap blog's EP MC2:
+ * the all-to-all fused with the experts' grouped matmul into one pipeline).
+ *
+ * Rows.  counts (HOST array, split x world x experts int64, read during the
+ * call only): in sequence piece p, source rank r routes counts[p][r][e] rows
+ * to this rank's local expert e.  A source's rows for this rank are ordered
+ * piece-major, then by local expert, then in the source's order.  The
+ * received matrix R (total x k, total = the sum of counts) orders its rows
+ * piece-major, then by local expert, then by source rank, then in the
+ * source's order: every (piece, expert) group is one contiguous block.  w
+ * holds the local experts' weights, experts x k x n (expert e at offset
+ * e * k * n).
+ *
+ *   coc_alltoall_grouped_matmul (dispatch, then the experts' first matmul):
+ *     R = the sources' rows in the received order (bit copy), into recv_out;
+ *     y[j] = round_dt(R[j] @ W_e(j))     (total x n), e(j) the row's expert.
+ *     x_own: this rank's own rows for itself (source `rank`); peer_bufs[r]:
+ *     source r's rows (HOST array of `world` device pointers, entry `rank`
+ *     ignored; an entry of a source with no rows may be NULL).
+ *
+ *   coc_grouped_matmul_alltoall (the experts' second matmul, then combine):
+ *     y_local[j] = round_dt(h[j] @ W_e(j))   (total x n, h in the received
+ *     order), then every row goes back to its source at the position it had
+ *     there: y_own receives this rank's own rows, peer_out[r] source r's
+ *     (HOST array of device pointers, entry `rank` ignored; an entry of a
+ *     source with no rows may be NULL).
+ *
+ * Pipeline: piece p's copy overlaps the matmul of other pieces (dispatch:
+ * each (piece, expert) group's tiles wait for that piece's copy; combine: a
+ * piece's rows go back once all its tiles are stored).  The dispatch
+ * overlaps only when recv_out is 128-byte aligned and a row is a whole
+ * number of 128-byte lines (k a multiple of 64); otherwise its copy runs
+ * before its matmul.  `split` is the
+ * number of sequence pieces (the Ampipe degree), 1..COC_MAX_SPLIT; it is the
+ * first dimension of counts and fixes the row layout.  A row's result does
+ * not depend on the pieces, the run or the other rows (binary32
+ * accumulation over k in increasing order).
+ *
+ * Requirements: bf16 or fp16; world in [1, COC_MAX_WORLD], rank in [0,
+ * world); experts in [1, 16]; k > 0 a multiple of 32; n > 0 a multiple of 8;
+ * at most 16 non-empty (piece, expert) groups and 128 non-empty (piece,
+ * expert, source) blocks; each matrix below 2^31 elements; 16-byte aligned
+ * pointers; no output overlapping an input or another output.  A call with
+ * no rows does nothing.
+ */
+coc_status coc_alltoall_grouped_matmul(const void* x_own, const void* const* peer_bufs, const int64_t* counts,
+                                       const void* w, void* y, void* recv_out, int32_t world, int32_t rank,
+                                       int32_t experts, int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                       void* stream);
+coc_status coc_grouped_matmul_alltoall(const void* h, const void* w, void* y_local, void* y_own,
+                                       void* const* peer_out, const int64_t* counts, int32_t world, int32_t rank,
+                                       int32_t experts, int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                       void* stream);
+
+/*
  * w8A16 pseudo-quantised MATMUL_ALL_REDUCE (CoC guide, "Approach", last item
  * of the fused-operator list: fp16, int8 weights, per-tensor / per-channel /
  * per-group scales).  Weight-only symmetric quantisation, no zero point:

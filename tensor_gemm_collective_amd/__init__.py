@@ -16,6 +16,8 @@ from .coc import (  # noqa: F401
     allgather_matmul,
     matmul_all_reduce_w8a16,
     weight_grad,
+    alltoall_grouped_matmul,
+    grouped_matmul_alltoall,
     workspace_bytes,
     plan,
     profile_enable,

@@ -33,7 +33,8 @@ KCLASS = ("gemm", "reduce", "gather")
 # exported symbols, as declared in include/coc.h
 EXPORTS = (
     "coc_matmul_all_reduce", "coc_matmul_reduce_scatter", "coc_allgather_matmul",
-    "coc_matmul_all_reduce_w8a16", "coc_weight_grad", "coc_workspace_bytes", "coc_status_string",
+    "coc_matmul_all_reduce_w8a16", "coc_weight_grad", "coc_alltoall_grouped_matmul",
+    "coc_grouped_matmul_alltoall", "coc_workspace_bytes", "coc_status_string",
     "coc_last_error", "coc_plan", "coc_profile_enable", "coc_profile_read", "coc_profile_records",
 )
 
@@ -76,8 +77,12 @@ def lib() -> ctypes.CDLL:
         _vp, _vp, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(_vp), _i32, _i32, _i64, _i64, _i64,
         _i32, _i32, _vp, _sz, _vp]
     L.coc_weight_grad.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]
+    moe_tail = [ctypes.POINTER(_i64), _i32, _i32, _i32, _i64, _i64, _i32, _i32, _vp]
+    L.coc_alltoall_grouped_matmul.argtypes = [_vp, ctypes.POINTER(_vp)] + moe_tail[:1] + [_vp, _vp, _vp] + moe_tail[1:]
+    L.coc_grouped_matmul_alltoall.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(_vp)] + moe_tail
     for f in ("coc_matmul_all_reduce", "coc_matmul_reduce_scatter", "coc_allgather_matmul",
-              "coc_matmul_all_reduce_w8a16", "coc_weight_grad"):
+              "coc_matmul_all_reduce_w8a16", "coc_weight_grad", "coc_alltoall_grouped_matmul",
+              "coc_grouped_matmul_alltoall"):
         getattr(L, f).restype = _i32
     L.coc_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64, _i32, _i32, _i32]
     L.coc_workspace_bytes.restype = _sz
@@ -212,6 +217,55 @@ def weight_grad(g, dy, *, dw=None, stream=None):
     _check(lib().coc_weight_grad(_ptr(g), _ptr(dy), _ptr(dw), m, n, k, _dtype_code(g),
                                  _stream(stream, g.device)))
     return dw
+
+
+def _counts_array(counts):
+    """(ctypes int64 array, (split, world, experts), total rows) of a
+    split x world x experts nested sequence or array of row counts."""
+    import numpy as np
+    c = np.ascontiguousarray(np.asarray(counts, dtype=np.int64))
+    if c.ndim != 3:
+        raise ValueError(f"counts must be split x world x experts, got shape {c.shape}")
+    arr = (_i64 * c.size)(*c.ravel().tolist())
+    return arr, c.shape, int(c.sum())
+
+
+def alltoall_grouped_matmul(x_own, peers, counts, w, rank, *, y=None, recv_out=None, stream=None):
+    """MoE dispatch all-to-all, then the experts' grouped matmul.
+
+    counts[p][r][e]: rows source r routes to local expert e in sequence piece p.
+    x_own / peers[r]: the rows this rank / source r sends here (piece, then
+    expert order); w: experts x k x n.  Returns (y, recv): recv the received
+    rows (piece, expert, source order), y[j] = recv[j] @ w[expert of j]."""
+    arr, (split, world, experts), total = _counts_array(counts)
+    k, n = w.shape[1], w.shape[2]
+    y = _empty((total, n), w) if y is None else y
+    recv_out = _empty((total, k), w) if recv_out is None else recv_out
+    _check(lib().coc_alltoall_grouped_matmul(
+        _ptr(x_own), _peer_array(peers, rank), arr, _ptr(w), _ptr(y), _ptr(recv_out), world, rank, experts,
+        n, k, _dtype_code(w), split, _stream(stream, w.device)))
+    return y, recv_out
+
+
+def grouped_matmul_alltoall(h, w, counts, rank, *, peer_out=None, y_own=None, y_local=None, stream=None):
+    """The experts' grouped matmul, then the MoE combine all-to-all.
+
+    h: the received rows (piece, expert, source order), total x k; w: experts
+    x k x n.  Every row of y_local = h @ w[expert] goes back to its source:
+    y_own receives this rank's rows, peer_out[r] source r's.  Returns
+    (y_own, peer_out, y_local)."""
+    import numpy as np
+    arr, (split, world, experts), total = _counts_array(counts)
+    k, n = w.shape[1], w.shape[2]
+    rows = np.asarray(counts, dtype=np.int64).sum(axis=(0, 2))
+    y_local = _empty((total, n), w) if y_local is None else y_local
+    y_own = _empty((int(rows[rank]), n), w) if y_own is None else y_own
+    if peer_out is None:
+        peer_out = [None if r == rank else _empty((int(rows[r]), n), w) for r in range(world)]
+    _check(lib().coc_grouped_matmul_alltoall(
+        _ptr(h), _ptr(w), _ptr(y_local), _ptr(y_own), _peer_array(peer_out, rank), arr, world, rank, experts,
+        n, k, _dtype_code(w), split, _stream(stream, w.device)))
+    return y_own, peer_out, y_local
 
 
 def matmul_all_reduce_w8a16(x, w_q, scales, mode, peers, rank, *, group_size=128, y=None,

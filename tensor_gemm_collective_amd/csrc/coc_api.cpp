@@ -654,6 +654,217 @@ coc_status compute_first_op(coc_op op, const void* x, const void* w, const void*
     return run_compute_first(P, g0, r0, (hipStream_t)stream);
 }
 
+// ------------------------------------------------------------------ expert all-to-all
+// Rows of the MoE expert all-to-all + grouped matmul pair (Ampipe page,
+// "Problem analysis" and "Solution"; the Overlap blog's EP MC2): in sequence
+// piece p, source rank r routes counts[p][r][e] rows to local expert e.  A
+// source's rows are ordered piece, expert; the received matrix piece, expert,
+// source, so each (piece, expert) group is one contiguous block.  Pieces are
+// the pipeline's chunks; each group is one piece of the chunk-walking matmul.
+struct MoePlan {
+    int32_t world, rank, experts, split;
+    int64_t n, k, total;
+    coc_dtype dt;
+    int64_t src_rows[COC_MAX_WORLD];
+    int64_t chunk_row0[COC_MAX_SPLIT], chunk_rows[COC_MAX_SPLIT];
+    int32_t ngroups;
+    int64_t group_row0[kMaxPieces], group_rows[kMaxPieces];
+    int32_t group_expert[kMaxPieces], group_chunk[kMaxPieces];
+    int32_t seg0[COC_MAX_SPLIT + 1];
+    A2ASegment seg[kMaxA2ASegs];
+};
+
+coc_status make_moe_plan(const int64_t* counts, int32_t world, int32_t rank, int32_t experts, int64_t n,
+                         int64_t k, coc_dtype dt, int32_t split, MoePlan* M) {
+    if (world < 1 || world > COC_MAX_WORLD || rank < 0 || rank >= world)
+        return fail(COC_ERR_WORLD, "world=%d rank=%d out of range", world, rank);
+    if (split < 1 || split > COC_MAX_SPLIT)
+        return fail(COC_ERR_SPLIT, "expert all-to-all: pieces (split) must be in [1, %d], got %d", COC_MAX_SPLIT,
+                    split);
+    if (experts < 1 || experts > kMaxPieces)
+        return fail(COC_ERR_SHAPE, "local experts must be in [1, %d], got %d", kMaxPieces, experts);
+    if (dt != COC_BF16 && dt != COC_F16) return fail(COC_ERR_DTYPE, "expert all-to-all: bf16 or fp16 only");
+    if (n <= 0 || k <= 0 || n % 8 != 0 || k % 32 != 0)
+        return fail(COC_ERR_SHAPE, "expert all-to-all needs n > 0, n %% 8 == 0, k > 0, k %% 32 == 0 (n=%lld k=%lld)",
+                    (long long)n, (long long)k);
+    if (!counts) return fail(COC_ERR_NULL, "counts is NULL");
+    const int64_t lim = int64_t(1) << 31;
+    if (n >= lim || k >= lim || k * n >= lim) return fail(COC_ERR_SHAPE, "an expert weight has 2^31 or more elements");
+    MoePlan& P = *M;
+    P = MoePlan{};
+    P.world = world;
+    P.rank = rank;
+    P.experts = experts;
+    P.split = split;
+    P.n = n;
+    P.k = k;
+    P.dt = dt;
+    const int64_t width = n > k ? n : k;
+    auto cnt = [&](int p, int r, int e) { return counts[((int64_t)p * world + r) * experts + e]; };
+    // each source's first row of (piece p, expert e)
+    std::vector<int64_t> src_off((size_t)split * world * experts);
+    for (int r = 0; r < world; ++r) {
+        int64_t row = 0;
+        for (int p = 0; p < split; ++p)
+            for (int e = 0; e < experts; ++e) {
+                const int64_t c = cnt(p, r, e);
+                if (c < 0 || c >= lim) return fail(COC_ERR_SHAPE, "counts[%d][%d][%d] = %lld", p, r, e, (long long)c);
+                src_off[((size_t)p * world + r) * experts + e] = row;
+                row += c;
+                if (row * width >= lim) return fail(COC_ERR_SHAPE, "source %d's rows have 2^31 or more elements", r);
+            }
+        P.src_rows[r] = row;
+    }
+    int64_t row = 0;
+    int nseg = 0;
+    for (int p = 0; p < split; ++p) {
+        P.chunk_row0[p] = row;
+        P.seg0[p] = nseg;
+        for (int e = 0; e < experts; ++e) {
+            const int64_t g0 = row;
+            for (int r = 0; r < world; ++r) {
+                const int64_t c = cnt(p, r, e);
+                if (c == 0) continue;
+                if (nseg == kMaxA2ASegs)
+                    return fail(COC_ERR_SHAPE, "more than %d non-empty (piece, expert, source) blocks", kMaxA2ASegs);
+                P.seg[nseg++] = A2ASegment{(int32_t)row, (int32_t)src_off[((size_t)p * world + r) * experts + e],
+                                           (int32_t)c, r};
+                row += c;
+                if (row * width >= lim) return fail(COC_ERR_SHAPE, "the received rows have 2^31 or more elements");
+            }
+            if (row > g0) {
+                if (P.ngroups == kMaxPieces)
+                    return fail(COC_ERR_SHAPE, "more than %d non-empty (piece, expert) groups", kMaxPieces);
+                const int i = P.ngroups++;
+                P.group_row0[i] = g0;
+                P.group_rows[i] = row - g0;
+                P.group_expert[i] = e;
+                P.group_chunk[i] = p;
+            }
+        }
+        P.chunk_rows[p] = row - P.chunk_row0[p];
+    }
+    P.seg0[split] = nseg;
+    P.total = row;
+    return COC_OK;
+}
+
+double moe_flops(const MoePlan& M) { return 2.0 * double(M.total) * double(M.n) * double(M.k); }
+
+// The grouped matmul: one piece per (piece, expert) group, A = `a` (the
+// received-order rows), weights w + e * k * n, output rows as the input's.
+ChunksLaunch moe_matmul(const MoePlan& M, const void* a, const void* w, void* y) {
+    ChunksLaunch L{};
+    L.kind = kind_of(M.dt);
+    L.b = w;
+    L.c = y;
+    L.n = M.n;
+    L.k = M.k;
+    const size_t wbytes = (size_t)M.k * (size_t)M.n * elem_size(M.dt);
+    for (int i = 0; i < M.ngroups; ++i) {
+        add_piece(&L, a, 0, M.group_row0[i], M.group_rows[i], -1);
+        L.bp[L.npieces - 1] = (const uint8_t*)w + (size_t)M.group_expert[i] * wbytes;
+    }
+    return L;
+}
+
+A2ALaunch moe_a2a(const MoePlan& M, void* local, int64_t row_bytes) {
+    A2ALaunch a{};
+    a.local = local;
+    a.row_bytes = row_bytes;
+    a.nchunks = M.split;
+    for (int p = 0; p < M.split; ++p) {
+        a.row0[p] = M.chunk_row0[p];
+        a.rows[p] = M.chunk_rows[p];
+    }
+    for (int p = 0; p <= M.split; ++p) a.seg0[p] = M.seg0[p];
+    for (int i = 0; i < M.seg0[M.split]; ++i) a.seg[i] = M.seg[i];
+    return a;
+}
+
+// Communicate first: the dispatch copy of every piece on the side stream,
+// each workgroup counting itself done per piece; the grouped matmul walks the
+// (piece, expert) groups on the caller's stream, each group waiting for its
+// piece's count.  The matmul reads the received rows through the L2, which
+// is safe only if no 128-byte line holds rows of two pieces (a tile of one
+// piece would cache the other's line before its copy): rows of whole lines on
+// a 128-byte aligned matrix.  Otherwise the copy runs first on the caller's
+// stream and the matmul after it (no overlap).
+coc_status run_moe_dispatch(const MoePlan& M, const void* const* src, const void* w, void* y, void* recv,
+                            hipStream_t main) {
+    StreamCtx* c = nullptr;
+    COC_TRY(get_ctx(main, &c));
+    ChainedCall chain;
+    COC_TRY(chain.begin(c, main));
+    const size_t es = elem_size(M.dt);
+    const bool overlap = (uintptr_t)recv % 128 == 0 && (M.k * (int64_t)es) % 128 == 0;
+    A2ALaunch a = moe_a2a(M, recv, M.k * (int64_t)es);
+    for (int r = 0; r < M.world; ++r) a.remote[r] = const_cast<void*>(src[r]);
+    a.to_remote = 0;
+    a.ready = c->sync + COC_MAX_SPLIT * kSyncWords;
+    hipStream_t cs = overlap ? c->side : main;
+    if (overlap) {
+        COC_HIP(hipEventRecord(c->fork, main));
+        COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
+    }
+    int32_t per_chunk = 0;
+    const double bytes = 2.0 * double(M.total) * double(M.k) * double(es);
+    COC_TRY(launch(KC_GATHER, bytes, cs, [&] { return launch_a2a_chunks(a, cs, &per_chunk); }));
+    ChunksLaunch L = moe_matmul(M, recv, w, y);
+    for (int i = 0; i < L.npieces; ++i) L.wait[i] = overlap ? M.group_chunk[i] : -1;
+    L.ready = overlap ? a.ready : nullptr;
+    L.order = 1;
+    L.spin_limit = spin_limit_override();
+    const uint32_t off = target_offset();
+    // the copy's adds happen either way: keep the running targets exact
+    for (int p = 0; p < M.split; ++p) L.ready_target[p] = (c->ready_sent[p] += (uint32_t)per_chunk) + off;
+    int32_t tiles[kMaxPieces + 1];
+    COC_TRY(launch(KC_GEMM, moe_flops(M), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
+    if (overlap) {
+        COC_HIP(hipEventRecord(c->join, c->side));
+        COC_HIP(hipStreamWaitEvent(main, c->join, 0));
+    }
+    return chain.finish();
+}
+
+// Compute first: the grouped matmul walks the groups piece by piece on the
+// caller's stream, counting each piece's finished tiles; the combine copy, on
+// the side stream from the start, sends a piece's rows back once its count is
+// complete.
+coc_status run_moe_combine(const MoePlan& M, const void* h, const void* w, void* y_local, void* const* dst,
+                           hipStream_t main) {
+    StreamCtx* c = nullptr;
+    COC_TRY(get_ctx(main, &c));
+    ChainedCall chain;
+    COC_TRY(chain.begin(c, main));
+    const size_t es = elem_size(M.dt);
+    ChunksLaunch L = moe_matmul(M, h, w, y_local);
+    for (int i = 0; i < L.npieces; ++i) L.signal[i] = M.group_chunk[i];
+    L.done = c->sync;
+    L.order = 0;
+    int32_t tiles[kMaxPieces + 1];
+    chunks_tiles(L, tiles);
+    A2ALaunch a = moe_a2a(M, y_local, M.n * (int64_t)es);
+    for (int r = 0; r < M.world; ++r) a.remote[r] = dst[r];
+    a.to_remote = 1;
+    a.done = c->sync;
+    a.spin_limit = spin_limit_override();
+    uint32_t per_piece[COC_MAX_SPLIT] = {};
+    for (int i = 0; i < L.npieces; ++i) per_piece[M.group_chunk[i]] += (uint32_t)tiles[i];
+    const uint32_t off = target_offset();
+    for (int p = 0; p < M.split; ++p) a.target[p] = (c->done_sent[p] += per_piece[p]) + off;
+    COC_HIP(hipEventRecord(c->fork, main));
+    COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
+    int32_t launched[kMaxPieces + 1];
+    COC_TRY(launch(KC_GEMM, moe_flops(M), main, [&] { return launch_gemm_chunks(L, main, launched); }));
+    int32_t unused = 0;
+    const double bytes = 2.0 * double(M.total) * double(M.n) * double(es);
+    COC_TRY(launch(KC_GATHER, bytes, c->side, [&] { return launch_a2a_chunks(a, c->side, &unused); }));
+    COC_HIP(hipEventRecord(c->join, c->side));
+    COC_HIP(hipStreamWaitEvent(main, c->join, 0));
+    return chain.finish();
+}
+
 }  // namespace
 }  // namespace coc
 
@@ -792,6 +1003,80 @@ coc_status coc_weight_grad(const void* g, const void* dy, void* dw, int64_t m, i
     hipStream_t s = (hipStream_t)stream;
     return launch(KC_GEMM, 2.0 * double(m) * double(n) * double(k), s,
                   [&] { return launch_gemm_chunks(L, s, tiles); });
+}
+
+coc_status coc_alltoall_grouped_matmul(const void* x_own, const void* const* peer_bufs, const int64_t* counts,
+                                       const void* w, void* y, void* recv_out, int32_t world, int32_t rank,
+                                       int32_t experts, int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                       void* stream) {
+    clear_error();
+    MoePlan M;
+    COC_TRY(make_moe_plan(counts, world, rank, experts, n, k, dt, split, &M));
+    if (M.total == 0) return COC_OK;
+    const int64_t es = 2;
+    static const char* names[COC_MAX_WORLD] = {"peer_bufs[0]", "peer_bufs[1]", "peer_bufs[2]", "peer_bufs[3]",
+                                               "peer_bufs[4]", "peer_bufs[5]", "peer_bufs[6]", "peer_bufs[7]"};
+    std::vector<Range> ins, outs;
+    const void* src[COC_MAX_WORLD] = {};
+    for (int r = 0; r < world; ++r) {
+        const int64_t bytes = M.src_rows[r] * k * es;
+        if (r == rank) {
+            COC_TRY(check_ptr(x_own, bytes, "x_own"));
+            ins.push_back(mk(x_own, bytes, "x_own"));
+            src[r] = x_own;
+            continue;
+        }
+        if (bytes > 0 && !peer_bufs) return fail(COC_ERR_NULL, "peer_bufs is NULL");
+        const void* pb = bytes > 0 ? peer_bufs[r] : nullptr;
+        COC_TRY(check_ptr(pb, bytes, names[r]));
+        ins.push_back(mk(pb, bytes, names[r]));
+        src[r] = pb;
+    }
+    COC_TRY(check_ptr(w, experts * k * n * es, "w"));
+    COC_TRY(check_ptr(y, M.total * n * es, "y"));
+    COC_TRY(check_ptr(recv_out, M.total * k * es, "recv_out"));
+    ins.push_back(mk(w, experts * k * n * es, "w"));
+    outs.push_back(mk(y, M.total * n * es, "y"));
+    outs.push_back(mk(recv_out, M.total * k * es, "recv_out"));
+    COC_TRY(check_alias(outs, ins));
+    return run_moe_dispatch(M, src, w, y, recv_out, (hipStream_t)stream);
+}
+
+coc_status coc_grouped_matmul_alltoall(const void* h, const void* w, void* y_local, void* y_own,
+                                       void* const* peer_out, const int64_t* counts, int32_t world, int32_t rank,
+                                       int32_t experts, int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                       void* stream) {
+    clear_error();
+    MoePlan M;
+    COC_TRY(make_moe_plan(counts, world, rank, experts, n, k, dt, split, &M));
+    if (M.total == 0) return COC_OK;
+    const int64_t es = 2;
+    static const char* names[COC_MAX_WORLD] = {"peer_out[0]", "peer_out[1]", "peer_out[2]", "peer_out[3]",
+                                               "peer_out[4]", "peer_out[5]", "peer_out[6]", "peer_out[7]"};
+    std::vector<Range> ins, outs;
+    COC_TRY(check_ptr(h, M.total * k * es, "h"));
+    COC_TRY(check_ptr(w, experts * k * n * es, "w"));
+    COC_TRY(check_ptr(y_local, M.total * n * es, "y_local"));
+    ins.push_back(mk(h, M.total * k * es, "h"));
+    ins.push_back(mk(w, experts * k * n * es, "w"));
+    outs.push_back(mk(y_local, M.total * n * es, "y_local"));
+    void* dst[COC_MAX_WORLD] = {};
+    for (int r = 0; r < world; ++r) {
+        const int64_t bytes = M.src_rows[r] * n * es;
+        if (r == rank) {
+            COC_TRY(check_ptr(y_own, bytes, "y_own"));
+            outs.push_back(mk(y_own, bytes, "y_own"));
+            dst[r] = y_own;
+            continue;
+        }
+        if (bytes > 0 && !peer_out) return fail(COC_ERR_NULL, "peer_out is NULL");
+        void* pb = bytes > 0 ? peer_out[r] : nullptr;
+        COC_TRY(check_ptr(pb, bytes, names[r]));
+        outs.push_back(mk(pb, bytes, names[r]));
+        dst[r] = pb;
+    }
+    COC_TRY(check_alias(outs, ins));
+    return run_moe_combine(M, h, w, y_local, dst, (hipStream_t)stream);
 }
 
 void coc_profile_enable(int32_t on) { g_prof_on.store(on ? 1 : 0); }

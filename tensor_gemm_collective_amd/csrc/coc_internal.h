@@ -115,6 +115,7 @@ struct ChunksLaunch {
     int64_t lda;
     int32_t npieces;
     const void* a[kMaxPieces];
+    const void* bp[kMaxPieces];   // piece i's weights if set (a grouped matmul), else b
     int64_t ashift[kMaxPieces];
     int64_t base[kMaxPieces], stride[kMaxPieces], rpb[kMaxPieces];
     int32_t nblk[kMaxPieces];
@@ -162,6 +163,34 @@ struct ReduceChunksLaunch {
     uint32_t spin_limit;     // polls before a wait gives up (0: the default, about 2 s)
 };
 
+// The copy of an expert all-to-all, chunk by chunk.  Chunk c covers local
+// rows [row0[c], row0[c] + rows[c]) of `local` (the received matrix, or the
+// grouped matmul's output), cut into segments seg0[c] .. seg0[c + 1] - 1 in
+// row order; segment i pairs its local rows with `rows` rows of remote buffer
+// remote[buf] from remote_row on.  to_remote == 0 copies remote -> local
+// (dispatch; system-scope stores, then each workgroup adds 1 to one of the
+// chunk's ready lines), 1 copies local -> remote (combine; each chunk first
+// waits for done[c] to reach target[c], if done is set).  All rows are
+// row_bytes wide (a multiple of 16).
+constexpr int kMaxA2ASegs = 128;
+struct A2ASegment {
+    int32_t local_row, remote_row, rows, buf;
+};
+struct A2ALaunch {
+    void* remote[COC_MAX_WORLD];
+    void* local;
+    int64_t row_bytes;
+    int32_t to_remote;
+    int32_t nchunks;
+    int64_t row0[COC_MAX_SPLIT], rows[COC_MAX_SPLIT];
+    int32_t seg0[COC_MAX_SPLIT + 1];
+    A2ASegment seg[kMaxA2ASegs];
+    uint32_t* ready;            // dispatch: counter lines as above
+    const uint32_t* done;       // combine: counter lines as above
+    uint32_t target[COC_MAX_SPLIT];
+    uint32_t spin_limit;        // polls before a wait gives up (0: the default, about 2 s)
+};
+
 // Launchers (kernels.hip).  Return a hipError_t value (0 = success).  The
 // caller guarantees that every size and pointer has been validated.
 int launch_gemm(const GemmLaunch& g, void* stream);
@@ -174,6 +203,11 @@ int launch_gather(const GatherLaunch& g, void* stream, int32_t* groups = nullptr
 // lines).  *per_chunk receives the workgroups per chunk (the adds each gets).
 int launch_gather_chunks(const GatherLaunch& g, int nchunks, const int64_t* row0, const int64_t* rows,
                          uint32_t* ready, void* stream, int32_t* per_chunk);
+
+// The all-to-all copy above in one launch.  Dispatch: *per_chunk receives
+// the workgroups per chunk (the adds each chunk's ready lines get).  Combine:
+// at most one workgroup per CU, walking the chunks in order.
+int launch_a2a_chunks(const A2ALaunch& a, void* stream, int32_t* per_chunk);
 
 // Whether the ring kernels take this matmul (bf16 / fp16 with k a positive
 // multiple of 32; w8a16 also needs n % 16 == 0 and, per group, group % 32 == 0

@@ -1163,8 +1163,9 @@ struct FusedGather {
 };
 
 struct PersistParams {
-    GemmParams g;   // b, c, n, k, tiles_n (a and the row map fields unused)
+    GemmParams g;   // c, n, k, tiles_n (a, b and the row map fields unused)
     const uint8_t* a[kMaxPieces];
+    const uint8_t* b[kMaxPieces];   // per piece: one expert's weights in a grouped matmul
     int64_t ashift[kMaxPieces], base[kMaxPieces], stride[kMaxPieces];
     int32_t rpb[kMaxPieces], rows[kMaxPieces], tiles_m[kMaxPieces];
     int32_t wait[kMaxPieces], signal[kMaxPieces];
@@ -1243,6 +1244,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P
         block_barrier();
         GemmParams g = P.g;
         g.a = P.a[c];
+        g.b = P.b[c];
         ring_tile<BM, BN, S, WM, WN, KIND, SIGNAL, TA, TB>(g, P.rows[c], P.rpb[c], P.base[c], P.stride[c], P.ashift[c],
                                                    tm * BM, tn * BN, sm, wi >= 0 && !ok);
         if constexpr (SIGNAL) {
@@ -1540,6 +1542,112 @@ __global__ __launch_bounds__(256) void gather_chunks(GatherParams p, GatherChunk
     wg_signal(C.ready + (c * kReadyLines + lb % kReadyLines) * kSyncWords);
 }
 
+// ------------------------------------------------------------------ all-to-all
+// The copy of an expert all-to-all (see A2ALaunch): local rows of chunk c are
+// consecutive, each segment pairing a run of them with rows of one remote
+// buffer.  A thread's vectors only move forward through a chunk, so its
+// segment is found by walking the chunk's list forward from the last one.
+struct A2AParams {
+    uint8_t* remote[COC_MAX_WORLD];
+    uint8_t* local;
+    int64_t row_bytes;
+    int32_t vpr, nchunks, per_chunk;
+    int32_t row0[COC_MAX_SPLIT], total[COC_MAX_SPLIT];   // first local row; rows * vpr
+    int32_t seg0[COC_MAX_SPLIT + 1];
+    const uint32_t* done;
+    uint32_t target[COC_MAX_SPLIT];
+    uint32_t spin_limit;
+    uint32_t* ready;
+    A2ASegment seg[kMaxA2ASegs];
+};
+
+// The segment of chunk c holding local row lr, searching from segment s.  p
+// must be the kernel argument itself (the table is read from the argument
+// segment, not copied).
+__device__ __forceinline__ int a2a_segment(const A2AParams& p, int c, int s, int lr) {
+    while (s + 1 < p.seg0[c + 1] && lr >= p.seg[s].local_row + p.seg[s].rows) ++s;
+    return s;
+}
+
+__device__ __forceinline__ int64_t a2a_remote_off(const A2AParams& p, int s, int lr, int cv) {
+    return (int64_t)(p.seg[s].remote_row + (lr - p.seg[s].local_row)) * p.row_bytes + (int64_t)cv * 16;
+}
+
+// Dispatch: workgroups [c * per_chunk, (c + 1) * per_chunk) copy chunk c's
+// rows from the sources into the received matrix, written through for the
+// matmul already running, then add 1 each to the chunk's ready lines.
+__global__ __launch_bounds__(256) void a2a_dispatch(A2AParams p) {
+    constexpr int U = 4;
+    const int c = blockIdx.x / p.per_chunk, lb = blockIdx.x % p.per_chunk;
+    const int total = p.total[c];
+    const int per = (total + p.per_chunk - 1) / p.per_chunk;
+    const int v_end = (lb + 1) * per < total ? (lb + 1) * per : total;
+    int s = p.seg0[c];
+    for (int v0 = lb * per + threadIdx.x; v0 < v_end; v0 += U * 256) {
+        u32x4 x[U];
+        uint32_t off[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * 256;
+            if (v < v_end) {
+                const int row = v / p.vpr, cv = v - row * p.vpr;
+                const int lr = p.row0[c] + row;
+                s = a2a_segment(p, c, s, lr);
+                x[u] = *(const u32x4*)(p.remote[p.seg[s].buf] + a2a_remote_off(p, s, lr, cv));
+                off[u] = (uint32_t)((int64_t)lr * p.row_bytes + (int64_t)cv * 16);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (v0 + u * 256 >= v_end) break;
+            store16_sys(sys_rsrc(p.local), off[u], x[u]);
+        }
+    }
+    wg_signal(p.ready + (c * kReadyLines + lb % kReadyLines) * kSyncWords);
+}
+
+// Combine: at most one workgroup per CU beside the matmul; chunk by chunk,
+// wait until the matmul has counted the chunk's tiles (if done is set), then
+// copy its rows of the matmul's output back to the sources (NaN if the wait
+// gave up).  The output is read at system scope: the matmul writes it through
+// while this kernel runs.
+__global__ __launch_bounds__(256) void a2a_combine(A2AParams p) {
+    constexpr int U = 4;
+    const int stride = gridDim.x * 256;
+    const u32x4 nan = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};   // NaN in every format
+    for (int c = 0; c < p.nchunks; ++c) {
+        bool ok = true;
+        if (p.done != nullptr) {
+            if (c > 0) __syncthreads();   // wg_wait's flag is reused
+            ok = wg_wait(p.done + c * kSyncWords, 1, p.target[c], p.spin_limit);
+        }
+        const int total = p.total[c];
+        int s = p.seg0[c];
+        for (int v0 = blockIdx.x * 256 + threadIdx.x; v0 < total; v0 += U * stride) {
+            u32x4 x[U];
+            int64_t off[U];
+            uint8_t* dst[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = v0 + u * stride;
+                if (v < total) {
+                    const int row = v / p.vpr, cv = v - row * p.vpr;
+                    const int lr = p.row0[c] + row;
+                    s = a2a_segment(p, c, s, lr);
+                    x[u] = load16_sys(p.local + (int64_t)lr * p.row_bytes + (int64_t)cv * 16);
+                    dst[u] = p.remote[p.seg[s].buf];
+                    off[u] = a2a_remote_off(p, s, lr, cv);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (v0 + u * stride >= total) break;
+                *(u32x4*)(dst[u] + off[u]) = ok ? x[u] : nan;
+            }
+        }
+    }
+}
+
 int grid_for(int64_t total_vec, int per_thread = 1) {
     const int64_t want = (total_vec + 256 * per_thread - 1) / (256 * per_thread);
     const int64_t cap = 256 * 8;
@@ -1770,6 +1878,47 @@ int launch_gather_chunks(const GatherLaunch& g, int nchunks, const int64_t* row0
     return e;
 }
 
+int launch_a2a_chunks(const A2ALaunch& a, void* stream, int32_t* per_chunk) {
+    *per_chunk = 0;
+    if (a.nchunks <= 0 || a.nchunks > COC_MAX_SPLIT || a.row_bytes <= 0 || a.row_bytes % 16 != 0)
+        return hipErrorInvalidValue;
+    A2AParams p{};
+    for (int i = 0; i < COC_MAX_WORLD; ++i) p.remote[i] = (uint8_t*)a.remote[i];
+    p.local = (uint8_t*)a.local;
+    p.row_bytes = a.row_bytes;
+    p.vpr = (int32_t)(a.row_bytes / 16);
+    p.nchunks = a.nchunks;
+    int64_t most = 0;
+    for (int c = 0; c < a.nchunks; ++c) {
+        p.row0[c] = (int32_t)a.row0[c];
+        p.total[c] = (int32_t)(a.rows[c] * p.vpr);
+        most = p.total[c] > most ? p.total[c] : most;
+    }
+    for (int c = 0; c <= a.nchunks; ++c) p.seg0[c] = a.seg0[c];
+    if (p.seg0[a.nchunks] > kMaxA2ASegs) return hipErrorInvalidValue;
+    for (int i = 0; i < p.seg0[a.nchunks]; ++i) p.seg[i] = a.seg[i];
+    p.done = a.done;
+    for (int c = 0; c < COC_MAX_SPLIT; ++c) p.target[c] = a.target[c];
+    p.spin_limit = a.spin_limit > 0 ? a.spin_limit : kSpinLimit;
+    p.ready = a.ready;
+    hipStream_t s = (hipStream_t)stream;
+    if (a.to_remote == 0) {
+        if (a.ready == nullptr) return hipErrorInvalidValue;
+        // as the all-gather copy: up to 2048 workgroups, each at least 4
+        // passes of 4 vectors per thread
+        const int64_t want = (most + 4 * 4 * 256 - 1) / (4 * 4 * 256);
+        const int64_t cap = 2048 / a.nchunks;
+        p.per_chunk = (int32_t)(want < cap ? (want > 0 ? want : 1) : cap);
+        hipLaunchKernelGGL(a2a_dispatch, dim3(p.per_chunk * a.nchunks), dim3(256), 0, s, p);
+        const hipError_t e = hipGetLastError();
+        if (e == hipSuccess) *per_chunk = p.per_chunk;
+        return e;
+    }
+    const int grid = grid_for(most, 4) < 256 ? grid_for(most, 4) : 256;   // at most one per CU
+    hipLaunchKernelGGL(a2a_combine, dim3(grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 bool chunks_supported(const GemmLaunch& g) {
     if (g.k < 32 || g.k % 32 != 0) return false;
     if (g.trans_b) return g.kind == GK_BF16 || g.kind == GK_F16;
@@ -1844,6 +1993,7 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     for (int c = 0; c < L.npieces; ++c) {
         const int64_t rows = L.rpb[c] * L.nblk[c];
         P.a[c] = (const uint8_t*)L.a[c];
+        P.b[c] = (const uint8_t*)(L.bp[c] != nullptr ? L.bp[c] : L.b);
         P.ashift[c] = L.ashift[c];
         P.base[c] = L.base[c];
         P.stride[c] = L.stride[c];
@@ -1901,6 +2051,8 @@ template <int KIND>
 hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* tiles) {
     if constexpr (KIND == GK_W8_F16) {
         if (L.trans_a || L.trans_b) return hipErrorInvalidValue;
+        for (int c = 0; c < L.npieces; ++c)
+            if (L.bp[c] != nullptr) return hipErrorInvalidValue;   // one weight, one scale table
         return launch_chunks_layout<KIND, false, false>(L, s, tiles);
     } else {
         if (L.trans_a && L.trans_b) return hipErrorInvalidValue;

@@ -117,3 +117,70 @@ def pow2_scales(wid, rank, shape, lo_exp=-6, hi_exp=-2):
 def peers_random(wid, world, rank, shape, sigma, dtype):
     """The other ranks' partials as random draws; entry ``rank`` is None."""
     return [None if r == rank else normal(wid, T_PEER, r, shape, sigma, dtype) for r in range(world)]
+
+
+# ------------------------------------------------------------------ MoE expert all-to-all
+# One expert-parallel rank of a MoE layer: every source rank of the group
+# routes each of its tokens to top-k distinct experts drawn uniformly (the
+# routing itself is input here, not part of the op), its tokens cut into
+# `pieces` equal sequence pieces.  Rows and weights are N(0,1) and N(0, 0.02^2).
+T_ROUTE, T_SEND, T_EXPERT_W = 5, 6, 7
+
+
+@dataclass(frozen=True)
+class MoeWorkload:
+    name: str
+    wid: int
+    dtype: str
+    world: int          # expert-parallel ranks
+    experts: int        # experts in all (world * local)
+    topk: int
+    tokens: int         # tokens per source rank
+    hidden: int         # k of the first matmul, n of the second
+    ffn: int            # n of the first matmul, k of the second
+    pieces: int
+    rank: int = 0
+    note: str = ""
+
+    @property
+    def local(self) -> int:
+        return self.experts // self.world
+
+
+MOE_WORKLOADS = {
+    "moe_small": MoeWorkload("moe_small", 20, "bf16", 2, 4, 2, 512, 256, 384, 2, rank=1,
+                             note="small case of the Ampipe scenario's routing (4 experts, top 2, EP 2)"),
+    "moe_ragged": MoeWorkload("moe_ragged", 21, "f16", 8, 16, 2, 300, 128, 224, 4, rank=5,
+                              note="EP 8, 2 local experts, ragged groups"),
+    "moe_ampipe": MoeWorkload("moe_ampipe", 22, "bf16", 2, 4, 2, 8192, 12288, 49152, 2, rank=0,
+                              note="Ampipe page scenario: hidden 12288, 4 experts, top 2, EP 2; "
+                                   "sequence 128k over CP 2 and TP 8 (sequence parallel): 8192 tokens "
+                                   "per rank; ffn 4 x hidden; Ampipe degree 2"),
+}
+
+
+def moe_counts(wl: MoeWorkload) -> np.ndarray:
+    """counts[p][r][e]: rows source r routes to local expert e of rank wl.rank
+    in sequence piece p (pieces: equal runs of the source's tokens)."""
+    local = wl.local
+    counts = np.zeros((wl.pieces, wl.world, local), dtype=np.int64)
+    bounds = [wl.tokens * p // wl.pieces for p in range(wl.pieces + 1)]
+    for r in range(wl.world):
+        g = rng_for(wl.wid, T_ROUTE, r)
+        choice = np.argsort(g.random((wl.tokens, wl.experts)), axis=1)[:, :wl.topk]
+        for p in range(wl.pieces):
+            sel = choice[bounds[p]:bounds[p + 1]].ravel() - wl.rank * local
+            sel = sel[(sel >= 0) & (sel < local)]
+            counts[p, r] = np.bincount(sel, minlength=local)
+    return counts
+
+
+def moe_sends(wl: MoeWorkload, counts: np.ndarray, width: int):
+    """Each source's rows for this rank (rows x width, N(0,1)), CPU tensors."""
+    return [normal(wl.wid, T_SEND, r, (int(counts[:, r, :].sum()), width), 1.0, wl.dtype)
+            for r in range(wl.world)]
+
+
+def moe_weights(wl: MoeWorkload, k: int, n: int, which: int = 0):
+    """The local experts' weights, local x k x n, N(0, 0.02^2) (CPU tensor)."""
+    return normal(wl.wid, T_EXPERT_W, which, (wl.local, k, n), 0.02, wl.dtype)

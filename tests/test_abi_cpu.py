@@ -259,3 +259,69 @@ def test_weight_grad_rejects():
     assert call(g=None) == 1
     assert call(dw=_addr(1) + 16) == 9   # dw overlaps g
     assert call(dy=_addr(2) * 16 + 8) == 6
+
+
+def _moe_counts(split, world, experts, value=3):
+    import numpy as np
+    c = np.full((split, world, experts), value, dtype=np.int64)
+    return c
+
+
+def test_expert_alltoall_rejects():
+    """Argument checks of the MoE all-to-all entry points: each fails on the
+    host, before anything is enqueued (no GPU needed)."""
+    import numpy as np
+    L = tgc.lib()
+
+    def arr(c):
+        c = np.asarray(c, dtype=np.int64)
+        return (ctypes.c_int64 * max(c.size, 1))(*c.ravel().tolist())
+
+    def dispatch(counts=None, world=2, rank=0, experts=2, split=2, n=32, k=64, dt=tgc.COC_BF16,
+                 x_own=_addr(1), peers=None, w=_addr(3), y=_addr(4), recv=_addr(5), null_counts=False):
+        c = _moe_counts(split, world, experts) if counts is None else counts
+        peers = _peers(world, rank) if peers is None else peers
+        return L.coc_alltoall_grouped_matmul(x_own, peers, None if null_counts else arr(c), w, y, recv,
+                                             world, rank, experts, n, k, dt, split, None)
+
+    def combine(counts=None, world=2, rank=0, experts=2, split=2, n=32, k=64, dt=tgc.COC_BF16,
+                h=_addr(1), w=_addr(3), y_local=_addr(4), y_own=_addr(5), peers=None):
+        c = _moe_counts(split, world, experts) if counts is None else counts
+        peers = _peers(world, rank) if peers is None else peers
+        return L.coc_grouped_matmul_alltoall(h, w, y_local, y_own, peers, arr(c), world, rank, experts,
+                                             n, k, dt, split, None)
+
+    assert dispatch(dt=tgc.COC_F32) == 5
+    assert dispatch(k=48) == 3 and dispatch(n=12) == 3 and dispatch(k=0) == 3
+    assert dispatch(split=0, counts=_moe_counts(1, 2, 2)) == 2
+    assert dispatch(split=9, counts=_moe_counts(9, 2, 2)) == 2
+    assert dispatch(world=9, counts=_moe_counts(2, 9, 2)) == 4
+    assert dispatch(rank=2) == 4
+    assert dispatch(experts=0, counts=_moe_counts(2, 2, 1)) == 3
+    assert dispatch(experts=17, counts=_moe_counts(1, 2, 17), split=1) == 3
+    bad = _moe_counts(2, 2, 2)
+    bad[1, 1, 0] = -1
+    assert dispatch(counts=bad) == 3
+    assert dispatch(null_counts=True) == 1
+    assert dispatch(x_own=None) == 1
+    nopeer = _peers(2, 0)
+    nopeer[1] = None
+    assert dispatch(peers=nopeer) == 1
+    # a source with no rows may pass NULL
+    empty_src = _moe_counts(2, 2, 2)
+    empty_src[:, 1, :] = 0
+    assert dispatch(peers=nopeer, counts=empty_src, y=_addr(4) + 8) == 6   # fails later, on alignment
+    assert dispatch(y=_addr(4) + 8) == 6
+    assert dispatch(recv=_addr(4) + 16) == 9          # recv overlaps y
+    assert dispatch(y=_addr(1) + 16) == 9             # y overlaps x_own
+    # 8 pieces x 3 experts: 24 non-empty groups, more than a launch takes
+    assert dispatch(split=8, experts=3, counts=_moe_counts(8, 2, 3)) == 3
+    # nothing routed here: nothing to do, nothing touched
+    assert dispatch(counts=_moe_counts(2, 2, 2, value=0), x_own=None, y=None, recv=None, w=None) == 0
+
+    assert combine(dt=tgc.COC_F16, k=40) == 3
+    assert combine(y_own=None) == 1
+    assert combine(peers=nopeer) == 1
+    assert combine(y_own=_addr(1) + 16) == 9          # y_own overlaps h
+    assert combine(y_local=_addr(20 + 1) * 64) == 9   # y_local overlaps peer_out[1]
+    assert combine(counts=_moe_counts(2, 2, 2, value=0), h=None, w=None, y_local=None, y_own=None) == 0
