@@ -228,6 +228,86 @@ def run_configs(torch, tgc, synth, dev, iters=10):
          timeit(lambda: torch.matmul(g.t(), dy)))
 
 
+def run_moe(torch, tgc, synth, dev, iters=10, prewarm_s=0.5):
+    """The MoE expert all-to-all + grouped matmul pair on the Ampipe page's
+    scenario (hidden 12288, ffn 49152, 8192 tokens per rank, 4 experts, top 2,
+    EP 2; rank 0's share) at 1, 2 and 4 sequence pieces: dispatch then the
+    first expert matmul, the second expert matmul then combine.  Rows and
+    weights come from a seeded GPU generator (2.4 GB of weights per matmul).
+    One JSON line per case on stderr; the GEMM-only comparator is one
+    torch.matmul (hipBLASLt) per expert over its rows."""
+    import dataclasses
+
+    import numpy as np
+    wl0 = synth.MOE_WORKLOADS["moe_ampipe"]
+    g = torch.Generator(device=dev).manual_seed(wl0.wid)
+    bf = torch.bfloat16
+    k1, n1 = wl0.hidden, wl0.ffn
+    w1 = (torch.randn(wl0.local, k1, n1, device=dev, generator=g) * 0.02).to(bf)
+    w2 = (torch.randn(wl0.local, n1, k1, device=dev, generator=g) * 0.02).to(bf)
+
+    def timeit(fn, warm=2):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    first = True
+    for pieces in (1, 2, 4):
+        wl = dataclasses.replace(wl0, pieces=pieces)
+        counts = synth.moe_counts(wl)
+        total = int(counts.sum())
+        rows = counts.sum(axis=(0, 2))
+        sends = [torch.randn(int(rows[r]), k1, device=dev, generator=g).to(bf) for r in range(wl.world)]
+        peers = [None if r == wl.rank else sends[r] for r in range(wl.world)]
+        y1 = torch.empty(total, n1, dtype=bf, device=dev)
+        recv = torch.empty(total, k1, dtype=bf, device=dev)
+        y2 = torch.empty(total, k1, dtype=bf, device=dev)
+        outs = [torch.empty(int(rows[r]), k1, dtype=bf, device=dev) for r in range(wl.world)]
+        po = [None if r == wl.rank else outs[r] for r in range(wl.world)]
+
+        def dispatch():
+            tgc.alltoall_grouped_matmul(sends[wl.rank], peers, counts, w1, wl.rank, y=y1, recv_out=recv)
+
+        def combine():
+            tgc.grouped_matmul_alltoall(y1, w2, counts, wl.rank, y_own=outs[wl.rank], peer_out=po, y_local=y2)
+
+        if first and prewarm_s > 0:
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < prewarm_s:
+                dispatch()
+                torch.cuda.synchronize()
+            first = False
+        per_expert = counts.sum(axis=(0, 1))
+        ref1 = ref2 = None
+        if pieces == 1:
+            # one matmul per expert over all its rows (the received order groups them)
+            starts = np.concatenate([[0], np.cumsum(per_expert)])
+            a1 = [recv[starts[e]:starts[e + 1]] for e in range(wl.local)]
+            a2 = [y1[starts[e]:starts[e + 1]] for e in range(wl.local)]
+            dispatch()
+            ref1 = timeit(lambda: [torch.matmul(a1[e], w1[e]) for e in range(wl.local)])
+            ref2 = timeit(lambda: [torch.matmul(a2[e], w2[e]) for e in range(wl.local)])
+        flops = 2.0 * total * k1 * n1
+        for name, fn, ref in (("dispatch + expert matmul 1", dispatch, ref1),
+                              ("expert matmul 2 + combine", combine, ref2)):
+            ms = timeit(fn)
+            line = {"case": f"moe_ampipe {name} pieces{pieces}", "rows": total, "ms": round(ms, 5),
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                    "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+            if ref is not None:
+                line["hipblaslt_gemm_only_ms"] = round(ref, 5)
+            print(json.dumps(line), file=sys.stderr, flush=True)
+        del sends, peers, y1, recv, y2, outs, po
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +323,9 @@ def main():
                     help="skip the per-op and serial timings after the timed region (profiling runs)")
     ap.add_argument("--configs", action="store_true",
                     help="after the main line, time every workload at its configured splits (stderr)")
+    ap.add_argument("--moe", action="store_true",
+                    help="only time the MoE expert all-to-all + grouped matmul pair on the Ampipe "
+                         "scenario (stderr lines) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) three "
                          "times, for scaling the HBM byte counters, and exit")
@@ -275,6 +358,9 @@ def main():
                           "bytes_written_per_launch": 4 * n, "launches": 3}), flush=True)
         return
     tgc.lib()
+    if args.moe:
+        run_moe(torch, tgc, synth, dev, prewarm_s=args.prewarm_s)
+        return
     log("generating inputs ...")
     inp = make_inputs(torch, tgc, synth, args.split, dev)
     torch.cuda.synchronize()
@@ -441,6 +527,7 @@ def main():
         del inp
         torch.cuda.empty_cache()
         run_configs(torch, tgc, synth, dev)
+        run_moe(torch, tgc, synth, dev, prewarm_s=0)
 
 
 if __name__ == "__main__":
