@@ -736,6 +736,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
 //   * Fragment reads go 2 per MFMA from the first MFMA of a phase; the DMA
 //     instructions are spread evenly over phase 2.  sched_barrier fixes that
 //     order against the compiler's scheduler.
+//   * Phase 2 runs at wave priority 1 and phase 1 at 0.  The two waves on a
+//     SIMD drift apart by up to a phase; the barrier then waits for the one
+//     still in phase 2, which the priority lets issue first.  Measured with a
+//     shader-cycle counter around the phases: 1229 -> 1153 cycles per stage
+//     on a 256 x 256 tile, the barrier wait 268 -> 178.
 //   * The k walk (16-k MFMA steps in increasing k, same operand roles) is the
 //     one every other kernel here uses, so results are bitwise identical to
 //     theirs.
@@ -1012,6 +1017,10 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             }
             deq(0);
         }
+        // Phase 1 at the low wave priority: a wave that is still in phase 2
+        // while the other wave on its SIMD has moved on is the one the
+        // barrier waits for, so it issues first.
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < NMM; ++s) {
@@ -1023,6 +1032,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             wait_vmcnt<decltype(WAITN)::value>();
             block_barrier();
         }
+        __builtin_amdgcn_s_setprio(1);
         if constexpr (W8) deq(1);
         __builtin_amdgcn_sched_barrier(0);
         const int nslot = (kt + 1) % S, dslot = (kt + S - 1) % S;
@@ -1044,6 +1054,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     for (; kt + S - 1 < KT; ++kt) stage(kt, yes{}, yes{}, std::integral_constant<int, (S - 3) * DPW>{});
     for (; kt + 1 < KT; ++kt) stage(kt, no{}, yes{}, std::integral_constant<int, 0>{});
     stage(kt, no{}, no{}, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_s_setprio(0);
 
     if (poison) {
 #pragma unroll
