@@ -13,6 +13,7 @@ sums are seeded buffers in the same HBM.  Prints one JSON line on stdout
 steady clocks; the JSON line reports them under "prewarm".
 
     python bench.py [--steps K] [--warmup W] [--split S] [--prewarm-s T] [--no-cpu-baseline]
+                    [--operands constant]   (clock diagnostic, not a benchmark figure)
 """
 import argparse
 import json
@@ -326,6 +327,10 @@ def main():
     ap.add_argument("--moe", action="store_true",
                     help="only time the MoE expert all-to-all + grouped matmul pair on the Ampipe "
                          "scenario (stderr lines) and exit")
+    ap.add_argument("--operands", choices=["seeded", "constant"], default="seeded",
+                    help="constant: every matmul operand of the step holds one value (same kernels, same "
+                         "work) -- a diagnostic of the clock the GPU sustains when the MFMA inputs do not "
+                         "toggle; its line is marked as such and is not a benchmark figure")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) three "
                          "times, for scaling the HBM byte counters, and exit")
@@ -363,6 +368,21 @@ def main():
         return
     log("generating inputs ...")
     inp = make_inputs(torch, tgc, synth, args.split, dev)
+    if args.operands == "constant":
+        # 2^-4 activations, 2^-6 weights: every product is exact and every sum
+        # stays far inside bf16's range (k * 2^-10 <= 8)
+        for key in ("ag_x", "rs_x"):
+            inp[key].fill_(0.0625)
+        for t in inp["ag_peers"]:
+            if t is not None:
+                t.fill_(0.0625)
+        for key in ("ag_w", "rs_w"):
+            inp[key].fill_(0.015625)
+        b = inp["rs"].m // inp["world"]
+        for t in inp["rs_peers"]:
+            if t is not None:
+                t[inp["rank"] * b:(inp["rank"] + 1) * b].fill_(1.0)
+        args.no_cpu_baseline = True
     torch.cuda.synchronize()
     f_ag, f_rs = flops_of(inp)
     rank, split = inp["rank"], args.split
@@ -485,7 +505,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, emulated peer shards/partials)",
+        "data": ("synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, emulated peer shards/partials)"
+                 if args.operands == "seeded" else
+                 "DIAGNOSTIC, not a benchmark figure: every matmul operand constant (clock under MFMA load "
+                 "without operand toggling)"),
         "config": {
             "workload": "LLaMA2-70B TP8+SP MLP, one rank: ALL_GATHER_MATMUL 8x(512x8192) @ 8192x7168 "
                         "then MATMUL_REDUCE_SCATTER 4096x3584 @ 3584x8192 -> 512x8192",
