@@ -42,6 +42,17 @@
  *     device the library runs them one after another even when they come
  *     from different streams: such a call waits on its stream for the
  *     previous one (unless the stream is being captured into a graph).
+ *   - Graph capture: the matmul/collective ops may be captured into a HIP
+ *     graph and replayed.  A captured call takes the per-chunk event
+ *     pipeline (separate matmul, reduce and gather launches joined by
+ *     events), because the one-launch pipelines hand chunks over through
+ *     device counters whose targets the host advances call by call and a
+ *     replay would repeat.  The first call on a stream creates the
+ *     library's side streams and counters for it and synchronises the
+ *     device, so it must not be captured: call once on the stream before
+ *     capturing it (COC_ERR_CAPTURE otherwise).  The MoE all-to-all pair
+ *     works only through those counters and returns COC_ERR_CAPTURE under
+ *     capture.  Replays of one graph must not overlap each other.
  *   - `split` is the number of m-chunks the work is pipelined over: 1
  *     (serial, no overlap), 2, 4 or 8 (CoC guide, "Usage": the split count
  *     options; the m dimension must divide by it, CoC guide "Approach" and
@@ -114,7 +125,8 @@ typedef enum coc_status {
     COC_ERR_ALIGN = 6,      /* a device pointer is not 16-byte aligned         */
     COC_ERR_WORKSPACE = 7,  /* workspace missing or too small                  */
     COC_ERR_HIP = 8,        /* the HIP runtime reported an error               */
-    COC_ERR_ALIAS = 9       /* an output overlaps an input or another output   */
+    COC_ERR_ALIAS = 9,      /* an output overlaps an input or another output   */
+    COC_ERR_CAPTURE = 10    /* not possible while the stream is captured        */
 } coc_status;
 
 typedef enum coc_op {

@@ -25,7 +25,7 @@ OP_MATMUL_ALL_REDUCE_W8A16 = 4
 STATUS = {
     0: "COC_OK", 1: "COC_ERR_NULL", 2: "COC_ERR_SPLIT", 3: "COC_ERR_SHAPE", 4: "COC_ERR_WORLD",
     5: "COC_ERR_DTYPE", 6: "COC_ERR_ALIGN", 7: "COC_ERR_WORKSPACE", 8: "COC_ERR_HIP",
-    9: "COC_ERR_ALIAS",
+    9: "COC_ERR_ALIAS", 10: "COC_ERR_CAPTURE",
 }
 QUANT_MODES = {"per_tensor": COC_PER_TENSOR, "per_channel": COC_PER_CHANNEL, "per_group": COC_PER_GROUP}
 KCLASS = ("gemm", "reduce", "gather")

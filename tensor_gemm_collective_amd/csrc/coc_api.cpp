@@ -104,6 +104,17 @@ struct StreamCtx {
 std::mutex g_ctx_mu;
 std::map<std::pair<int, hipStream_t>, StreamCtx*> g_ctx;
 
+// Whether `s` is being captured into a graph.  The one-launch pipelines hand
+// chunks over through device counters whose targets the host advances call by
+// call; a replayed graph would repeat the captured targets, so captured calls
+// take the per-chunk event pipelines instead.
+coc_status capturing(hipStream_t s, bool* out) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    COC_HIP(hipStreamIsCapturing(s, &cs));
+    *out = cs != hipStreamCaptureStatusNone;
+    return COC_OK;
+}
+
 coc_status get_ctx(hipStream_t main, StreamCtx** out) {
     int dev = 0;
     COC_HIP(hipGetDevice(&dev));
@@ -114,6 +125,12 @@ coc_status get_ctx(hipStream_t main, StreamCtx** out) {
         *out = it->second;
         return COC_OK;
     }
+    bool cap = false;
+    COC_TRY(capturing(main, &cap));
+    if (cap)
+        return fail(COC_ERR_CAPTURE, "the first call on a stream sets up its side streams and counters (with a "
+                                     "device synchronisation) and cannot be captured: call once on this stream "
+                                     "before capturing it");
     StreamCtx* c = new StreamCtx;
     COC_HIP(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
     COC_HIP(hipStreamCreateWithFlags(&c->gemm2, hipStreamNonBlocking));
@@ -519,7 +536,9 @@ coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLa
         COC_TRY(gemm(0, main));
         return reduce(0, main);
     }
-    if (one_launch(P, g0)) return run_compute_first_chunks(P, g0, r0, main);
+    bool cap = false;
+    COC_TRY(capturing(main, &cap));
+    if (one_launch(P, g0) && !cap) return run_compute_first_chunks(P, g0, r0, main);
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
     COC_HIP(hipEventRecord(c->fork, main));
@@ -557,7 +576,9 @@ coc_status run_comm_first(const Plan& P, const GemmLaunch& g0, const GatherLaunc
         COC_TRY(gather(0, main));
         return gemm(0, main);
     }
-    if (one_launch_gather(P, g0)) return run_comm_first_chunks(P, g0, a0, main);
+    bool cap = false;
+    COC_TRY(capturing(main, &cap));
+    if (one_launch_gather(P, g0) && !cap) return run_comm_first_chunks(P, g0, a0, main);
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
     COC_HIP(hipEventRecord(c->fork, main));
@@ -792,6 +813,11 @@ A2ALaunch moe_a2a(const MoePlan& M, void* local, int64_t row_bytes) {
 // stream and the matmul after it (no overlap).
 coc_status run_moe_dispatch(const MoePlan& M, const void* const* src, const void* w, void* y, void* recv,
                             hipStream_t main) {
+    bool cap = false;
+    COC_TRY(capturing(main, &cap));
+    if (cap)
+        return fail(COC_ERR_CAPTURE, "the expert all-to-all hands sequence pieces over through device counters "
+                                     "and cannot be captured into a graph");
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
     ChainedCall chain;
@@ -833,6 +859,11 @@ coc_status run_moe_dispatch(const MoePlan& M, const void* const* src, const void
 // complete.
 coc_status run_moe_combine(const MoePlan& M, const void* h, const void* w, void* y_local, void* const* dst,
                            hipStream_t main) {
+    bool cap = false;
+    COC_TRY(capturing(main, &cap));
+    if (cap)
+        return fail(COC_ERR_CAPTURE, "the expert all-to-all hands sequence pieces over through device counters "
+                                     "and cannot be captured into a graph");
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
     ChainedCall chain;

@@ -186,6 +186,7 @@ const char* coc_status_string(coc_status s) {
         case COC_ERR_WORKSPACE: return "COC_ERR_WORKSPACE";
         case COC_ERR_HIP: return "COC_ERR_HIP";
         case COC_ERR_ALIAS: return "COC_ERR_ALIAS";
+        case COC_ERR_CAPTURE: return "COC_ERR_CAPTURE";
     }
     return "COC_ERR_UNKNOWN";
 }
