@@ -467,6 +467,27 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / iters
 
+    def time_cold(fn, iters=20):
+        """Per-call times with the caches cold: before each call a 512 MB write
+        evicts the L2s and the 256 MB memory-side cache (outside the events).
+        Returns (median, p10, p90) in ms."""
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ts = []
+        for i in range(iters + 1):
+            flush.fill_(i & 0xff)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if i > 0:
+                ts.append(a.elapsed_time(b))
+        del flush
+        ts.sort()
+        q = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
+        return q(0.5), q(0.1), q(0.9)
+
+    cold = None
     if args.no_breakdown:
         ms_ag = ms_rs = ms_serial = float("nan")
     else:
@@ -476,6 +497,12 @@ def main():
         split = 1
         ms_serial = time_op(step)
         split = split_saved
+        cold = {"flush_bytes": 512 << 20, "iterations": 20}
+        for name, fn, fl in (("allgather_matmul", run_ag, f_ag), ("matmul_reduce_scatter", run_rs, f_rs),
+                             ("step", step, f_ag + f_rs)):
+            med, p10, p90 = time_cold(fn)
+            cold[name] = {"median_ms": round(med, 5), "p10_ms": round(p10, 5), "p90_ms": round(p90, 5),
+                          "tflops_median": round(fl / (med * 1e-3) / 1e12, 2)}
 
     value = (f_ag + f_rs) / (ms_step * 1e-3) / 1e12
     g = prof["gemm"]
@@ -519,6 +546,7 @@ def main():
             "allgather_matmul": {"ms": round(ms_ag, 5), "tflops": tf(f_ag, ms_ag)},
             "matmul_reduce_scatter": {"ms": round(ms_rs, 5), "tflops": tf(f_rs, ms_rs)},
             "serial_split1": {"ms": round(ms_serial, 5), "tflops": tf(f_ag + f_rs, ms_serial)},
+            "cold_cache": cold,
             "kernel_busy_ms_per_step": {k: round(v["busy_ms"] / args.steps, 5) for k, v in prof.items()},
             "kernel_launches_per_step": {k: v["launches"] / args.steps for k, v in prof.items()},
             "reduce_gbs": gbs(prof["reduce"]),
