@@ -96,6 +96,65 @@ def make_inputs(torch, tgc, synth, split, dev):
     return inp
 
 
+def sample_clock(step, torch, seconds=1.0, period=0.005):
+    """GFX clock and socket power sampled through amdsmi every `period` s while
+    steps run back to back for `seconds` s; None when amdsmi is unavailable."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+        limit = amdsmi.amdsmi_get_power_info(h).get("power_limit")
+    except Exception as e:   # no amdsmi, or no access to the device's metrics
+        log(f"clock sampling unavailable: {e}")
+        return None
+    clk, pw, stop = [], [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk")
+                p = amdsmi.amdsmi_get_power_info(h).get("current_socket_power")
+            except Exception:
+                break
+            if isinstance(c, (int, float)):
+                clk.append(c)
+            if isinstance(p, (int, float)):
+                pw.append(p)
+            time.sleep(period)
+
+    for _ in range(100):   # reach the load's clock before sampling
+        step()
+    torch.cuda.synchronize()
+    t = threading.Thread(target=sampler)
+    t.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    t.join()
+    if not clk:
+        return None
+    mean = sum(clk) / len(clk)
+    out = {"source": f"amdsmi GFX clock every {period * 1e3:g} ms while steps run back to back for "
+                     f"{seconds:g} s after the timed region",
+           "samples": len(clk), "mhz_mean": round(mean, 1), "mhz_min": min(clk), "mhz_max": max(clk),
+           "mhz_rated_max": info.get("max_clk"),
+           "bf16_peak_at_mean_clock_tflops": round(256 * 4096 * mean * 1e6 / 1e12, 1)}
+    if pw:
+        out["socket_power_w_mean"] = round(sum(pw) / len(pw), 1)
+    if isinstance(limit, (int, float)) and limit > 0:
+        out["power_limit_w"] = round(limit / 1e6, 1)
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    return out
+
+
 def flops_of(inp):
     ag, rs = inp["ag"], inp["rs"]
     return 2.0 * ag.m * ag.n * ag.k, 2.0 * rs.m * rs.n * rs.k
@@ -504,6 +563,9 @@ def main():
             cold[name] = {"median_ms": round(med, 5), "p10_ms": round(p10, 5), "p90_ms": round(p90, 5),
                           "tflops_median": round(fl / (med * 1e-3) / 1e12, 2)}
 
+    # ---- the GPU clock under this load (after everything above is measured)
+    clock = None if args.no_breakdown else sample_clock(step, torch)
+
     value = (f_ag + f_rs) / (ms_step * 1e-3) / 1e12
     g = prof["gemm"]
     avg_ms = g["ms"] / max(1, g["launches"])
@@ -563,6 +625,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(),
+            "gpu_clock": clock,
+            "frac_of_peak_at_measured_clock": (round(achieved / clock["bf16_peak_at_mean_clock_tflops"], 4)
+                                               if clock else None),
             "avg_launch_us": round(avg_ms * 1e3, 3),
             "launches_per_step": g["launches"] / args.steps,
             "flops_per_launch": flops_per_launch,
