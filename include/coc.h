@@ -52,7 +52,9 @@
  *     device, so it must not be captured: call once on the stream before
  *     capturing it (COC_ERR_CAPTURE otherwise).  The MoE all-to-all pair
  *     works only through those counters and returns COC_ERR_CAPTURE under
- *     capture.  Replays of one graph must not overlap each other.
+ *     capture.  Replays of one graph must not overlap each other.  Each op
+ *     is tested captured into a graph of its own; graphs holding several of
+ *     these calls are not tested.
  *   - `split` is the number of m-chunks the work is pipelined over: 1
  *     (serial, no overlap), 2, 4 or 8 (CoC guide, "Usage": the split count
  *     options; the m dimension must divide by it, CoC guide "Approach" and
