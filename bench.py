@@ -96,10 +96,11 @@ def make_inputs(torch, tgc, synth, split, dev):
     return inp
 
 
-def sample_clock(step, torch, seconds=1.0, period=0.005):
-    """GFX clock and socket power sampled through amdsmi every `period` s while
-    steps run back to back for `seconds` s; None when amdsmi is unavailable."""
-    import threading
+def sample_clock(step, torch, seconds=1.0, batch=40, per_batch=5, period=0.003):
+    """GFX clock and socket power read through amdsmi while steps run back to back for
+    `seconds` s: each round queues `batch` steps (tens of ms of GPU work), reads the
+    clock `per_batch` times `period` s apart while the GPU works through them, then
+    synchronises.  One thread throughout.  None when amdsmi is unavailable."""
     try:
         import amdsmi
         amdsmi.amdsmi_init()
@@ -109,49 +110,40 @@ def sample_clock(step, torch, seconds=1.0, period=0.005):
     except Exception as e:   # no amdsmi, or no access to the device's metrics
         log(f"clock sampling unavailable: {e}")
         return None
-    clk, pw, stop = [], [], threading.Event()
-
-    def sampler():
-        while not stop.is_set():
-            try:
-                c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk")
-                p = amdsmi.amdsmi_get_power_info(h).get("current_socket_power")
-            except Exception:
-                break
+    clk, pw = [], []
+    for _ in range(100):   # reach the load's clock before sampling
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            step()
+        for _ in range(per_batch):
+            time.sleep(period)
+            c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk")
+            p = amdsmi.amdsmi_get_power_info(h).get("current_socket_power")
             if isinstance(c, (int, float)):
                 clk.append(c)
             if isinstance(p, (int, float)):
                 pw.append(p)
-            time.sleep(period)
-
-    for _ in range(100):   # reach the load's clock before sampling
-        step()
-    torch.cuda.synchronize()
-    t = threading.Thread(target=sampler)
-    t.start()
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        for _ in range(20):
-            step()
         torch.cuda.synchronize()
-    stop.set()
-    t.join()
-    if not clk:
-        return None
-    mean = sum(clk) / len(clk)
-    out = {"source": f"amdsmi GFX clock every {period * 1e3:g} ms while steps run back to back for "
-                     f"{seconds:g} s after the timed region",
-           "samples": len(clk), "mhz_mean": round(mean, 1), "mhz_min": min(clk), "mhz_max": max(clk),
-           "mhz_rated_max": info.get("max_clk"),
-           "bf16_peak_at_mean_clock_tflops": round(256 * 4096 * mean * 1e6 / 1e12, 1)}
-    if pw:
-        out["socket_power_w_mean"] = round(sum(pw) / len(pw), 1)
-    if isinstance(limit, (int, float)) and limit > 0:
-        out["power_limit_w"] = round(limit / 1e6, 1)
     try:
         amdsmi.amdsmi_shut_down()
     except Exception:
         pass
+    if not clk:
+        return None
+    mean = sum(clk) / len(clk)
+    med = sorted(clk)[len(clk) // 2]   # robust to a read that catches the GPU between kernels
+    out = {"source": f"amdsmi GFX clock, {per_batch} reads {period * 1e3:g} ms apart while each batch of "
+                     f"{batch} queued steps runs, for {seconds:g} s after the timed region",
+           "samples": len(clk), "mhz_median": med, "mhz_mean": round(mean, 1), "mhz_min": min(clk),
+           "mhz_max": max(clk), "mhz_rated_max": info.get("max_clk"),
+           "bf16_peak_at_median_clock_tflops": round(256 * 4096 * med * 1e6 / 1e12, 1)}
+    if pw:
+        out["socket_power_w_mean"] = round(sum(pw) / len(pw), 1)
+    if isinstance(limit, (int, float)) and limit > 0:
+        out["power_limit_w"] = round(limit / 1e6, 1)
     return out
 
 
@@ -488,6 +480,7 @@ def main():
 
     # ---- the same K steps again with HIP events around every library launch
     # (recorded by the library on the stream each kernel goes to)
+    log("per-launch events pass ...")
     tgc.profile_enable(True)
     tgc.profile_records()
     torch.cuda.synchronize()
@@ -550,12 +543,14 @@ def main():
     if args.no_breakdown:
         ms_ag = ms_rs = ms_serial = float("nan")
     else:
+        log("per-op and serial timings ...")
         ms_ag = time_op(run_ag)
         ms_rs = time_op(run_rs)
         split_saved = split
         split = 1
         ms_serial = time_op(step)
         split = split_saved
+        log("cold-cache timings ...")
         cold = {"flush_bytes": 512 << 20, "iterations": 20}
         for name, fn, fl in (("allgather_matmul", run_ag, f_ag), ("matmul_reduce_scatter", run_rs, f_rs),
                              ("step", step, f_ag + f_rs)):
@@ -564,6 +559,8 @@ def main():
                           "tflops_median": round(fl / (med * 1e-3) / 1e12, 2)}
 
     # ---- the GPU clock under this load (after everything above is measured)
+    if not args.no_breakdown:
+        log("clock sampling ...")
     clock = None if args.no_breakdown else sample_clock(step, torch)
 
     value = (f_ag + f_rs) / (ms_step * 1e-3) / 1e12
@@ -626,7 +623,7 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(),
             "gpu_clock": clock,
-            "frac_of_peak_at_measured_clock": (round(achieved / clock["bf16_peak_at_mean_clock_tflops"], 4)
+            "frac_of_peak_at_measured_clock": (round(achieved / clock["bf16_peak_at_median_clock_tflops"], 4)
                                                if clock else None),
             "avg_launch_us": round(avg_ms * 1e3, 3),
             "launches_per_step": g["launches"] / args.steps,
