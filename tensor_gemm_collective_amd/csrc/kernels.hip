@@ -27,6 +27,12 @@
 // Build-time tuning knob (default: the measured best): the fewest workgroups
 // the chunk matmuls running side by side should have together before the
 // ring kernel moves to a larger tile.
+// Activations of two consecutive k stages staged together as whole 128-byte
+// row segments (bf16 / fp16, k % 64 == 0): measured 1.2-2.8 % faster on the
+// LLaMA2-70B shapes with random operands, bit-identical results.
+#ifndef COC_PAIR_A
+#define COC_PAIR_A 1
+#endif
 #ifndef COC_RING_MIN_TILES
 #define COC_RING_MIN_TILES 200
 #endif
@@ -475,6 +481,12 @@ __device__ __forceinline__ int gA(int r) {
     else return (r ^ (r >> 3)) & 7;
 }
 __device__ __forceinline__ int gB(int K) { return (K & 3) << 2; }
+// Paired activation stages (128-byte rows of 8 chunks): chunk c of row r at
+// c ^ gP(r).  A 16-lane group of a fragment read takes 16 consecutive rows at
+// one chunk; the 8 rows of each parity then land on 8 distinct 16-byte bank
+// groups.  The period, 16 rows, divides the 32 rows between a wave's
+// fragments, so one offset per lane serves every fragment.
+__device__ __forceinline__ int gP(int r) { return (r >> 1) & 7; }
 
 // DEV_SCOPE: device-scope load (sc1), which does not allocate in the
 // per-CU L1; each 16-byte chunk is read once per workgroup, so L1 caching buys
@@ -736,6 +748,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
 //   * Fragment reads go 2 per MFMA from the first MFMA of a phase; the DMA
 //     instructions are spread evenly over phase 2.  sched_barrier fixes that
 //     order against the compiler's scheduler.
+//   * With k % 64 == 0 (bf16 / fp16, plain operands) the activations of stages
+//     2j and 2j + 1 arrive together, whole 128-byte row segments, in one of
+//     two pair blocks; the weights keep their four 32-k slots.  The pair is
+//     loaded with the weights of stage 2j, in phase 2 of stage 2j - 3, which
+//     keeps the same two stages of load slack.  The fragments, and so the
+//     bits, are those of the 32-k layout.
 //   * Phase 2 runs at wave priority 1 and phase 1 at 0.  The two waves on a
 //     SIMD drift apart by up to a phase; the barrier then waits for the one
 //     still in phase 2, which the priority lets issue first.  Measured with a
@@ -766,7 +784,8 @@ constexpr int ring_lds_bytes() {
 // normally (rows of one k step's 64 bytes, or k rows read with the LDS
 // transpose), so both come out in the same MFMA fragments and the result
 // bits do not change.
-template <int BM, int BN, int S, int WM, int WN, int KIND, bool SYS = false, bool TA = false, bool TB = false>
+template <int BM, int BN, int S, int WM, int WN, int KIND, bool SYS = false, bool TA = false, bool TB = false,
+          bool PA = false>
 __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb, int64_t base, int64_t stride,
                                           int64_t ashift, int m0, int n0, uint8_t* sm, bool poison) {
     constexpr int BK = 32, NW = WM * WN;
@@ -790,6 +809,12 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     static_assert(!(W8 && (TA || TB)) && !(TA && TB), "transposed operands: bf16 / fp16, one at a time");
     static_assert(!TA || (AROW >= 16 && AROW <= 64), "activation swizzle");
     static_assert(S >= 3 && ring_lds_bytes<BM, BN, S, WM, WN, KIND>() <= 160 * 1024, "LDS ring");
+    // PA: the activations of two consecutive stages arrive together as whole
+    // 128-byte row segments (64 k) into a pair block; LDS holds S / 2 pair
+    // blocks (the A of S stages) and then S weight slots.  k % 64 == 0.
+    constexpr int A_REG = PA ? S * A_BYTES : 0;
+    constexpr int APW2 = 2 * APW;   // PA: load instructions per wave for an A pair
+    static_assert(!PA || (!W8 && !TA && !TB && S == 4), "paired activation stages: bf16 / fp16, 4 slots");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -826,6 +851,29 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
         // chunk) or c ^ (K & 7) (int8: 16 columns per chunk)
         const int col = W8 ? n0 + (((lane % BROW) ^ (K & 7)) << 4) : n0 + (((lane % BROW) ^ gB(K)) << 3);
         bof[i] = (uint32_t)K * (uint32_t)p.n * BE + (uint32_t)(col < p.n ? col : 0) * BE;
+    }
+    // PA: A pair loads, 8 lanes per 128-byte row segment; chunk c of row r at c ^ gP(r)
+    uint32_t aofp[PA ? APW2 : 1];
+    if constexpr (PA) {
+#pragma unroll
+        for (int i = 0; i < APW2; ++i) {
+            const int q = (wave * APW2 + i) * 64 + lane;
+            const int row = q >> 3;
+            const int r = m0 + row < rows ? m0 + row : rows - 1;
+            const int64_t gr = map_row(r, rpb, base, stride) + ashift;
+            aofp[i] = (uint32_t)(gr * p.k * 2) + (((q & 7) ^ gP(row)) << 4);
+        }
+    }
+    // PA: activation fragment offsets in a pair block, per stage half h
+    int ardp[PA ? 2 : 1][2];
+    if constexpr (PA) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int row = wm * WTM + (lane & 31);
+                ardp[h][ks] = row * 128 + (((h * 4 + ks * 2 + (lane >> 5)) ^ gP(row)) << 4);
+            }
     }
     // fragment offsets within a stage (the rest are immediates)
     int ard[2];
@@ -881,6 +929,13 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     const int KT = p.k / BK;   // >= 1 (the launcher sends k == 0 elsewhere)
     const int64_t astep = TA ? (int64_t)BK * p.lda * 2 : (int64_t)BK * 2;
     const int64_t bstep = TB ? (int64_t)BK * 2 : (int64_t)BK * p.n * BE;
+    // PA: weights of stage kt into slot `slot`; activations of stages kt, kt + 1 (kt even)
+    auto dma_b = [&](int d, int kt, int slot) {
+        dma16_sbase(bof[d], p.b + (int64_t)kt * bstep, lds0 + A_REG + slot * B_BYTES + (wave * BPW + d) * 1024);
+    };
+    auto dma_a2 = [&](int d, int kt, int slot) {
+        dma16_sbase(aofp[PA ? d : 0], p.a + (int64_t)kt * astep, lds0 + (slot >> 1) * 2 * A_BYTES + (wave * APW2 + d) * 1024);
+    };
     auto dma = [&](int d, int kt, int slot) {
         const uint32_t l = lds0 + slot * STAGE;
         if (d < APW)
@@ -892,8 +947,17 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     u32x2 bq[2][FN];   // w8: raw int8 weight fragments, dequantised right before use
     // fragment r of k step ks of a slot: weight fragments (two halves each, or
     // one int8 read each), then activation rows
-    auto rdf = [&](int r, int slot, int ks, int buf) {
-        const COC_LDS uint8_t* st = (const COC_LDS uint8_t*)sm + slot * STAGE;
+    // h: PA, the stage's half of its pair block (kt & 1, a constant at every call)
+    auto rdf = [&](int r, int slot, int ks, int buf, int h) {
+        // (PA: brd holds the weight offsets past an A_BYTES stage head)
+        const COC_LDS uint8_t* st = (const COC_LDS uint8_t*)sm + (PA ? A_REG + slot * B_BYTES - A_BYTES : slot * STAGE);
+        if constexpr (PA) {
+            if (r >= WRD * FN) {
+                af[buf][r - WRD * FN] = *(const COC_LDS u32x4*)((const COC_LDS uint8_t*)sm + (slot >> 1) * 2 * A_BYTES +
+                                                              ardp[h][ks] + (r - WRD * FN) * 32 * 128);
+                return;
+            }
+        }
         if constexpr (W8) {
             if (r < FN) {
                 bq[buf][r] = __builtin_bit_cast(
@@ -925,14 +989,24 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             af[buf][r - WRD * FN] = *(const COC_LDS u32x4*)(st + ard[ks] + (r - WRD * FN) * 32 * BK * 2);
         }
     };
-    auto reads_at = [&](int s, int slot, int ks, int buf) {
-        if (2 * s < NRD) rdf(2 * s, slot, ks, buf);
-        if (2 * s + 1 < NRD) rdf(2 * s + 1, slot, ks, buf);
+    auto reads_at = [&](int s, int slot, int ks, int buf, int h) {
+        if (2 * s < NRD) rdf(2 * s, slot, ks, buf, h);
+        if (2 * s + 1 < NRD) rdf(2 * s + 1, slot, ks, buf, h);
     };
     auto dmas_at = [&](int s, int kt, int slot) {
 #pragma unroll
         for (int d = 0; d < DPW; ++d)
             if ((d * NMM) / DPW == s) dma(d, kt, slot);
+    };
+    // PA: the weights of stage kt, and with APAIR the activations of stages kt, kt + 1
+    auto dmas_pa = [&](int s, int kt, int slot, auto APAIR) {
+        constexpr int NA = decltype(APAIR)::value ? APW2 : 0, ND = NA + BPW;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+            if ((d * NMM) / ND == s) {
+                if (d < NA) dma_a2(d, kt, slot);
+                else dma_b(d - NA, kt, slot);
+            }
     };
 
     // w8A16 scales: spk[j] = this lane's scale (packed twice) for weight
@@ -999,16 +1073,31 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     }
 
     // prologue: stages 0 .. S-2 in flight, stage 0 visible, its k step 0 read
-    for (int s = 0; s < S - 1; ++s)
-        if (s < KT)
-            for (int d = 0; d < DPW; ++d) dma(d, s, s);
-    if (KT >= S - 1) wait_vmcnt<(S - 2) * DPW>();
-    else wait_vmcnt<0>();
+    if constexpr (PA) {
+        // A pair (0, 1), B 0, B 1, A pair (2, 3), B 2 (KT is even); stage 0 = the first two
+        for (int d = 0; d < APW2; ++d) dma_a2(d, 0, 0);
+        for (int d = 0; d < BPW; ++d) dma_b(d, 0, 0);
+        for (int d = 0; d < BPW; ++d) dma_b(d, 1, 1);
+        if (KT >= 4) {
+            for (int d = 0; d < APW2; ++d) dma_a2(d, 2, 2);
+            for (int d = 0; d < BPW; ++d) dma_b(d, 2, 2);
+            wait_vmcnt<2 * BPW + APW2>();
+        } else {
+            wait_vmcnt<0>();
+        }
+    } else {
+        for (int s = 0; s < S - 1; ++s)
+            if (s < KT)
+                for (int d = 0; d < DPW; ++d) dma(d, s, s);
+        if (KT >= S - 1) wait_vmcnt<(S - 2) * DPW>();
+        else wait_vmcnt<0>();
+    }
     block_barrier();
-    for (int r = 0; r < NRD; ++r) rdf(r, 0, 0, 0);
+    for (int r = 0; r < NRD; ++r) rdf(r, 0, 0, 0, 0);
 
-    auto stage = [&](int kt, auto LOAD, auto MORE, auto WAITN) {
+    auto stage = [&](int kt, auto LOAD, auto MORE, auto WAITN, auto APAIR, auto PAR) {
         constexpr bool load = decltype(LOAD)::value, more = decltype(MORE)::value;
+        constexpr int par = decltype(PAR)::value;   // PA: kt & 1
         const int slot = kt % S;
         if constexpr (W8) {
             if (grouped) {
@@ -1025,7 +1114,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
 #pragma unroll
         for (int s = 0; s < NMM; ++s) {
             acc[s / FN][s % FN] = mfma32<KIND>(bf[0][s % FN], af[0][s / FN], acc[s / FN][s % FN]);
-            reads_at(s, slot, 1, 1);
+            reads_at(s, slot, 1, 1, par);
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (more) {
@@ -1039,8 +1128,11 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
 #pragma unroll
         for (int s = 0; s < NMM; ++s) {
             acc[s / FN][s % FN] = mfma32<KIND>(bf[1][s % FN], af[1][s / FN], acc[s / FN][s % FN]);
-            if constexpr (more) reads_at(s, nslot, 0, 0);
-            if constexpr (load) dmas_at(s, kt + S - 1, dslot);
+            if constexpr (more) reads_at(s, nslot, 0, 0, 1 - par);
+            if constexpr (load) {
+                if constexpr (PA) dmas_pa(s, kt + S - 1, dslot, APAIR);
+                else dmas_at(s, kt + S - 1, dslot);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (W8) {
@@ -1050,10 +1142,34 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     using yes = std::true_type;
     using no = std::false_type;
     int kt = 0;
-    // steady state: stages kt+2 .. kt+S-2 may stay in flight at the wait
-    for (; kt + S - 1 < KT; ++kt) stage(kt, yes{}, yes{}, std::integral_constant<int, (S - 3) * DPW>{});
-    for (; kt + 1 < KT; ++kt) stage(kt, no{}, yes{}, std::integral_constant<int, 0>{});
-    stage(kt, no{}, no{}, std::integral_constant<int, 0>{});
+    // steady state: stages kt+2 .. kt+S-2 may stay in flight at the wait.
+    // PA: stage t's phase 2 loads the weights of stage t + 3 and, for odd t, the
+    // activation pair (t + 3, t + 4); at stage kt's wait the loads of stage
+    // kt - 1's phase 2 may stay in flight.
+    using even = std::integral_constant<int, 0>;
+    using odd = std::integral_constant<int, 1>;
+    using none = std::integral_constant<int, 0>;
+    if constexpr (PA) {
+        // KT is even: stages run in (even, odd) pairs.  In the loop both stages
+        // load (one version of each, so the accumulators keep their registers);
+        // then at most one pair whose even stage loads the last weights; then
+        // the last pair.
+        for (; kt + S < KT; kt += 2) {
+            stage(kt, yes{}, yes{}, std::integral_constant<int, BPW + APW2>{}, no{}, even{});
+            stage(kt + 1, yes{}, yes{}, std::integral_constant<int, BPW>{}, yes{}, odd{});
+        }
+        if (kt + S - 1 < KT) {
+            stage(kt, yes{}, yes{}, std::integral_constant<int, BPW + APW2>{}, no{}, even{});
+            stage(kt + 1, no{}, yes{}, none{}, no{}, odd{});
+            kt += 2;
+        }
+        stage(kt, no{}, yes{}, none{}, no{}, even{});
+        stage(kt + 1, no{}, no{}, none{}, no{}, odd{});
+    } else {
+        for (; kt + S - 1 < KT; ++kt) stage(kt, yes{}, yes{}, std::integral_constant<int, (S - 3) * DPW>{}, no{}, even{});
+        for (; kt + 1 < KT; ++kt) stage(kt, no{}, yes{}, none{}, no{}, even{});
+        stage(kt, no{}, no{}, none{}, no{}, even{});
+    }
     __builtin_amdgcn_s_setprio(0);
 
     if (poison) {
@@ -1218,7 +1334,8 @@ __device__ __forceinline__ void fused_gather(const FusedGather& F, int c0, int c
     }
 }
 
-template <int BM, int BN, int S, int WM, int WN, int KIND, bool SIGNAL, bool TA = false, bool TB = false>
+template <int BM, int BN, int S, int WM, int WN, int KIND, bool SIGNAL, bool TA = false, bool TB = false,
+          bool PA = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P) {
     __shared__ __attribute__((aligned(1024))) uint8_t sm[ring_lds_bytes<BM, BN, S, WM, WN, KIND>()];
     constexpr int NX = 8;
@@ -1256,7 +1373,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P
         GemmParams g = P.g;
         g.a = P.a[c];
         g.b = P.b[c];
-        ring_tile<BM, BN, S, WM, WN, KIND, SIGNAL, TA, TB>(g, P.rows[c], P.rpb[c], P.base[c], P.stride[c], P.ashift[c],
+        ring_tile<BM, BN, S, WM, WN, KIND, SIGNAL, TA, TB, PA>(g, P.rows[c], P.rpb[c], P.base[c], P.stride[c], P.ashift[c],
                                                    tm * BM, tn * BN, sm, wi >= 0 && !ok);
         if constexpr (SIGNAL) {
             if (P.signal[c] >= 0) wg_signal(P.done + P.signal[c] * kSyncWords);
@@ -2039,6 +2156,18 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
         F.early = fp.early;
     }
     tiles[kMaxPieces] = 8 * P.per_xcd;
+    // activations in whole 128-byte row segments, two stages at a time (k % 64 == 0)
+    if constexpr (COC_PAIR_A && KIND != GK_W8_F16 && !TA && !TB) {
+        if (L.k % 64 == 0) {
+            if (signal)
+                hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true, false, false, true>),
+                                   dim3(8 * P.per_xcd), dim3(64 * WM * WN), 0, s, P);
+            else
+                hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, false, false, false, true>),
+                                   dim3(8 * P.per_xcd), dim3(64 * WM * WN), 0, s, P);
+            return hipGetLastError();
+        }
+    }
     if (signal)
         hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true, TA, TB>), dim3(8 * P.per_xcd),
                            dim3(64 * WM * WN), 0, s, P);
