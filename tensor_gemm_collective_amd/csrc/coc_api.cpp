@@ -415,7 +415,7 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
         R.nchunks = early;
         R.done = c->sync;
         R.own = P.rank;
-        R.narrow = g0.kind == GK_W8_F16;   // the int8 matmul leaves ~90 VGPRs per SIMD lane
+        R.narrow = chunks_reduce_narrow(L);   // fits beside the matmul's two waves per SIMD
         double bytes = 0;
         R.spin_limit = spin_limit_override();
         const uint32_t off = target_offset();

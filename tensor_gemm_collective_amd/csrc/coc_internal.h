@@ -219,6 +219,9 @@ int launch_gemm_chunks(const ChunksLaunch& L, void* stream, int32_t tiles[kMaxPi
 // Tiles per piece of L's launch, and in tiles[kMaxPieces] its workgroups
 // (what launch_gemm_chunks reports), without launching.
 void chunks_tiles(const ChunksLaunch& L, int32_t tiles[kMaxPieces + 1]);
+// Whether the waiting reduce beside this launch must be the one-vector form
+// (the matmul leaves too few VGPRs for the two-vector one to share a CU).
+bool chunks_reduce_narrow(const ChunksLaunch& L);
 // The plan by which L's launch would run the gather itself (L.gather_nchunks
 // set); the caller sets each chunk's ready target from it.
 FusedGatherPlan chunks_fused_gather(const ChunksLaunch& L);

@@ -2206,6 +2206,16 @@ hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* til
 
 }  // namespace
 
+bool chunks_reduce_narrow(const ChunksLaunch& L) {
+    // The int8-weight matmul (209 VGPRs) and the 256 x 256 paired-stage one
+    // (210) leave 80 VGPRs per SIMD lane beside their two waves, too few for
+    // the two-vector waiting reduce (104); the others (<= 200) leave 112.
+    if (L.kind == GK_W8_F16) return true;
+    int bm = 0, bn = 0, per_cu = 0;
+    const bool paired = COC_PAIR_A && !L.trans_a && !L.trans_b && L.k % 64 == 0;
+    return paired && chunks_shape(L, &bm, &bn, &per_cu) == 0;
+}
+
 void chunks_tiles(const ChunksLaunch& L, int32_t tiles[kMaxPieces + 1]) {
     for (int c = 0; c <= kMaxPieces; ++c) tiles[c] = 0;
     int per_cu = 0;
