@@ -814,7 +814,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     // blocks (the A of S stages) and then S weight slots.  k % 64 == 0.
     constexpr int A_REG = PA ? S * A_BYTES : 0;
     constexpr int APW2 = 2 * APW;   // PA: load instructions per wave for an A pair
-    static_assert(!PA || (!W8 && !TA && !TB && S == 4), "paired activation stages: bf16 / fp16, 4 slots");
+    static_assert(!PA || (!TA && !TB && S == 4), "paired activation stages: plain operands, 4 slots");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2157,7 +2157,7 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     }
     tiles[kMaxPieces] = 8 * P.per_xcd;
     // activations in whole 128-byte row segments, two stages at a time (k % 64 == 0)
-    if constexpr (COC_PAIR_A && KIND != GK_W8_F16 && !TA && !TB) {
+    if constexpr (COC_PAIR_A && !TA && !TB) {
         if (L.k % 64 == 0) {
             if (signal)
                 hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true, false, false, true>),
