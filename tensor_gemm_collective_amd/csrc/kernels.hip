@@ -814,7 +814,12 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     // blocks (the A of S stages) and then S weight slots.  k % 64 == 0.
     constexpr int A_REG = PA ? S * A_BYTES : 0;
     constexpr int APW2 = 2 * APW;   // PA: load instructions per wave for an A pair
-    static_assert(!PA || (!TA && !TB && S == 4), "paired activation stages: plain operands, 4 slots");
+    // PB (PA with the weights stored transposed, k-contiguous like the
+    // activations): the weights are paired the same way, in S / 2 pair blocks
+    // after the activations', and both pairs load together in odd stages.
+    constexpr bool PB = PA && TB;
+    constexpr int BPW2 = 2 * BPW;
+    static_assert(!PA || (!TA && S == 4), "paired stages: no transposed activations, 4 slots");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -875,6 +880,25 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
                 ardp[h][ks] = row * 128 + (((h * 4 + ks * 2 + (lane >> 5)) ^ gP(row)) << 4);
             }
     }
+    // PB: weight pair loads (n rows of 128-byte k segments) and fragment offsets
+    uint32_t bofp[PB ? BPW2 : 1];
+    int brtp[PB ? 2 : 1][2];
+    if constexpr (PB) {
+#pragma unroll
+        for (int i = 0; i < BPW2; ++i) {
+            const int q = (wave * BPW2 + i) * 64 + lane;
+            const int row = q >> 3;
+            const int nr = n0 + row < p.n ? n0 + row : p.n - 1;
+            bofp[i] = (uint32_t)nr * (uint32_t)p.k * 2 + (((q & 7) ^ gP(row)) << 4);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int row = wn * WTN + (lane & 31);
+                brtp[h][ks] = row * 128 + (((h * 4 + ks * 2 + (lane >> 5)) ^ gP(row)) << 4);
+            }
+    }
     // fragment offsets within a stage (the rest are immediates)
     int ard[2];
 #pragma unroll
@@ -933,6 +957,10 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     auto dma_b = [&](int d, int kt, int slot) {
         dma16_sbase(bof[d], p.b + (int64_t)kt * bstep, lds0 + A_REG + slot * B_BYTES + (wave * BPW + d) * 1024);
     };
+    auto dma_b2 = [&](int d, int kt, int slot) {
+        dma16_sbase(bofp[PB ? d : 0], p.b + (int64_t)kt * bstep,
+                    lds0 + A_REG + (slot >> 1) * 2 * B_BYTES + (wave * BPW2 + d) * 1024);
+    };
     auto dma_a2 = [&](int d, int kt, int slot) {
         dma16_sbase(aofp[PA ? d : 0], p.a + (int64_t)kt * astep, lds0 + (slot >> 1) * 2 * A_BYTES + (wave * APW2 + d) * 1024);
     };
@@ -968,7 +996,10 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             return;
         }
         if (r < WRD * FN) {
-            if constexpr (TB) {
+            if constexpr (PB) {
+                bf[buf][r] = *(const COC_LDS u32x4*)((const COC_LDS uint8_t*)sm + A_REG + (slot >> 1) * 2 * B_BYTES +
+                                                     brtp[PB ? h : 0][ks] + r * 32 * 128);
+            } else if constexpr (TB) {
                 bf[buf][r] = *(const COC_LDS u32x4*)(st + brt[ks] + r * 32 * BK * 2);
             } else {
                 const int j = r >> 1, h = r & 1;
@@ -1000,13 +1031,24 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     };
     // PA: the weights of stage kt, and with APAIR the activations of stages kt, kt + 1
     auto dmas_pa = [&](int s, int kt, int slot, auto APAIR) {
-        constexpr int NA = decltype(APAIR)::value ? APW2 : 0, ND = NA + BPW;
+        if constexpr (PB) {
+            // both pairs, in odd stages only
+            constexpr int ND = APW2 + BPW2;
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
-            if ((d * NMM) / ND == s) {
-                if (d < NA) dma_a2(d, kt, slot);
-                else dma_b(d - NA, kt, slot);
-            }
+            for (int d = 0; d < ND; ++d)
+                if ((d * NMM) / ND == s) {
+                    if (d < APW2) dma_a2(d, kt, slot);
+                    else dma_b2(d - APW2, kt, slot);
+                }
+        } else {
+            constexpr int NA = decltype(APAIR)::value ? APW2 : 0, ND = NA + BPW;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                if ((d * NMM) / ND == s) {
+                    if (d < NA) dma_a2(d, kt, slot);
+                    else dma_b(d - NA, kt, slot);
+                }
+        }
     };
 
     // w8A16 scales: spk[j] = this lane's scale (packed twice) for weight
@@ -1073,7 +1115,18 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     }
 
     // prologue: stages 0 .. S-2 in flight, stage 0 visible, its k step 0 read
-    if constexpr (PA) {
+    if constexpr (PB) {
+        // pairs (0, 1) of both operands, then pairs (2, 3) (KT is even)
+        for (int d = 0; d < APW2; ++d) dma_a2(d, 0, 0);
+        for (int d = 0; d < BPW2; ++d) dma_b2(d, 0, 0);
+        if (KT >= 4) {
+            for (int d = 0; d < APW2; ++d) dma_a2(d, 2, 2);
+            for (int d = 0; d < BPW2; ++d) dma_b2(d, 2, 2);
+            wait_vmcnt<APW2 + BPW2>();
+        } else {
+            wait_vmcnt<0>();
+        }
+    } else if constexpr (PA) {
         // A pair (0, 1), B 0, B 1, A pair (2, 3), B 2 (KT is even); stage 0 = the first two
         for (int d = 0; d < APW2; ++d) dma_a2(d, 0, 0);
         for (int d = 0; d < BPW; ++d) dma_b(d, 0, 0);
@@ -1149,7 +1202,22 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     using even = std::integral_constant<int, 0>;
     using odd = std::integral_constant<int, 1>;
     using none = std::integral_constant<int, 0>;
-    if constexpr (PA) {
+    if constexpr (PB) {
+        // odd stages load the next pairs of both operands (two stages ahead),
+        // even stages nothing; at an even stage's wait the pairs the previous
+        // odd stage loaded may stay in flight
+        for (; kt + S < KT; kt += 2) {
+            stage(kt, no{}, yes{}, std::integral_constant<int, APW2 + BPW2>{}, no{}, even{});
+            stage(kt + 1, yes{}, yes{}, none{}, yes{}, odd{});
+        }
+        if (kt + S - 1 < KT) {
+            stage(kt, no{}, yes{}, std::integral_constant<int, APW2 + BPW2>{}, no{}, even{});
+            stage(kt + 1, no{}, yes{}, none{}, no{}, odd{});
+            kt += 2;
+        }
+        stage(kt, no{}, yes{}, none{}, no{}, even{});
+        stage(kt + 1, no{}, no{}, none{}, no{}, odd{});
+    } else if constexpr (PA) {
         // KT is even: stages run in (even, odd) pairs.  In the loop both stages
         // load (one version of each, so the accumulators keep their registers);
         // then at most one pair whose even stage loads the last weights; then
@@ -2157,13 +2225,13 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     }
     tiles[kMaxPieces] = 8 * P.per_xcd;
     // activations in whole 128-byte row segments, two stages at a time (k % 64 == 0)
-    if constexpr (COC_PAIR_A && !TA && !TB) {
+    if constexpr (COC_PAIR_A && !TA) {
         if (L.k % 64 == 0) {
             if (signal)
-                hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true, false, false, true>),
+                hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true, false, TB, true>),
                                    dim3(8 * P.per_xcd), dim3(64 * WM * WN), 0, s, P);
             else
-                hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, false, false, false, true>),
+                hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, false, false, TB, true>),
                                    dim3(8 * P.per_xcd), dim3(64 * WM * WN), 0, s, P);
             return hipGetLastError();
         }
@@ -2207,12 +2275,12 @@ hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* til
 }  // namespace
 
 bool chunks_reduce_narrow(const ChunksLaunch& L) {
-    // The int8-weight matmul (209 VGPRs) and the 256 x 256 paired-stage one
-    // (210) leave 80 VGPRs per SIMD lane beside their two waves, too few for
-    // the two-vector waiting reduce (104); the others (<= 200) leave 112.
+    // The int8-weight matmul (209-219 VGPRs) and the 256 x 256 paired-stage
+    // ones (208-210) leave 80 VGPRs per SIMD lane beside their two waves, too
+    // few for the two-vector waiting reduce (104); the others (<= 200) leave 112.
     if (L.kind == GK_W8_F16) return true;
     int bm = 0, bn = 0, per_cu = 0;
-    const bool paired = COC_PAIR_A && !L.trans_a && !L.trans_b && L.k % 64 == 0;
+    const bool paired = COC_PAIR_A && !L.trans_a && L.k % 64 == 0;
     return paired && chunks_shape(L, &bm, &bn, &per_cu) == 0;
 }
 
