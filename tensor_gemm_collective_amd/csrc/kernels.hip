@@ -28,8 +28,9 @@
 // the chunk matmuls running side by side should have together before the
 // ring kernel moves to a larger tile.
 // Activations of two consecutive k stages staged together as whole 128-byte
-// row segments (bf16 / fp16, k % 64 == 0): measured 1.2-2.8 % faster on the
-// LLaMA2-70B shapes with random operands, bit-identical results.
+// row segments (k % 64 == 0; transposed weights likewise): measured 1.2-2.8 %
+// faster on the LLaMA2-70B shapes with random operands (5-10 % with
+// transposed weights), bit-identical results.
 #ifndef COC_PAIR_A
 #define COC_PAIR_A 1
 #endif
@@ -748,12 +749,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
 //   * Fragment reads go 2 per MFMA from the first MFMA of a phase; the DMA
 //     instructions are spread evenly over phase 2.  sched_barrier fixes that
 //     order against the compiler's scheduler.
-//   * With k % 64 == 0 (bf16 / fp16, plain operands) the activations of stages
+//   * With k % 64 == 0 (activations not transposed) the activations of stages
 //     2j and 2j + 1 arrive together, whole 128-byte row segments, in one of
 //     two pair blocks; the weights keep their four 32-k slots.  The pair is
 //     loaded with the weights of stage 2j, in phase 2 of stage 2j - 3, which
-//     keeps the same two stages of load slack.  The fragments, and so the
-//     bits, are those of the 32-k layout.
+//     keeps the same two stages of load slack.  Transposed weights (k
+//     contiguous) are paired the same way and load with the activations'
+//     pair.  The fragments, and so the bits, are those of the 32-k layout.
 //   * Phase 2 runs at wave priority 1 and phase 1 at 0.  The two waves on a
 //     SIMD drift apart by up to a phase; the barrier then waits for the one
 //     still in phase 2, which the priority lets issue first.  Measured with a
@@ -953,7 +955,9 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     const int KT = p.k / BK;   // >= 1 (the launcher sends k == 0 elsewhere)
     const int64_t astep = TA ? (int64_t)BK * p.lda * 2 : (int64_t)BK * 2;
     const int64_t bstep = TB ? (int64_t)BK * 2 : (int64_t)BK * p.n * BE;
-    // PA: weights of stage kt into slot `slot`; activations of stages kt, kt + 1 (kt even)
+    // PA: dma_b, the weights of stage kt into slot `slot`; dma_b2 (PB) and
+    // dma_a2, the weights / activations of stages kt and kt + 1 (kt even) into
+    // the pair block of slot `slot`
     auto dma_b = [&](int d, int kt, int slot) {
         dma16_sbase(bof[d], p.b + (int64_t)kt * bstep, lds0 + A_REG + slot * B_BYTES + (wave * BPW + d) * 1024);
     };
@@ -1198,7 +1202,8 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     // steady state: stages kt+2 .. kt+S-2 may stay in flight at the wait.
     // PA: stage t's phase 2 loads the weights of stage t + 3 and, for odd t, the
     // activation pair (t + 3, t + 4); at stage kt's wait the loads of stage
-    // kt - 1's phase 2 may stay in flight.
+    // kt - 1's phase 2 may stay in flight.  PB: odd stages load both pairs
+    // (t + 3, t + 4), even stages nothing.
     using even = std::integral_constant<int, 0>;
     using odd = std::integral_constant<int, 1>;
     using none = std::integral_constant<int, 0>;
