@@ -81,8 +81,10 @@ def test_gemm_integer_inputs_bit_exact(dtype, m, n, k):
 
 def test_gemm_bits_independent_of_kernel_and_tile():
     """Rows 0..127 of X @ W through the 256x256, 128x256 and 128x128 ring tiles
-    and through the any-k kernel (k padded with zeros) are the same bits: every
-    kernel walks k in the same 16-k MFMA steps."""
+    (k = 512: activations staged two 32-k stages at a time), through the ring
+    with single 32-k stages (k padded with zeros to 544, not a multiple of 64)
+    and through the any-k kernel (k padded to 520) are the same bits: every
+    kernel walks k in the same 16-k MFMA steps, and zero steps add nothing."""
     log("GEMM bits across kernels and tiles")
     k, n = 512, 8192
     x = synth.normal(WID_TEST + 12, synth.T_X, 0, (2048, k), 1.0, "bf16")
@@ -92,12 +94,13 @@ def test_gemm_bits_independent_of_kernel_and_tile():
     for rows in (2048, 1024, 128):      # 256 tiles of 256x256, 256 of 128x256, 32 of 128x128
         _, p = tgc.matmul_all_reduce(xd[:rows].contiguous(), wd, [None], 0, split=1)
         outs.append(p[:128])
-    xpad = torch.zeros((128, k + 8), dtype=torch.bfloat16, device="cuda")
-    xpad[:, :k] = xd[:128]
-    wpad = torch.zeros((k + 8, n), dtype=torch.bfloat16, device="cuda")
-    wpad[:k] = wd
-    _, p = tgc.matmul_all_reduce(xpad, wpad, [None], 0, split=1)
-    outs.append(p)
+    for pad in (32, 8):
+        xpad = torch.zeros((128, k + pad), dtype=torch.bfloat16, device="cuda")
+        xpad[:, :k] = xd[:128]
+        wpad = torch.zeros((k + pad, n), dtype=torch.bfloat16, device="cuda")
+        wpad[:k] = wd
+        _, p = tgc.matmul_all_reduce(xpad, wpad, [None], 0, split=1)
+        outs.append(p)
     torch.cuda.synchronize()
     for i, o in enumerate(outs[1:], 1):
         assert_bits_equal(o, raw(outs[0]), f"variant {i} vs 256x256 tiles")
@@ -316,15 +319,19 @@ def test_weight_grad_of_gathered_matrix():
 @pytest.mark.parametrize("mode", ["per_tensor", "per_channel", "per_group"])
 @pytest.mark.parametrize("split", [1, 4])
 @pytest.mark.parametrize("n,g", [(520, 128), (1040, 128), (1040, 32), (528, 16)])
-def test_w8a16_exact_with_power_of_two_scales(mode, split, n, g):
+@pytest.mark.parametrize("k", [512, 544])
+def test_w8a16_exact_with_power_of_two_scales(mode, split, n, g, k):
     """X in {-2..2}, q in {-15..15}, scales 2^-6..2^-2 differing per channel and
     group: every product and the binary32 sums are exact, so partial_out is the
     correctly rounded exact result, bit for bit, whatever the scale index.
     n % 16 == 0 with group a multiple of 32 takes the ring kernel (int8
-    transpose reads, in-register dequantisation); the others the
+    transpose reads, in-register dequantisation; k = 512 stages the
+    activations two 32-k stages at a time, k = 544 one); the others the
     register-staged kernel."""
-    log(f"w8a16 exact {mode} split={split} n={n} g={g}")
-    m, k, world, rank = 256, 512, 4, 1
+    if mode == "per_group" and k % g:
+        pytest.skip("the group must divide k")
+    log(f"w8a16 exact {mode} split={split} n={n} g={g} k={k}")
+    m, world, rank = 256, 4, 1
     x = _ints(7, (m, k), -2, 2, "f16")
     q = synth.integers(WID_TEST + 7, synth.T_W, 0, (k, n), -15, 15, "i8")
     shape = {"per_tensor": (1,), "per_channel": (n,), "per_group": (k // g, n)}[mode]
