@@ -611,6 +611,10 @@ def main():
             "reduce_gbs": gbs(prof["reduce"]),
             "gather_gbs": gbs(prof["gather"]),
             "comm_hidden_frac": None if hidden is None else round(hidden, 3),
+            # the part of the step with no matmul launch running: exposed
+            # communication, launch gaps and the reduce of the last round
+            "no_matmul_ms_per_step": round(ms_step - gemm_ms, 5),
+            "no_matmul_frac_of_step": round(max(0.0, ms_step - gemm_ms) / ms_step, 4),
             "comm_note": "reduce and gather launches start beside the matmul and wait on its per-chunk "
                          "counters, so their intervals (and the GB/s above) include the waiting",
         },
