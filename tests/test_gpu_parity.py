@@ -234,6 +234,33 @@ def test_allgather_matmul(dtype, split, rank, k):
 TW_SHAPES = [(528, 392, 256), (2080, 1032, 96), (1024, 8200, 64)]   # m, n (output), k (reduction)
 
 
+@pytest.mark.parametrize("trans_w", [False, True])
+@pytest.mark.parametrize("k", [64, 128, 192, 256, 320, 384])
+def test_paired_stage_edges(k, trans_w):
+    """k a multiple of 64 stages two 32-k activation stages (and, with transposed
+    weights, weight stages) at a time; the schedule has its own code for 2, 4 and
+    6 stages and for longer loops.  Integer operands make every sum exact: the
+    paired product must be the exact result, and equal bit for bit to the product
+    of the same operands padded with 32 zero k (single 32-k stages)."""
+    log(f"paired stage edges k={k} trans_w={trans_w}")
+    m, n = 512, 768
+    x = _ints(20, (m, k), -3, 3, "bf16")
+    w = synth.integers(WID_TEST + 20, synth.T_W, 0, (k, n), -3, 3, "bf16")
+    exact = oracle.matmul(f64(x, "bf16"), f64(w, "bf16"))
+    outs = []
+    for pad in (0, 32):
+        xp = torch.zeros((m, k + pad), dtype=torch.bfloat16)
+        xp[:, :k] = x
+        wp = torch.zeros((k + pad, n), dtype=torch.bfloat16)
+        wp[:k] = w
+        wd = dev(wp.t().contiguous()) if trans_w else dev(wp)
+        _, p = tgc.matmul_all_reduce(dev(xp), wd, [None], 0, split=4, deterministic=1, trans_w=trans_w)
+        torch.cuda.synchronize()
+        outs.append(p)
+    assert_bits_equal(outs[0], encode_dtype(exact, "bf16"), "paired stages vs the exact product")
+    assert_bits_equal(outs[1], raw(outs[0]), "single 32-k stages vs paired")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("m,n,k", TW_SHAPES)
 @pytest.mark.parametrize("split", [1, 4])
