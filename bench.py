@@ -256,28 +256,71 @@ def run_configs(torch, tgc, synth, dev, iters=10):
         emit(f"w8a16_ar {mode} split4", 2.0 * wl.m * wl.n * wl.k, ms, ref)
     del x, q, pr, wf
 
-    # backward of the LLaMA2-70B pair: dX of the down projection (AG(dY) @ W^T,
-    # the 3584 x 8192 forward weight read transposed), dX of the gate/up layer
-    # (dY @ W^T reduce-scattered, W 8192 x 7168 read transposed), and dW of the
-    # gate/up layer from the gathered G
+    run_backward(torch, tgc, synth, dev, timeit, emit)
+
+
+def run_backward(torch, tgc, synth, dev, timeit, emit, warm_passes=0):
+    """The backward of the LLaMA2-70B pair: dX of the down projection (AG(dY) @ W^T,
+    the 3584 x 8192 forward weight read transposed), dX of the gate/up layer
+    (dY @ W^T reduce-scattered, W 8192 x 7168 read transposed), and dW of the
+    gate/up layer from the gathered G.  Inputs are drawn once; `warm_passes`
+    untimed passes over the cases first; then one JSON line per case (emit)."""
+    W = synth.WORKLOADS
     wl = W["llama70b_ag"]
     shard = wl.m // wl.world
     dys = [synth.normal(wl.wid, synth.T_PEER, 9 + r, (shard, wl.k), 1.0, "bf16").to(dev) for r in range(wl.world)]
     w_down = synth.normal(wl.wid, synth.T_W, 9, (3584, wl.k), 0.02, "bf16").to(dev)
-    ms = timeit(lambda: tgc.allgather_matmul(dys[0], dys, w_down, 0, split=4, trans_w=True))
-    emit("llama70b backward dX down-proj: AG(dY 8x512x8192) @ W^T (8192 -> 3584) split4",
-         2.0 * wl.m * 3584 * wl.k, ms, timeit(lambda: torch.matmul(torch.cat(dys), w_down.t())))
     w_up = synth.normal(wl.wid, synth.T_W, 0, (wl.k, wl.n), 0.02, "bf16").to(dev)
     dy = synth.normal(wl.wid, synth.T_X, 9, (wl.m, wl.n), 1.0, "bf16").to(dev)
     pr = [None] + [synth.normal(wl.wid, synth.T_PEER, 20 + r, (wl.m, wl.k), 1.0, "bf16").to(dev)
                    for r in range(1, wl.world)]
-    ms = timeit(lambda: tgc.matmul_reduce_scatter(dy, w_up, pr, 0, split=4, trans_w=True))
-    emit("llama70b backward dX gate/up: dY 4096x7168 @ W^T (7168 -> 8192) reduce-scattered split4",
-         2.0 * wl.m * wl.k * wl.n, ms, timeit(lambda: torch.matmul(dy, w_up.t())))
     g = torch.cat(dys)
-    ms = timeit(lambda: tgc.weight_grad(g, dy))
-    emit("llama70b backward dW gate/up: G^T (8192x4096) @ dY (4096x7168)", 2.0 * wl.m * wl.k * wl.n, ms,
-         timeit(lambda: torch.matmul(g.t(), dy)))
+    cases = [
+        ("llama70b backward dX down-proj: AG(dY 8x512x8192) @ W^T (8192 -> 3584) split4",
+         2.0 * wl.m * 3584 * wl.k,
+         lambda: tgc.allgather_matmul(dys[0], dys, w_down, 0, split=4, trans_w=True),
+         lambda: torch.matmul(torch.cat(dys), w_down.t())),
+        ("llama70b backward dX gate/up: dY 4096x7168 @ W^T (7168 -> 8192) reduce-scattered split4",
+         2.0 * wl.m * wl.k * wl.n,
+         lambda: tgc.matmul_reduce_scatter(dy, w_up, pr, 0, split=4, trans_w=True),
+         lambda: torch.matmul(dy, w_up.t())),
+        ("llama70b backward dW gate/up: G^T (8192x4096) @ dY (4096x7168)",
+         2.0 * wl.m * wl.k * wl.n,
+         lambda: tgc.weight_grad(g, dy),
+         lambda: torch.matmul(g.t(), dy)),
+    ]
+    for _ in range(warm_passes):
+        for _, _, fn, _ in cases:
+            for _ in range(10):
+                fn()
+        torch.cuda.synchronize()
+    for name, flops, fn, ref in cases:
+        ms = timeit(fn)
+        emit(name, flops, ms, timeit(ref))
+
+
+def run_backward_only(torch, tgc, synth, dev, iters=10, warm_passes=3):
+    """Only the backward cases (stderr lines), after `warm_passes` untimed passes
+    so the GPU is at its steady clocks."""
+    def timeit(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    def emit(name, flops, ms, ref_ms, **kw):
+        line = {"case": name, "ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                "hipblaslt_gemm_only_ms": round(ref_ms, 5)}
+        line.update(kw)
+        print(json.dumps(line), file=sys.stderr, flush=True)
+
+    run_backward(torch, tgc, synth, dev, timeit, emit, warm_passes=warm_passes)
 
 
 def run_moe(torch, tgc, synth, dev, iters=10, prewarm_s=0.5):
@@ -382,6 +425,8 @@ def main():
                     help="constant: every matmul operand of the step holds one value (same kernels, same "
                          "work) -- a diagnostic of the clock the GPU sustains when the MFMA inputs do not "
                          "toggle; its line is marked as such and is not a benchmark figure")
+    ap.add_argument("--backward", action="store_true",
+                    help="only time the backward cases of the LLaMA2-70B pair (stderr lines) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) three "
                          "times, for scaling the HBM byte counters, and exit")
@@ -416,6 +461,9 @@ def main():
     tgc.lib()
     if args.moe:
         run_moe(torch, tgc, synth, dev, prewarm_s=args.prewarm_s)
+        return
+    if args.backward:
+        run_backward_only(torch, tgc, synth, dev, warm_passes=3 if args.prewarm_s > 0 else 0)
         return
     log("generating inputs ...")
     inp = make_inputs(torch, tgc, synth, args.split, dev)
