@@ -323,6 +323,84 @@ def run_backward_only(torch, tgc, synth, dev, iters=10, warm_passes=3):
     run_backward(torch, tgc, synth, dev, timeit, emit, warm_passes=warm_passes)
 
 
+def run_lone(torch, tgc, synth, dev, iters=20, reps=3):
+    """The lone matmuls of the LLaMA2-70B pair against hipBLASLt (torch.matmul):
+    the all-gather op's 4096x7168x8192 and the reduce-scatter op's 4096x8192x3584
+    (k x n weights), and the backward 4096x8192x7168 with the weight read
+    transposed (n x k).  Each is one matmul of the library with one rank and
+    split 1; its launch time comes from the library's per-launch events (the op
+    itself also copies partial_out into y).  The cases run interleaved, in a
+    seeded shuffled order per repetition; one stderr JSON line per case and
+    repetition."""
+    import random
+
+    W = synth.WORKLOADS
+    ag, rs = W["llama70b_ag"], W["llama70b_rs"]
+    m = ag.m
+    x_ag = synth.normal(ag.wid, synth.T_X, 30, (m, ag.k), 1.0, "bf16").to(dev)
+    w_ag = synth.normal(ag.wid, synth.T_W, 30, (ag.k, ag.n), 0.02, "bf16").to(dev)
+    x_rs = synth.normal(rs.wid, synth.T_X, 31, (m, rs.k), 1.0, "bf16").to(dev)
+    w_rs = synth.normal(rs.wid, synth.T_W, 31, (rs.k, rs.n), 0.02, "bf16").to(dev)
+    dy = synth.normal(ag.wid, synth.T_X, 32, (m, ag.n), 1.0, "bf16").to(dev)
+    outs = {}
+
+    def ours(name, x, w, trans_w=False):
+        n = w.shape[0] if trans_w else w.shape[1]
+        y, p = (torch.empty((x.shape[0], n), dtype=x.dtype, device=dev) for _ in range(2))
+        outs[name] = (y, p)
+        return lambda: tgc.matmul_all_reduce(x, w, [None], 0, y=y, partial_out=p, split=1, trans_w=trans_w)
+
+    def ref(x, w):
+        y = torch.empty((x.shape[0], w.shape[1]), dtype=x.dtype, device=dev)
+        return lambda: torch.matmul(x, w, out=y)
+
+    cases = {
+        "NN 4096x7168x8192 (all-gather op's matmul)": (2.0 * m * ag.n * ag.k, ours("ag", x_ag, w_ag),
+                                                      ref(x_ag, w_ag)),
+        "NN 4096x8192x3584 (reduce-scatter op's matmul)": (2.0 * m * rs.n * rs.k, ours("rs", x_rs, w_rs),
+                                                          ref(x_rs, w_rs)),
+        "NT 4096x8192x7168 (backward dX, weight read transposed)": (2.0 * m * ag.k * ag.n,
+                                                                    ours("nt", dy, w_ag, trans_w=True),
+                                                                    ref(dy, w_ag.t())),
+    }
+
+    def timeit(fn):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    def kernel_ms(fn):
+        torch.cuda.synchronize()
+        tgc.profile_read()
+        tgc.profile_enable(True)
+        for _ in range(iters):
+            fn()
+        torch.cuda.synchronize()
+        tgc.profile_enable(False)
+        gm = tgc.profile_read()["gemm"]
+        return gm["ms"] / gm["launches"]
+
+    order = random.Random(7)
+    for rep in range(reps):
+        names = list(cases)
+        order.shuffle(names)
+        for name in names:
+            flops, fn, rfn = cases[name]
+            op_ms, k_ms, r_ms = timeit(fn), kernel_ms(fn), timeit(rfn)
+            print(json.dumps({"case": name, "rep": rep, "matmul_launch_ms": round(k_ms, 5),
+                              "matmul_launch_tflops": round(flops / (k_ms * 1e-3) / 1e12, 1),
+                              "op_ms": round(op_ms, 5), "hipblaslt_ms": round(r_ms, 5),
+                              "hipblaslt_tflops": round(flops / (r_ms * 1e-3) / 1e12, 1)}),
+                  file=sys.stderr, flush=True)
+
+
 def run_moe(torch, tgc, synth, dev, iters=10, prewarm_s=0.5):
     """The MoE expert all-to-all + grouped matmul pair on the Ampipe page's
     scenario (hidden 12288, ffn 49152, 8192 tokens per rank, 4 experts, top 2,
@@ -427,6 +505,9 @@ def main():
                          "toggle; its line is marked as such and is not a benchmark figure")
     ap.add_argument("--backward", action="store_true",
                     help="only time the backward cases of the LLaMA2-70B pair (stderr lines) and exit")
+    ap.add_argument("--lone", action="store_true",
+                    help="only time the lone matmuls of the step's two ops and of the backward dX "
+                         "against hipBLASLt, interleaved (stderr lines), and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) three "
                          "times, for scaling the HBM byte counters, and exit")
@@ -461,6 +542,9 @@ def main():
     tgc.lib()
     if args.moe:
         run_moe(torch, tgc, synth, dev, prewarm_s=args.prewarm_s)
+        return
+    if args.lone:
+        run_lone(torch, tgc, synth, dev)
         return
     if args.backward:
         run_backward_only(torch, tgc, synth, dev, warm_passes=3 if args.prewarm_s > 0 else 0)
