@@ -52,20 +52,21 @@
  *     device, so it must not be captured: call once on the stream before
  *     capturing it (COC_ERR_CAPTURE otherwise).  The MoE all-to-all pair
  *     works only through those counters and returns COC_ERR_CAPTURE under
- *     capture.  Replays of one graph must not overlap each other.  Each op
- *     is tested captured into a graph of its own; graphs holding several of
- *     these calls are not tested.
+ *     capture.  Replays of one graph must not overlap each other.  One
+ *     capture holds at most one call of this library: a second call made
+ *     while the same capture is open (on any stream) returns
+ *     COC_ERR_CAPTURE and enqueues nothing.
  *   - `split` is the number of m-chunks the work is pipelined over: 1
  *     (serial, no overlap), 2, 4 or 8 (CoC guide, "Usage": the split count
  *     options; the m dimension must divide by it, CoC guide "Approach" and
  *     Overlap blog, third-layer caveats).
- *   - `trans_w` != 0 (matmul all-reduce / reduce-scatter / all-gather):
- *     `w` holds the weights transposed, n rows of k elements, so the
- *     backward pass of a layer (CoC guide, "Approach": forward / backward
- *     operator pairs) multiplies by the forward k x n weight read as its
- *     transpose without copying it: dX = dY @ W^T.  bf16 / fp16 and
- *     k % 32 == 0; the result bits equal those of trans_w = 0 with the
- *     transpose stored.
+ *   - The *_trans_w entry points (matmul all-reduce / reduce-scatter /
+ *     all-gather) take the same arguments as the plain ones, but `w` holds
+ *     the weights transposed, n rows of k elements, so the backward pass of
+ *     a layer (CoC guide, "Approach": forward / backward operator pairs)
+ *     multiplies by the forward k x n weight read as its transpose without
+ *     copying it: dX = dY @ W^T.  bf16 / fp16 and k % 32 == 0; the result
+ *     bits equal those of the plain entry point with the transpose stored.
  *   - `deterministic` != 0 selects the deterministic variants (CoC guide,
  *     "Approach", fused-operator list): partial sums are added in ascending
  *     rank order 0..world-1 in binary32 with this rank's own partial taken
@@ -86,8 +87,16 @@
  *
  * Hand-over waits.  The pipelined forms hand chunks between kernels through
  * device counters; every wait is bounded (about 2 s), and a wait that gives
- * up writes NaN into the tile or rows it guards instead of hanging.  Two
- * environment variables, read at each call, exist to test that path:
+ * up writes NaN into the tile or rows it guards instead of hanging, and
+ * records that it gave up: coc_check_waits() reports it to the host as
+ * COC_ERR_TIMEOUT.  A wait can only give up when the work it waits for
+ * cannot run: the one-launch all-gather matmul that copies the gathered rows
+ * itself has workgroups waiting for rows other workgroups of the same launch
+ * copy, so it needs all its workgroups (one per compute unit) resident at
+ * once; a kernel of another process (or of another library) that holds
+ * compute units for longer than the bound can starve it.  Calls of this
+ * library on one device are chained so that they cannot starve each other.
+ * Two environment variables, read at each call, exist to test that path:
  * COC_SPIN_LIMIT=n (polls before giving up) and COC_TEST_UNREACHABLE_WAIT=1
  * (the calls made meanwhile wait for counts that never arrive; the library's
  * own counter bookkeeping stays exact, so later calls are unaffected).
@@ -97,6 +106,10 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+/* hipStream_t.  A host compiler other than hipcc needs -D__HIP_PLATFORM_AMD__
+ * and the ROCm include directory for this header. */
+#include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -128,7 +141,8 @@ typedef enum coc_status {
     COC_ERR_WORKSPACE = 7,  /* workspace missing or too small                  */
     COC_ERR_HIP = 8,        /* the HIP runtime reported an error               */
     COC_ERR_ALIAS = 9,      /* an output overlaps an input or another output   */
-    COC_ERR_CAPTURE = 10    /* not possible while the stream is captured        */
+    COC_ERR_CAPTURE = 10,   /* not possible while the stream is captured        */
+    COC_ERR_TIMEOUT = 11    /* a hand-over wait gave up (coc_check_waits)       */
 } coc_status;
 
 typedef enum coc_op {
@@ -156,8 +170,8 @@ typedef enum coc_op {
 coc_status coc_matmul_all_reduce(const void* x, const void* w, void* y, void* partial_out,
                                  const void* const* peer_bufs, int32_t world, int32_t rank,
                                  int64_t m, int64_t n, int64_t k, coc_dtype dt,
-                                 int32_t split, int32_t deterministic, int32_t trans_w,
-                                 void* ws, size_t ws_bytes, void* stream);
+                                 int32_t split, int32_t deterministic,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * MATMUL_REDUCE_SCATTER (CoC guide, "Approach", fused-operator list: compute
@@ -177,8 +191,8 @@ coc_status coc_matmul_all_reduce(const void* x, const void* w, void* y, void* pa
 coc_status coc_matmul_reduce_scatter(const void* x, const void* w, void* y, void* partial_out,
                                      const void* const* peer_bufs, int32_t world, int32_t rank,
                                      int64_t m, int64_t n, int64_t k, coc_dtype dt,
-                                     int32_t split, int32_t deterministic, int32_t trans_w,
-                                     void* ws, size_t ws_bytes, void* stream);
+                                     int32_t split, int32_t deterministic,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * ALL_GATHER_MATMUL and ALL_GATHER_MATMUL_V2 (CoC guide, "Approach",
@@ -201,8 +215,34 @@ coc_status coc_matmul_reduce_scatter(const void* x, const void* w, void* y, void
 coc_status coc_allgather_matmul(const void* x_shard, const void* const* peer_bufs, const void* w,
                                 void* y, void* gathered_out, int32_t world, int32_t rank,
                                 int64_t m, int64_t n, int64_t k, coc_dtype dt,
-                                int32_t split, int32_t deterministic, int32_t trans_w,
-                                void* ws, size_t ws_bytes, void* stream);
+                                int32_t split, int32_t deterministic,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The same three ops with the weights given transposed (the backward pass of
+ * the pair; CoC guide, "Approach": the fused operators come in forward /
+ * backward pairs): `w` holds n rows of k elements, the forward layer's
+ * k x n weight as stored, and the matmul is round_dt(X @ w^T).  Everything
+ * else (arguments, layout, errors, pipeline) is as in the plain entry
+ * point.  The RS-layer's input gradient is the all-gather form, AG(dY) @
+ * W^T; the AG-layer's is the reduce-scatter form, RS(dY @ W^T).  bf16 / fp16
+ * only (COC_ERR_DTYPE otherwise) and k % 32 == 0 (COC_ERR_SHAPE otherwise).
+ */
+coc_status coc_matmul_all_reduce_trans_w(const void* x, const void* w, void* y, void* partial_out,
+                                         const void* const* peer_bufs, int32_t world, int32_t rank,
+                                         int64_t m, int64_t n, int64_t k, coc_dtype dt,
+                                         int32_t split, int32_t deterministic,
+                                         void* ws, size_t ws_bytes, hipStream_t stream);
+coc_status coc_matmul_reduce_scatter_trans_w(const void* x, const void* w, void* y, void* partial_out,
+                                             const void* const* peer_bufs, int32_t world, int32_t rank,
+                                             int64_t m, int64_t n, int64_t k, coc_dtype dt,
+                                             int32_t split, int32_t deterministic,
+                                             void* ws, size_t ws_bytes, hipStream_t stream);
+coc_status coc_allgather_matmul_trans_w(const void* x_shard, const void* const* peer_bufs, const void* w,
+                                        void* y, void* gathered_out, int32_t world, int32_t rank,
+                                        int64_t m, int64_t n, int64_t k, coc_dtype dt,
+                                        int32_t split, int32_t deterministic,
+                                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Weight gradient of the sequence-parallel pair (CoC guide, "Approach": the
@@ -218,7 +258,7 @@ coc_status coc_allgather_matmul(const void* x_shard, const void* const* peer_buf
  * matmul: no collective.
  */
 coc_status coc_weight_grad(const void* g, const void* dy, void* dw, int64_t m, int64_t n, int64_t k,
-                           coc_dtype dt, void* stream);
+                           coc_dtype dt, hipStream_t stream);
 
 /*
  * MoE expert all-to-all + grouped matmul, one expert-parallel rank's share
@@ -273,11 +313,11 @@ coc_status coc_weight_grad(const void* g, const void* dy, void* dw, int64_t m, i
 coc_status coc_alltoall_grouped_matmul(const void* x_own, const void* const* peer_bufs, const int64_t* counts,
                                        const void* w, void* y, void* recv_out, int32_t world, int32_t rank,
                                        int32_t experts, int64_t n, int64_t k, coc_dtype dt, int32_t split,
-                                       void* stream);
+                                       hipStream_t stream);
 coc_status coc_grouped_matmul_alltoall(const void* h, const void* w, void* y_local, void* y_own,
                                        void* const* peer_out, const int64_t* counts, int32_t world, int32_t rank,
                                        int32_t experts, int64_t n, int64_t k, coc_dtype dt, int32_t split,
-                                       void* stream);
+                                       hipStream_t stream);
 
 /*
  * w8A16 pseudo-quantised MATMUL_ALL_REDUCE (CoC guide, "Approach", last item
@@ -303,13 +343,22 @@ coc_status coc_matmul_all_reduce_w8a16(const void* x_f16, const int8_t* w_q, con
                                        const void* const* peer_bufs, int32_t world, int32_t rank,
                                        int64_t m, int64_t n, int64_t k,
                                        int32_t split, int32_t deterministic,
-                                       void* ws, size_t ws_bytes, void* stream);
+                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes an op needs at these sizes (0 when it needs none).
+/* Workspace bytes an op (a coc_op value) needs at these sizes (0 when it needs none).
  * dt is ignored for COC_OP_MATMUL_ALL_REDUCE_W8A16.  Returns 0 for invalid
  * arguments as well; the op call itself reports the error. */
-size_t coc_workspace_bytes(coc_op op, int64_t m, int64_t n, int64_t k, coc_dtype dt,
+size_t coc_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, coc_dtype dt,
                            int32_t world, int32_t split);
+
+/* Whether a hand-over wait of the library's work on `stream` gave up since
+ * the last check (see "Hand-over waits" above).  Waits for the work enqueued
+ * on `stream` so far, then returns COC_ERR_TIMEOUT if any wait of that work
+ * (or of earlier work of the library on the same stream, or of the
+ * allocation-free entry points on the current device) gave up, and clears
+ * that record; COC_OK otherwise.  COC_ERR_CAPTURE while `stream` is being
+ * captured, COC_ERR_HIP if a HIP call fails. */
+coc_status coc_check_waits(hipStream_t stream);
 
 /* Static name of a status code. */
 const char* coc_status_string(coc_status s);

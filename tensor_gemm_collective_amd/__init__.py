@@ -19,6 +19,7 @@ from .coc import (  # noqa: F401
     alltoall_grouped_matmul,
     grouped_matmul_alltoall,
     workspace_bytes,
+    check_waits,
     plan,
     profile_enable,
     profile_read,

@@ -25,7 +25,7 @@ OP_MATMUL_ALL_REDUCE_W8A16 = 4
 STATUS = {
     0: "COC_OK", 1: "COC_ERR_NULL", 2: "COC_ERR_SPLIT", 3: "COC_ERR_SHAPE", 4: "COC_ERR_WORLD",
     5: "COC_ERR_DTYPE", 6: "COC_ERR_ALIGN", 7: "COC_ERR_WORKSPACE", 8: "COC_ERR_HIP",
-    9: "COC_ERR_ALIAS", 10: "COC_ERR_CAPTURE",
+    9: "COC_ERR_ALIAS", 10: "COC_ERR_CAPTURE", 11: "COC_ERR_TIMEOUT",
 }
 QUANT_MODES = {"per_tensor": COC_PER_TENSOR, "per_channel": COC_PER_CHANNEL, "per_group": COC_PER_GROUP}
 KCLASS = ("gemm", "reduce", "gather")
@@ -33,9 +33,11 @@ KCLASS = ("gemm", "reduce", "gather")
 # exported symbols, as declared in include/coc.h
 EXPORTS = (
     "coc_matmul_all_reduce", "coc_matmul_reduce_scatter", "coc_allgather_matmul",
-    "coc_matmul_all_reduce_w8a16", "coc_weight_grad", "coc_alltoall_grouped_matmul",
+    "coc_matmul_all_reduce_w8a16", "coc_matmul_all_reduce_trans_w", "coc_matmul_reduce_scatter_trans_w",
+    "coc_allgather_matmul_trans_w", "coc_weight_grad", "coc_alltoall_grouped_matmul",
     "coc_grouped_matmul_alltoall", "coc_workspace_bytes", "coc_status_string",
-    "coc_last_error", "coc_plan", "coc_profile_enable", "coc_profile_read", "coc_profile_records",
+    "coc_last_error", "coc_check_waits", "coc_plan", "coc_profile_enable", "coc_profile_read",
+    "coc_profile_records",
 )
 
 
@@ -69,10 +71,13 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
     L = ctypes.CDLL(LIB_PATH)
-    common = [_i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
-    L.coc_matmul_all_reduce.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(_vp)] + common
-    L.coc_matmul_reduce_scatter.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(_vp)] + common
-    L.coc_allgather_matmul.argtypes = [_vp, ctypes.POINTER(_vp), _vp, _vp, _vp] + common
+    # world, rank, m, n, k, dt, split, deterministic, ws, ws_bytes, stream
+    common = [_i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _sz, _vp]
+    for f in ("coc_matmul_all_reduce", "coc_matmul_reduce_scatter", "coc_matmul_all_reduce_trans_w",
+              "coc_matmul_reduce_scatter_trans_w"):
+        getattr(L, f).argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(_vp)] + common
+    for f in ("coc_allgather_matmul", "coc_allgather_matmul_trans_w"):
+        getattr(L, f).argtypes = [_vp, ctypes.POINTER(_vp), _vp, _vp, _vp] + common
     L.coc_matmul_all_reduce_w8a16.argtypes = [
         _vp, _vp, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(_vp), _i32, _i32, _i64, _i64, _i64,
         _i32, _i32, _vp, _sz, _vp]
@@ -81,9 +86,12 @@ def lib() -> ctypes.CDLL:
     L.coc_alltoall_grouped_matmul.argtypes = [_vp, ctypes.POINTER(_vp)] + moe_tail[:1] + [_vp, _vp, _vp] + moe_tail[1:]
     L.coc_grouped_matmul_alltoall.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(_vp)] + moe_tail
     for f in ("coc_matmul_all_reduce", "coc_matmul_reduce_scatter", "coc_allgather_matmul",
-              "coc_matmul_all_reduce_w8a16", "coc_weight_grad", "coc_alltoall_grouped_matmul",
-              "coc_grouped_matmul_alltoall"):
+              "coc_matmul_all_reduce_trans_w", "coc_matmul_reduce_scatter_trans_w",
+              "coc_allgather_matmul_trans_w", "coc_matmul_all_reduce_w8a16", "coc_weight_grad",
+              "coc_alltoall_grouped_matmul", "coc_grouped_matmul_alltoall"):
         getattr(L, f).restype = _i32
+    L.coc_check_waits.argtypes = [_vp]
+    L.coc_check_waits.restype = _i32
     L.coc_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64, _i32, _i32, _i32]
     L.coc_workspace_bytes.restype = _sz
     L.coc_status_string.argtypes = [_i32]
@@ -159,10 +167,10 @@ def matmul_all_reduce(x, w, peers, rank, *, y=None, partial_out=None, split=4, d
     n = _wdims(w, trans_w)[1]
     y = _empty((m, n), x) if y is None else y
     partial_out = _empty((m, n), x) if partial_out is None else partial_out
-    _check(lib().coc_matmul_all_reduce(
+    fn = lib().coc_matmul_all_reduce_trans_w if trans_w else lib().coc_matmul_all_reduce
+    _check(fn(
         _ptr(x), _ptr(w), _ptr(y), _ptr(partial_out), _peer_array(peers, rank), len(peers), rank,
-        m, n, k, _dtype_code(x), split, int(bool(deterministic)), int(bool(trans_w)), None, 0,
-        _stream(stream, x.device)))
+        m, n, k, _dtype_code(x), split, int(bool(deterministic)), None, 0, _stream(stream, x.device)))
     return y, partial_out
 
 
@@ -175,10 +183,10 @@ def matmul_reduce_scatter(x, w, peers, rank, *, y=None, partial_out=None, split=
     world = len(peers)
     y = _empty((m // world, n), x) if y is None else y
     partial_out = _empty((m, n), x) if partial_out is None else partial_out
-    _check(lib().coc_matmul_reduce_scatter(
+    fn = lib().coc_matmul_reduce_scatter_trans_w if trans_w else lib().coc_matmul_reduce_scatter
+    _check(fn(
         _ptr(x), _ptr(w), _ptr(y), _ptr(partial_out), _peer_array(peers, rank), world, rank,
-        m, n, k, _dtype_code(x), split, int(bool(deterministic)), int(bool(trans_w)), None, 0,
-        _stream(stream, x.device)))
+        m, n, k, _dtype_code(x), split, int(bool(deterministic)), None, 0, _stream(stream, x.device)))
     return y, partial_out
 
 
@@ -202,9 +210,10 @@ def allgather_matmul(x_shard, peers, w, rank, *, y=None, gathered_out=None, v2=F
         if ws is None and need:
             ws = torch.empty(need, dtype=torch.uint8, device=x_shard.device)
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check(lib().coc_allgather_matmul(
+    fn = lib().coc_allgather_matmul_trans_w if trans_w else lib().coc_allgather_matmul
+    _check(fn(
         _ptr(x_shard), _peer_array(peers, rank), _ptr(w), _ptr(y), _ptr(gathered_out) if v2 else None,
-        world, rank, m, n, k, _dtype_code(x_shard), split, int(bool(deterministic)), int(bool(trans_w)),
+        world, rank, m, n, k, _dtype_code(x_shard), split, int(bool(deterministic)),
         _ptr(ws) if not v2 else None, ws_bytes, _stream(stream, x_shard.device)))
     return (y, gathered_out) if v2 else y
 
@@ -284,6 +293,14 @@ def matmul_all_reduce_w8a16(x, w_q, scales, mode, peers, rank, *, group_size=128
         _peer_array(peers, rank), len(peers), rank, m, n, k, split, int(bool(deterministic)),
         None, 0, _stream(stream, x.device)))
     return y, partial_out
+
+
+def check_waits(stream=None, device=None) -> None:
+    """Raise CocError(COC_ERR_TIMEOUT) if a hand-over wait of the library's work
+    on `stream` (default: the current stream) gave up since the last check."""
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    _check(lib().coc_check_waits(s.cuda_stream))
 
 
 def workspace_bytes(op: int, m: int, n: int, k: int, dt: int, world: int, split: int) -> int:

@@ -99,6 +99,7 @@ struct StreamCtx {
     uint32_t done_sent[COC_MAX_SPLIT] = {};
     uint32_t ready_sent[COC_MAX_SPLIT] = {};
     hipEvent_t tail = nullptr;     // end of this stream's last counter-waiting call
+    uint32_t* gave_up() const { return sync + kGaveUpLine * kSyncWords; }
 };
 
 std::mutex g_ctx_mu;
@@ -113,6 +114,41 @@ coc_status capturing(hipStream_t s, bool* out) {
     COC_HIP(hipStreamIsCapturing(s, &cs));
     *out = cs != hipStreamCaptureStatusNone;
     return COC_OK;
+}
+
+// One capture holds at most one call of the library.  A bench run that
+// captured two ops into one graph ended in a host segmentation fault whose
+// cause was not found (the two calls record the same context events and
+// side-stream joins twice within one capture), so a second call while the
+// same capture is open is refused.  Capture ids are unique per capture; the
+// last few that took a call are remembered.
+std::mutex g_cap_mu;
+unsigned long long g_cap_ids[64] = {};
+int g_cap_next = 0;
+
+coc_status capture_once(hipStream_t s, bool* cap) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    unsigned long long id = 0;
+    COC_HIP(hipStreamGetCaptureInfo(s, &cs, &id));
+    *cap = cs != hipStreamCaptureStatusNone;
+    if (cs == hipStreamCaptureStatusInvalidated)
+        return fail(COC_ERR_CAPTURE, "the stream's capture has been invalidated");
+    if (!*cap) return COC_OK;
+    std::lock_guard<std::mutex> lk(g_cap_mu);
+    for (unsigned long long v : g_cap_ids)
+        if (v == id && id != 0)
+            return fail(COC_ERR_CAPTURE, "this capture already holds a call of the library; one graph holds "
+                                         "at most one (capture each op into a graph of its own)");
+    g_cap_ids[g_cap_next] = id;
+    g_cap_next = (g_cap_next + 1) % 64;
+    return COC_OK;
+}
+
+// The gave-up word of the allocation-free entry points' counters on device
+// `dev`, or NULL while they have not been set up there.
+uint32_t* static_gave_up(int dev) {
+    (void)dev;
+    return nullptr;
 }
 
 coc_status get_ctx(hipStream_t main, StreamCtx** out) {
@@ -418,6 +454,7 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
         R.narrow = chunks_reduce_narrow(L);   // fits beside the matmul's two waves per SIMD
         double bytes = 0;
         R.spin_limit = spin_limit_override();
+        R.gave_up = c->gave_up();
         const uint32_t off = target_offset();
         for (int i = 0; i < early; ++i) {
             R.target[i] = (c->done_sent[i] += (uint32_t)tiles[i]) + off;
@@ -482,9 +519,11 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
     }
     int32_t tiles[kMaxPieces + 1];
     L.gather_nchunks = P.nchunks;   // (the plan depends on it)
+    L.gave_up = c->gave_up();
     const FusedGatherPlan fp = COC_FUSED_GATHER ? chunks_fused_gather(L) : FusedGatherPlan{};
     if (fp.gatherers > 0) {
-        // the matmul launch copies the rows itself, chunk by chunk
+        // the matmul launch copies the rows itself, chunk by chunk; the host's
+        // running targets advance only once that launch is enqueued
         L.gather_plan = fp;
         for (int r = 0; r < COC_MAX_WORLD; ++r) L.gather_src[r] = a0.src[r < a0.nsrc ? r : 0];
         L.gather_dst = a0.dst;
@@ -492,12 +531,15 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
         L.gather_shard_rows = shard;
         L.spin_limit = spin_limit_override();
         const uint32_t off = target_offset();
+        uint32_t sent[COC_MAX_SPLIT];
         for (int i = 0; i < P.nchunks; ++i) {
             L.gather_row0[i] = grow0[i];
             L.gather_rows[i] = grows[i];
-            L.ready_target[i] = (c->ready_sent[i] += (uint32_t)(i < fp.early ? fp.workgroups : fp.gatherers)) + off;
+            sent[i] = c->ready_sent[i] + (uint32_t)(i < fp.early ? fp.workgroups : fp.gatherers);
+            L.ready_target[i] = sent[i] + off;
         }
         COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
+        for (int i = 0; i < P.nchunks; ++i) c->ready_sent[i] = sent[i];
         return chain.finish();
     }
     L.gather_nchunks = 0;
@@ -508,6 +550,7 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
         return launch_gather_chunks(a0, P.nchunks, grow0, grows, c->sync + COC_MAX_SPLIT * kSyncWords, c->side,
                                     &per_chunk);
     }));
+    // the gather is enqueued: its adds will happen whatever follows
     L.spin_limit = spin_limit_override();
     for (int i = 0; i < P.nchunks; ++i) L.ready_target[i] = (c->ready_sent[i] += (uint32_t)per_chunk) + target_offset();
     COC_TRY(launch(KC_GEMM, total_flops(P), main, [&] { return launch_gemm_chunks(L, main, tiles); }));
@@ -518,7 +561,7 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
 
 // Compute first, then reduce: all-reduce, reduce-scatter, w8a16 all-reduce.
 coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLaunch& r0,
-                             hipStream_t main) {
+                             hipStream_t main, bool cap) {
     const size_t es = elem_size(P.dt);
     auto gemm = [&](int i, hipStream_t s) {
         const GemmLaunch g = gemm_for_chunk(P, g0, P.chunk[i]);
@@ -536,8 +579,6 @@ coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLa
         COC_TRY(gemm(0, main));
         return reduce(0, main);
     }
-    bool cap = false;
-    COC_TRY(capturing(main, &cap));
     if (one_launch(P, g0) && !cap) return run_compute_first_chunks(P, g0, r0, main);
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
@@ -559,7 +600,7 @@ coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLa
 
 // Communicate first, then compute: all-gather matmul (and V2).
 coc_status run_comm_first(const Plan& P, const GemmLaunch& g0, const GatherLaunch& a0,
-                          hipStream_t main) {
+                          hipStream_t main, bool cap) {
     const size_t es = elem_size(P.dt);
     auto gather = [&](int i, hipStream_t s) {
         GatherLaunch a = a0;
@@ -576,8 +617,6 @@ coc_status run_comm_first(const Plan& P, const GemmLaunch& g0, const GatherLaunc
         COC_TRY(gather(0, main));
         return gemm(0, main);
     }
-    bool cap = false;
-    COC_TRY(capturing(main, &cap));
     if (one_launch_gather(P, g0) && !cap) return run_comm_first_chunks(P, g0, a0, main);
     StreamCtx* c = nullptr;
     COC_TRY(get_ctx(main, &c));
@@ -618,7 +657,7 @@ coc_status compute_first_op(coc_op op, const void* x, const void* w, const void*
                             int32_t qmode, int32_t group, void* y, void* partial,
                             const void* const* peers, int32_t world, int32_t rank, int64_t m,
                             int64_t n, int64_t k, coc_dtype dt, int32_t split, int32_t det,
-                            int32_t trans_w, void* stream) {
+                            int32_t trans_w, hipStream_t stream) {
     clear_error();
     Plan P;
     COC_TRY(make_plan(op, m, n, k, dt, world, rank, split, det, &P));
@@ -672,7 +711,9 @@ coc_status compute_first_op(coc_op op, const void* x, const void* w, const void*
     for (int r = 0; r < world; ++r) r0.src[r] = (r == rank) ? partial : peers[r];
     r0.dst = y;
     r0.n = n;
-    return run_compute_first(P, g0, r0, (hipStream_t)stream);
+    bool cap = false;
+    COC_TRY(capture_once(stream, &cap));
+    return run_compute_first(P, g0, r0, stream, cap);
 }
 
 // ------------------------------------------------------------------ expert all-to-all
@@ -841,6 +882,7 @@ coc_status run_moe_dispatch(const MoePlan& M, const void* const* src, const void
     L.ready = overlap ? a.ready : nullptr;
     L.order = 1;
     L.spin_limit = spin_limit_override();
+    L.gave_up = c->gave_up();
     const uint32_t off = target_offset();
     // the copy's adds happen either way: keep the running targets exact
     for (int p = 0; p < M.split; ++p) L.ready_target[p] = (c->ready_sent[p] += (uint32_t)per_chunk) + off;
@@ -880,14 +922,16 @@ coc_status run_moe_combine(const MoePlan& M, const void* h, const void* w, void*
     a.to_remote = 1;
     a.done = c->sync;
     a.spin_limit = spin_limit_override();
+    a.gave_up = c->gave_up();
     uint32_t per_piece[COC_MAX_SPLIT] = {};
     for (int i = 0; i < L.npieces; ++i) per_piece[M.group_chunk[i]] += (uint32_t)tiles[i];
     const uint32_t off = target_offset();
-    for (int p = 0; p < M.split; ++p) a.target[p] = (c->done_sent[p] += per_piece[p]) + off;
     COC_HIP(hipEventRecord(c->fork, main));
     COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
     int32_t launched[kMaxPieces + 1];
     COC_TRY(launch(KC_GEMM, moe_flops(M), main, [&] { return launch_gemm_chunks(L, main, launched); }));
+    // the matmul is enqueued: its adds will happen, so the running targets advance
+    for (int p = 0; p < M.split; ++p) a.target[p] = (c->done_sent[p] += per_piece[p]) + off;
     int32_t unused = 0;
     const double bytes = 2.0 * double(M.total) * double(M.n) * double(es);
     COC_TRY(launch(KC_GATHER, bytes, c->side, [&] { return launch_a2a_chunks(a, c->side, &unused); }));
@@ -896,53 +940,10 @@ coc_status run_moe_combine(const MoePlan& M, const void* h, const void* w, void*
     return chain.finish();
 }
 
-}  // namespace
-}  // namespace coc
-
-using namespace coc;
-
-extern "C" {
-
-coc_status coc_matmul_all_reduce(const void* x, const void* w, void* y, void* partial_out,
-                                 const void* const* peer_bufs, int32_t world, int32_t rank,
-                                 int64_t m, int64_t n, int64_t k, coc_dtype dt, int32_t split,
-                                 int32_t deterministic, int32_t trans_w, void* ws, size_t ws_bytes,
-                                 void* stream) {
-    (void)ws;
-    (void)ws_bytes;
-    return compute_first_op(COC_OP_MATMUL_ALL_REDUCE, x, w, nullptr, 0, 0, y, partial_out, peer_bufs,
-                            world, rank, m, n, k, dt, split, deterministic, trans_w, stream);
-}
-
-coc_status coc_matmul_reduce_scatter(const void* x, const void* w, void* y, void* partial_out,
-                                     const void* const* peer_bufs, int32_t world, int32_t rank,
-                                     int64_t m, int64_t n, int64_t k, coc_dtype dt, int32_t split,
-                                     int32_t deterministic, int32_t trans_w, void* ws,
-                                     size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
-    return compute_first_op(COC_OP_MATMUL_REDUCE_SCATTER, x, w, nullptr, 0, 0, y, partial_out,
-                            peer_bufs, world, rank, m, n, k, dt, split, deterministic, trans_w, stream);
-}
-
-coc_status coc_matmul_all_reduce_w8a16(const void* x_f16, const int8_t* w_q, const void* scales_f16,
-                                       coc_quant_mode mode, int32_t group_size, void* y_f16,
-                                       void* partial_out, const void* const* peer_bufs,
-                                       int32_t world, int32_t rank, int64_t m, int64_t n, int64_t k,
-                                       int32_t split, int32_t deterministic, void* ws,
-                                       size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
-    return compute_first_op(COC_OP_MATMUL_ALL_REDUCE_W8A16, x_f16, w_q, scales_f16, (int32_t)mode,
-                            group_size, y_f16, partial_out, peer_bufs, world, rank, m, n, k, COC_F16,
-                            split, deterministic, 0, stream);
-}
-
-coc_status coc_allgather_matmul(const void* x_shard, const void* const* peer_bufs, const void* w,
-                                void* y, void* gathered_out, int32_t world, int32_t rank, int64_t m,
-                                int64_t n, int64_t k, coc_dtype dt, int32_t split,
-                                int32_t deterministic, int32_t trans_w, void* ws, size_t ws_bytes,
-                                void* stream) {
+coc_status allgather_op(const void* x_shard, const void* const* peer_bufs, const void* w, void* y,
+                        void* gathered_out, int32_t world, int32_t rank, int64_t m, int64_t n, int64_t k,
+                        coc_dtype dt, int32_t split, int32_t deterministic, int32_t trans_w, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
     clear_error();
     const coc_op op = gathered_out ? COC_OP_ALLGATHER_MATMUL_V2 : COC_OP_ALLGATHER_MATMUL;
     Plan P;
@@ -989,11 +990,93 @@ coc_status coc_allgather_matmul(const void* x_shard, const void* const* peer_buf
     g0.n = n;
     g0.k = k;
     g0.trans_b = trans_w;
-    return run_comm_first(P, g0, a0, (hipStream_t)stream);
+    bool cap = false;
+    COC_TRY(capture_once(stream, &cap));
+    return run_comm_first(P, g0, a0, stream, cap);
+}
+
+
+}  // namespace
+}  // namespace coc
+
+using namespace coc;
+
+extern "C" {
+
+coc_status coc_matmul_all_reduce(const void* x, const void* w, void* y, void* partial_out,
+                                 const void* const* peer_bufs, int32_t world, int32_t rank,
+                                 int64_t m, int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                 int32_t deterministic, void* ws, size_t ws_bytes, hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return compute_first_op(COC_OP_MATMUL_ALL_REDUCE, x, w, nullptr, 0, 0, y, partial_out, peer_bufs,
+                            world, rank, m, n, k, dt, split, deterministic, 0, stream);
+}
+
+coc_status coc_matmul_all_reduce_trans_w(const void* x, const void* w, void* y, void* partial_out,
+                                         const void* const* peer_bufs, int32_t world, int32_t rank,
+                                         int64_t m, int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                         int32_t deterministic, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return compute_first_op(COC_OP_MATMUL_ALL_REDUCE, x, w, nullptr, 0, 0, y, partial_out, peer_bufs,
+                            world, rank, m, n, k, dt, split, deterministic, 1, stream);
+}
+
+coc_status coc_matmul_reduce_scatter(const void* x, const void* w, void* y, void* partial_out,
+                                     const void* const* peer_bufs, int32_t world, int32_t rank,
+                                     int64_t m, int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                     int32_t deterministic, void* ws, size_t ws_bytes, hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return compute_first_op(COC_OP_MATMUL_REDUCE_SCATTER, x, w, nullptr, 0, 0, y, partial_out,
+                            peer_bufs, world, rank, m, n, k, dt, split, deterministic, 0, stream);
+}
+
+coc_status coc_matmul_reduce_scatter_trans_w(const void* x, const void* w, void* y, void* partial_out,
+                                             const void* const* peer_bufs, int32_t world, int32_t rank,
+                                             int64_t m, int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                             int32_t deterministic, void* ws, size_t ws_bytes,
+                                             hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return compute_first_op(COC_OP_MATMUL_REDUCE_SCATTER, x, w, nullptr, 0, 0, y, partial_out,
+                            peer_bufs, world, rank, m, n, k, dt, split, deterministic, 1, stream);
+}
+
+coc_status coc_matmul_all_reduce_w8a16(const void* x_f16, const int8_t* w_q, const void* scales_f16,
+                                       coc_quant_mode mode, int32_t group_size, void* y_f16,
+                                       void* partial_out, const void* const* peer_bufs,
+                                       int32_t world, int32_t rank, int64_t m, int64_t n, int64_t k,
+                                       int32_t split, int32_t deterministic, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return compute_first_op(COC_OP_MATMUL_ALL_REDUCE_W8A16, x_f16, w_q, scales_f16, (int32_t)mode,
+                            group_size, y_f16, partial_out, peer_bufs, world, rank, m, n, k, COC_F16,
+                            split, deterministic, 0, stream);
+}
+
+coc_status coc_allgather_matmul(const void* x_shard, const void* const* peer_bufs, const void* w,
+                                void* y, void* gathered_out, int32_t world, int32_t rank, int64_t m,
+                                int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                int32_t deterministic, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return allgather_op(x_shard, peer_bufs, w, y, gathered_out, world, rank, m, n, k, dt, split, deterministic,
+                        0, ws, ws_bytes, stream);
+}
+
+coc_status coc_allgather_matmul_trans_w(const void* x_shard, const void* const* peer_bufs, const void* w,
+                                        void* y, void* gathered_out, int32_t world, int32_t rank, int64_t m,
+                                        int64_t n, int64_t k, coc_dtype dt, int32_t split,
+                                        int32_t deterministic, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+    return allgather_op(x_shard, peer_bufs, w, y, gathered_out, world, rank, m, n, k, dt, split, deterministic,
+                        1, ws, ws_bytes, stream);
 }
 
 coc_status coc_weight_grad(const void* g, const void* dy, void* dw, int64_t m, int64_t n, int64_t k,
-                           coc_dtype dt, void* stream) {
+                           coc_dtype dt, hipStream_t stream) {
     clear_error();
     if (dt != COC_BF16 && dt != COC_F16) return fail(COC_ERR_DTYPE, "weight gradient: bf16 or fp16 only");
     if (m < 0 || n < 0 || k < 0) return fail(COC_ERR_SHAPE, "negative size");
@@ -1031,15 +1114,16 @@ coc_status coc_weight_grad(const void* g, const void* dy, void* dw, int64_t m, i
     L.wait[0] = -1;
     L.signal[0] = -1;
     int32_t tiles[kMaxPieces + 1];
-    hipStream_t s = (hipStream_t)stream;
-    return launch(KC_GEMM, 2.0 * double(m) * double(n) * double(k), s,
-                  [&] { return launch_gemm_chunks(L, s, tiles); });
+    bool cap = false;
+    COC_TRY(capture_once(stream, &cap));
+    return launch(KC_GEMM, 2.0 * double(m) * double(n) * double(k), stream,
+                  [&] { return launch_gemm_chunks(L, stream, tiles); });
 }
 
 coc_status coc_alltoall_grouped_matmul(const void* x_own, const void* const* peer_bufs, const int64_t* counts,
                                        const void* w, void* y, void* recv_out, int32_t world, int32_t rank,
                                        int32_t experts, int64_t n, int64_t k, coc_dtype dt, int32_t split,
-                                       void* stream) {
+                                       hipStream_t stream) {
     clear_error();
     MoePlan M;
     COC_TRY(make_moe_plan(counts, world, rank, experts, n, k, dt, split, &M));
@@ -1070,13 +1154,13 @@ coc_status coc_alltoall_grouped_matmul(const void* x_own, const void* const* pee
     outs.push_back(mk(y, M.total * n * es, "y"));
     outs.push_back(mk(recv_out, M.total * k * es, "recv_out"));
     COC_TRY(check_alias(outs, ins));
-    return run_moe_dispatch(M, src, w, y, recv_out, (hipStream_t)stream);
+    return run_moe_dispatch(M, src, w, y, recv_out, stream);
 }
 
 coc_status coc_grouped_matmul_alltoall(const void* h, const void* w, void* y_local, void* y_own,
                                        void* const* peer_out, const int64_t* counts, int32_t world, int32_t rank,
                                        int32_t experts, int64_t n, int64_t k, coc_dtype dt, int32_t split,
-                                       void* stream) {
+                                       hipStream_t stream) {
     clear_error();
     MoePlan M;
     COC_TRY(make_moe_plan(counts, world, rank, experts, n, k, dt, split, &M));
@@ -1107,7 +1191,38 @@ coc_status coc_grouped_matmul_alltoall(const void* h, const void* w, void* y_loc
         dst[r] = pb;
     }
     COC_TRY(check_alias(outs, ins));
-    return run_moe_combine(M, h, w, y_local, dst, (hipStream_t)stream);
+    return run_moe_combine(M, h, w, y_local, dst, stream);
+}
+
+coc_status coc_check_waits(hipStream_t stream) {
+    clear_error();
+    bool cap = false;
+    COC_TRY(capturing(stream, &cap));
+    if (cap) return fail(COC_ERR_CAPTURE, "coc_check_waits reads device memory and cannot be captured");
+    int dev = 0;
+    COC_HIP(hipGetDevice(&dev));
+    StreamCtx* c = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_ctx_mu);
+        auto it = g_ctx.find(std::make_pair(dev, stream));
+        if (it != g_ctx.end()) c = it->second;
+    }
+    COC_HIP(hipStreamSynchronize(stream));
+    uint32_t* words[2] = {c != nullptr ? c->gave_up() : nullptr, static_gave_up(dev)};
+    bool gave_up = false;
+    for (uint32_t* w : words) {
+        if (w == nullptr) continue;
+        uint32_t v = 0;
+        COC_HIP(hipMemcpy(&v, w, sizeof v, hipMemcpyDeviceToHost));
+        if (v != 0) {
+            static const uint32_t zero = 0;
+            COC_HIP(hipMemcpy(w, &zero, sizeof zero, hipMemcpyHostToDevice));
+            gave_up = true;
+        }
+    }
+    if (gave_up)
+        return fail(COC_ERR_TIMEOUT, "a hand-over wait gave up: the rows or tiles it guarded were written as NaN");
+    return COC_OK;
 }
 
 void coc_profile_enable(int32_t on) { g_prof_on.store(on ? 1 : 0); }

@@ -129,6 +129,7 @@ struct ChunksLaunch {
     // last two rounds start on the first chunks (communicate first)
     int32_t order;
     uint32_t spin_limit;     // polls before a wait gives up (0: the default, about 2 s)
+    uint32_t* gave_up;       // set to non-zero by a wait that gives up (may be NULL)
     // All-gather rows that the launch's one-tile workgroups copy before their
     // tile (gather_nchunks > 0; see chunks_fused_gatherers): gathered row g of
     // chunk c's rows [gather_row0[c], + gather_rows[c]) comes from row
@@ -146,9 +147,12 @@ struct ChunksLaunch {
 // over kReadyLines lines from line COC_MAX_SPLIT + c * kReadyLines (gather
 // workgroup b adds to line b % kReadyLines, so its adds do not queue on one
 // address) and a waiter sums them.
+// The line after them holds the "gave up" word: a wait that gives up stores
+// a non-zero value into it (read and cleared by coc_check_waits).
 constexpr int kSyncWords = 32;
 constexpr int kReadyLines = 16;
-constexpr int kSyncLines = COC_MAX_SPLIT + COC_MAX_SPLIT * kReadyLines;
+constexpr int kGaveUpLine = COC_MAX_SPLIT + COC_MAX_SPLIT * kReadyLines;
+constexpr int kSyncLines = kGaveUpLine + 1;
 
 // The reduce that waits beside the one-launch matmul: every chunk in one
 // launch, chunk c's rows once done[c] reaches target[c].
@@ -161,6 +165,7 @@ struct ReduceChunksLaunch {
     int32_t own;             // index of the source the matmul is writing meanwhile
     bool narrow;             // one vector per thread: fits beside a matmul using more registers
     uint32_t spin_limit;     // polls before a wait gives up (0: the default, about 2 s)
+    uint32_t* gave_up;       // set to non-zero by a wait that gives up (may be NULL)
 };
 
 // The copy of an expert all-to-all, chunk by chunk.  Chunk c covers local
@@ -189,6 +194,7 @@ struct A2ALaunch {
     const uint32_t* done;       // combine: counter lines as above
     uint32_t target[COC_MAX_SPLIT];
     uint32_t spin_limit;        // polls before a wait gives up (0: the default, about 2 s)
+    uint32_t* gave_up;          // set to non-zero by a wait that gives up (may be NULL)
 };
 
 // Launchers (kernels.hip).  Return a hipError_t value (0 = success).  The

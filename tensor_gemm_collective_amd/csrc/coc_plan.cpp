@@ -187,17 +187,19 @@ const char* coc_status_string(coc_status s) {
         case COC_ERR_HIP: return "COC_ERR_HIP";
         case COC_ERR_ALIAS: return "COC_ERR_ALIAS";
         case COC_ERR_CAPTURE: return "COC_ERR_CAPTURE";
+        case COC_ERR_TIMEOUT: return "COC_ERR_TIMEOUT";
     }
     return "COC_ERR_UNKNOWN";
 }
 
 const char* coc_last_error(void) { return g_last_error.c_str(); }
 
-size_t coc_workspace_bytes(coc_op op, int64_t m, int64_t n, int64_t k, coc_dtype dt,
+size_t coc_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, coc_dtype dt,
                            int32_t world, int32_t split) {
+    if (op < COC_OP_MATMUL_ALL_REDUCE || op > COC_OP_MATMUL_ALL_REDUCE_W8A16) return 0;
     Plan p;
     const std::string saved = g_last_error;
-    coc_status s = make_plan(op, m, n, k, dt, world, 0, split, 0, &p);
+    coc_status s = make_plan((coc_op)op, m, n, k, dt, world, 0, split, 0, &p);
     g_last_error = saved;
     return s == COC_OK ? workspace_bytes(p) : 0;
 }

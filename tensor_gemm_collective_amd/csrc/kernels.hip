@@ -179,10 +179,15 @@ __device__ __forceinline__ bool spin_until(const uint32_t* p, int lines, uint32_
 // Workgroup-wide wait for the counters: thread 0 polls and the outcome goes to
 // every wave through LDS.  The barrier orders every later load after the
 // poll.  Two calls must be separated by a workgroup barrier (the flag is
-// reused).
-__device__ __forceinline__ bool wg_wait(const uint32_t* p, int lines, uint32_t target, uint32_t limit) {
+// reused).  A wait that gives up also stores 1 into *gave_up (if set), the
+// word the host reads back to report the time-out.
+__device__ __forceinline__ bool wg_wait(const uint32_t* p, int lines, uint32_t target, uint32_t limit,
+                                        uint32_t* gave_up) {
     __shared__ int ok;
-    if (threadIdx.x == 0) ok = spin_until(p, lines, target, limit) ? 1 : 0;
+    if (threadIdx.x == 0) {
+        ok = spin_until(p, lines, target, limit) ? 1 : 0;
+        if (!ok && gave_up != nullptr) __hip_atomic_store(gave_up, 1u, __ATOMIC_RELAXED, kSyncScope);
+    }
     __syncthreads();
     return ok != 0;
 }
@@ -1373,6 +1378,7 @@ struct PersistParams {
     int32_t npieces, per_xcd;
     int32_t order;   // 0: whole rounds in list order; 1: two-tile workgroups first (schedule_item)
     uint32_t spin_limit;   // polls before a wait gives up (the tile is then NaN)
+    uint32_t* gave_up;     // set by a wait that gives up (may be NULL)
     uint32_t* done;
     uint32_t* ready;
     FusedGather fg;
@@ -1437,7 +1443,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P
         grouped_coords(x * (T / NX) + (x < T % NX ? x : T % NX) + jj, P.tiles_m[c], tn_all, &tm, &tn);
         const int wi = P.wait[c];
         if (P.ready != nullptr && wi >= 0 && wi != waited) {
-            ok = wg_wait(P.ready + wi * kReadyLines * kSyncWords, kReadyLines, P.ready_target[wi], P.spin_limit);
+            ok = wg_wait(P.ready + wi * kReadyLines * kSyncWords, kReadyLines, P.ready_target[wi], P.spin_limit,
+                         P.gave_up);
             waited = wi;
         }
         // the previous tile's stores are done and every wave is off the LDS ring
@@ -1537,6 +1544,7 @@ struct ReduceChunks {
     const uint32_t* done;
     int32_t nchunks, own;
     uint32_t spin_limit;   // polls before a wait gives up (rows then NaN)
+    uint32_t* gave_up;     // set by a wait that gives up (may be NULL)
 };
 
 // Two sources are loaded at a time and added in rank order before the next
@@ -1659,7 +1667,7 @@ __global__ __launch_bounds__(256) void reduce_chunks_wait(ReduceParams p, Reduce
     const int stride = gridDim.x * 256;
     for (int c = 0; c < C.nchunks; ++c) {
         if (c > 0) __syncthreads();   // wg_wait's flag is reused
-        const bool ok = wg_wait(C.done + c * kSyncWords, 1, C.target[c], C.spin_limit);
+        const bool ok = wg_wait(C.done + c * kSyncWords, 1, C.target[c], C.spin_limit, C.gave_up);
         const int total = C.total[c];
         for (int v = blockIdx.x * 256 + threadIdx.x; v < total; v += U * stride) {
             const int v2 = v + stride;
@@ -1758,6 +1766,7 @@ struct A2AParams {
     const uint32_t* done;
     uint32_t target[COC_MAX_SPLIT];
     uint32_t spin_limit;
+    uint32_t* gave_up;     // set by a wait that gives up (may be NULL)
     uint32_t* ready;
     A2ASegment seg[kMaxA2ASegs];
 };
@@ -1820,7 +1829,7 @@ __global__ __launch_bounds__(256) void a2a_combine(A2AParams p) {
         bool ok = true;
         if (p.done != nullptr) {
             if (c > 0) __syncthreads();   // wg_wait's flag is reused
-            ok = wg_wait(p.done + c * kSyncWords, 1, p.target[c], p.spin_limit);
+            ok = wg_wait(p.done + c * kSyncWords, 1, p.target[c], p.spin_limit, p.gave_up);
         }
         const int total = p.total[c];
         int s = p.seg0[c];
@@ -2013,6 +2022,7 @@ int launch_reduce_chunks(const ReduceChunksLaunch& L, void* stream) {
     C.nchunks = L.nchunks;
     C.own = L.own;
     C.spin_limit = L.spin_limit > 0 ? L.spin_limit : kSpinLimit;
+    C.gave_up = L.gave_up;
     const int grid = grid_for(most) < 256 ? grid_for(most) : 256;   // at most one per CU
     hipStream_t s = (hipStream_t)stream;
     auto go = [&](auto DTC) {
@@ -2101,6 +2111,7 @@ int launch_a2a_chunks(const A2ALaunch& a, void* stream, int32_t* per_chunk) {
     p.done = a.done;
     for (int c = 0; c < COC_MAX_SPLIT; ++c) p.target[c] = a.target[c];
     p.spin_limit = a.spin_limit > 0 ? a.spin_limit : kSpinLimit;
+    p.gave_up = a.gave_up;
     p.ready = a.ready;
     hipStream_t s = (hipStream_t)stream;
     if (a.to_remote == 0) {
@@ -2188,6 +2199,7 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     P.npieces = L.npieces;
     P.order = L.order;
     P.spin_limit = L.spin_limit > 0 ? L.spin_limit : kSpinLimit;
+    P.gave_up = L.gave_up;
     bool signal = false;
     int per_cu_chk = 0;
     P.per_xcd = chunks_layout(L, tiles, &per_cu_chk);

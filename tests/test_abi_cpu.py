@@ -165,9 +165,10 @@ def _ar(**kw):
                 world=8, rank=0, m=64, n=64, k=64, dt=tgc.COC_BF16, split=4, det=0, tw=0)
     args.update(kw)
     L = tgc.lib()
-    return L.coc_matmul_all_reduce(args["x"], args["w"], args["y"], args["p"], args["peers"],
-                                   args["world"], args["rank"], args["m"], args["n"], args["k"],
-                                   args["dt"], args["split"], args["det"], args["tw"], None, 0, None)
+    fn = L.coc_matmul_all_reduce_trans_w if args["tw"] else L.coc_matmul_all_reduce
+    return fn(args["x"], args["w"], args["y"], args["p"], args["peers"],
+              args["world"], args["rank"], args["m"], args["n"], args["k"],
+              args["dt"], args["split"], args["det"], None, 0, None)
 
 
 @no_gpu_only
@@ -236,7 +237,7 @@ def test_allgather_rejects():
 
     def call(gathered=None, ws=None, ws_bytes=0, m=64, split=4):
         return L.coc_allgather_matmul(_addr(1), _peers(8, 0), _addr(2) * 16, _addr(3) * 256, gathered,
-                                      8, 0, m, 64, 64, tgc.COC_BF16, split, 0, 0, ws, ws_bytes, None)
+                                      8, 0, m, 64, 64, tgc.COC_BF16, split, 0, ws, ws_bytes, None)
     assert call() == 7                                   # no workspace for the non-V2 form
     assert call(ws=_addr(5) * 512, ws_bytes=100) == 7    # too small
     assert call(ws=_addr(5) * 512 + 8, ws_bytes=1 << 20) == 6

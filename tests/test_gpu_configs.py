@@ -1,8 +1,19 @@
 """Parity at the full workload sizes (one TP8 rank of BLOOM-7B, LLaMA2-70B,
 BLOOM-176B, the w8A16 case), in the pipelined launch configurations the
-benchmark uses.  The oracle computes sampled output rows one by one (float64);
-whole-tensor properties are checked on the GPU: bit-exact gather, deterministic
-bits identical across splits and repeated runs.
+benchmark uses.  Every element of every output is compared with the oracle
+(float64 definitions, computed once per workload and shared by the cases):
+
+* normwise relative error of y and partial_out over the whole tensor
+  (5e-3 for bf16 / fp16);
+* the gathered matrix bit for bit against the concatenated shards;
+* in deterministic mode, y bit for bit against the oracle's fixed-order
+  emulation of the stored partial_out and the peers' partials (ascending rank
+  order, binary32 adds, one rounding), at every split, and identical over
+  repeated runs;
+* BLOOM-7B end to end with true shard peers: the other ranks' partials are
+  the oracle's products of their own K shards, and y is compared with the
+  unsplit full-K product X_full @ W_full (split-K invariance through the
+  whole pipeline).
 """
 import numpy as np
 import pytest
@@ -11,20 +22,10 @@ import torch
 import oracle
 import tensor_gemm_collective_amd as tgc
 from tensor_gemm_collective_amd import synth
-from tests._util import TORCH_DT, assert_bits_equal, assert_close, f64, log
+from tests._util import assert_bits_equal, assert_close, encode_dtype, f64, log, raw
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-
-
-def sample_rows(m, chunks, n=48, seed=0):
-    """Rows spread over every chunk, plus each chunk's first and last row."""
-    rng = np.random.default_rng(seed)
-    rows = set(rng.choice(m, size=min(n, m), replace=False).tolist())
-    step = m // chunks
-    for c in range(chunks):
-        rows.update((c * step, c * step + step - 1))
-    return np.array(sorted(rows))
 
 
 def _peers_full(wl, world, rank, dtype):
@@ -32,8 +33,24 @@ def _peers_full(wl, world, rank, dtype):
             for r in range(world)]
 
 
-def _f64_rows(t, rows, dtype):
-    return f64(t[torch.as_tensor(rows)], dtype)
+def _dev_list(ts):
+    return [None if t is None else t.to(DEV) for t in ts]
+
+
+def _torch_from_oracle(x64, dtype):
+    """A tensor holding the oracle's rounding of float64 values (an input the
+    oracle computed, never the library)."""
+    bits = encode_dtype(x64, dtype)
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+
+
+def assert_fixed_order(y, partial_out, peers, rank, dtype, what):
+    """y bit for bit against the oracle's deterministic emulation, with this
+    rank's own partial taken as the library stored it."""
+    parts = [f64(partial_out, dtype) if r == rank else f64(p, dtype) for r, p in enumerate(peers)]
+    want = oracle.reduce_fixed_order(parts, dtype)
+    assert_bits_equal(y, encode_dtype(want, dtype), what)
 
 
 # ------------------------------------------------------------------ BLOOM-7B all-reduce
@@ -43,29 +60,29 @@ def bloom7b():
     x = synth.normal(wl.wid, synth.T_X, 0, (wl.m, wl.k), wl.x_sigma, "bf16")
     w = synth.normal(wl.wid, synth.T_W, 0, (wl.k, wl.n), wl.w_sigma, "bf16")
     peers = _peers_full(wl, wl.world, 0, "bf16")
-    return wl, x, w, peers
+    y_ref, p_ref = oracle.matmul_all_reduce(f64(x, "bf16"), f64(w, "bf16"),
+                                            [None if p is None else f64(p, "bf16") for p in peers], 0)
+    return wl, x, w, peers, y_ref, p_ref
 
 
 @pytest.mark.parametrize("split", [4, 2, 8])
 def test_bloom7b_all_reduce(bloom7b, split):
-    wl, x, w, peers = bloom7b
+    wl, x, w, peers, y_ref, p_ref = bloom7b
     log(f"BLOOM-7B AR bf16 {wl.m}x{wl.k}x{wl.n} split={split}")
-    xd, wd, pd = x.to(DEV), w.to(DEV), [None if p is None else p.to(DEV) for p in peers]
-    rows = sample_rows(wl.m, split)
-    wf = f64(w, "bf16")
+    xd, wd, pd = x.to(DEV), w.to(DEV), _dev_list(peers)
     for det in (0, 1):
         y, p = tgc.matmul_all_reduce(xd, wd, pd, 0, split=split, deterministic=det)
         torch.cuda.synchronize()
-        y_ref, p_ref = oracle.matmul_all_reduce(
-            _f64_rows(x, rows, "bf16"), wf, [None if q is None else _f64_rows(q, rows, "bf16") for q in peers], 0)
-        assert_close(p[torch.as_tensor(rows)], p_ref, "bf16", "partial_out (sampled rows)")
-        assert_close(y[torch.as_tensor(rows)], y_ref, "bf16", f"y det={det} (sampled rows)")
+        assert_close(p, p_ref, "bf16", "partial_out")
+        assert_close(y, y_ref, "bf16", f"y det={det}")
+        if det:
+            assert_fixed_order(y, p, peers, 0, "bf16", f"y det split={split} vs the fixed-order emulation")
 
 
 def test_bloom7b_deterministic_across_splits(bloom7b):
-    wl, x, w, peers = bloom7b
+    wl, x, w, peers, _, _ = bloom7b
     log("BLOOM-7B AR det bits across splits 2/4/8")
-    xd, wd, pd = x.to(DEV), w.to(DEV), [None if p is None else p.to(DEV) for p in peers]
+    xd, wd, pd = x.to(DEV), w.to(DEV), _dev_list(peers)
     ref = None
     for split in (2, 4, 8):
         y, _ = tgc.matmul_all_reduce(xd, wd, pd, 0, split=split, deterministic=1)
@@ -76,6 +93,28 @@ def test_bloom7b_deterministic_across_splits(bloom7b):
             assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), f"split {split}"
 
 
+@pytest.mark.parametrize("det", [0, 1])
+def test_bloom7b_end_to_end_split_k(det):
+    """The RowParallel layer of one TP8 group: rank r holds K shard r of
+    X_full (2048 x 16384) and of W_full (16384 x 4096); the peers' partials
+    are the oracle's bf16 products of their own shards.  y must match the
+    unsplit product X_full @ W_full."""
+    wl = synth.WORKLOADS["bloom7b_ar"]
+    log(f"BLOOM-7B AR end to end with true shard peers det={det}")
+    xs = [synth.normal(wl.wid, synth.T_X if r == 0 else synth.T_PEER, r, (wl.m, wl.k), wl.x_sigma, "bf16")
+          for r in range(wl.world)]
+    ws = [synth.normal(wl.wid, synth.T_W if r == 0 else synth.T_PEER_W, r, (wl.k, wl.n), wl.w_sigma, "bf16")
+          for r in range(wl.world)]
+    xf = [f64(t, "bf16") for t in xs]
+    wf = [f64(t, "bf16") for t in ws]
+    peers = [None] + [_torch_from_oracle(oracle.matmul(xf[r], wf[r]), "bf16") for r in range(1, wl.world)]
+    y, p = tgc.matmul_all_reduce(xs[0].to(DEV), ws[0].to(DEV), _dev_list(peers), 0, split=4, deterministic=det)
+    torch.cuda.synchronize()
+    full = oracle.matmul(np.hstack(xf), np.vstack(wf))
+    assert_close(y, full, "bf16", "y vs the unsplit full-K product")
+    assert_close(p, oracle.matmul(xf[0], wf[0]), "bf16", "partial_out")
+
+
 # ------------------------------------------------------------------ LLaMA2-70B all-gather matmul
 @pytest.fixture(scope="module")
 def llama_ag():
@@ -83,13 +122,15 @@ def llama_ag():
     shard = wl.m // wl.world
     shards = [synth.normal(wl.wid, synth.T_PEER, r, (shard, wl.k), wl.x_sigma, "bf16") for r in range(wl.world)]
     w = synth.normal(wl.wid, synth.T_W, 0, (wl.k, wl.n), wl.w_sigma, "bf16")
-    return wl, shards, w
+    G = oracle.allgather([f64(s, "bf16") for s in shards])
+    y_ref = oracle.matmul(G, f64(w, "bf16"))
+    return wl, shards, w, G, y_ref
 
 
 @pytest.mark.parametrize("split", [4, 8])
 @pytest.mark.parametrize("rank", [0, 3])
 def test_llama_allgather_matmul(llama_ag, split, rank):
-    wl, shards, w = llama_ag
+    wl, shards, w, _, y_ref = llama_ag
     log(f"LLaMA2-70B AG bf16 m={wl.m} k={wl.k} n={wl.n} split={split} rank={rank}")
     sd = [s.to(DEV) for s in shards]
     peers = [None if r == rank else sd[r] for r in range(wl.world)]
@@ -99,9 +140,7 @@ def test_llama_allgather_matmul(llama_ag, split, rank):
     torch.cuda.synchronize()
     assert torch.equal(g.view(torch.int16), torch.cat(sd).view(torch.int16)), "gathered rows differ"
     assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), "V2 and plain results differ"
-    rows = sample_rows(wl.m, split, seed=split + rank)
-    g_rows = oracle.allgather([f64(s, "bf16") for s in shards])[rows]
-    assert_close(y[torch.as_tensor(rows)], oracle.matmul(g_rows, f64(w, "bf16")), "bf16", "y (sampled rows)")
+    assert_close(y, y_ref, "bf16", "y")
 
 
 # ------------------------------------------------------------------ LLaMA2-70B backward of the pair
@@ -110,7 +149,7 @@ def test_llama_backward_pair(llama_ag):
     gate/up layer from V2's gathered G (8192 x 7168), and the dX of the down
     projection, AG(dY) @ W^T, with the 3584 x 8192 forward weight read
     transposed (reduction 8192, output 3584)."""
-    wl, shards, w = llama_ag
+    wl, shards, w, G, _ = llama_ag
     rank = 2
     log(f"LLaMA2-70B backward: weight_grad {wl.k}x{wl.n} over m={wl.m}; AG dX with transposed weights")
     sd = [s.to(DEV) for s in shards]
@@ -124,12 +163,9 @@ def test_llama_backward_pair(llama_ag):
     dx = tgc.allgather_matmul(dys[rank].to(DEV), dpeers, w_down.to(DEV), rank, split=4, trans_w=True)
     torch.cuda.synchronize()
     assert dw.shape == (wl.k, wl.n) and dx.shape == (wl.m, 3584)
-    rows = sample_rows(wl.k, 8, n=24, seed=21)
-    G = oracle.allgather([f64(s, "bf16") for s in shards])
-    assert_close(dw[torch.as_tensor(rows)], oracle.weight_grad(G[:, rows], f64(dy, "bf16")), "bf16", "dW rows")
-    rows = sample_rows(wl.m, 4, n=24, seed=22)
+    assert_close(dw, oracle.weight_grad(G, f64(dy, "bf16")), "bf16", "dW")
     DY = oracle.allgather([f64(d, "bf16") for d in dys])
-    assert_close(dx[torch.as_tensor(rows)], oracle.matmul(DY[rows], f64(w_down, "bf16").T), "bf16", "dX rows")
+    assert_close(dx, oracle.matmul(DY, f64(w_down, "bf16").T), "bf16", "dX")
 
 
 # ------------------------------------------------------------------ LLaMA2-70B matmul reduce-scatter
@@ -142,7 +178,12 @@ def llama_rs():
     w = synth.normal(wl.wid, synth.T_W, rank, (wl.k, wl.n), wl.w_sigma, "bf16")
     slices = [None if r == rank else synth.normal(wl.wid, synth.T_PEER, r, (b, wl.n), wl.peer_sigma, "bf16")
               for r in range(wl.world)]
-    return wl, rank, x, w, slices
+    p_ref = oracle.matmul(f64(x, "bf16"), f64(w, "bf16"))
+    y_ref = p_ref[rank * b:(rank + 1) * b].copy()
+    for s in slices:
+        if s is not None:
+            y_ref += f64(s, "bf16")
+    return wl, rank, x, w, slices, p_ref, y_ref
 
 
 def _rs_peers_dev(wl, rank, slices):
@@ -159,12 +200,10 @@ def _rs_peers_dev(wl, rank, slices):
 
 
 def test_llama_reduce_scatter(llama_rs):
-    wl, rank, x, w, slices = llama_rs
+    wl, rank, x, w, slices, p_ref, y_ref = llama_rs
     b = wl.m // wl.world
     peers = _rs_peers_dev(wl, rank, slices)
     xd, wd = x.to(DEV), w.to(DEV)
-    wf = f64(w, "bf16")
-    local = sample_rows(b, 8, n=40, seed=7)
     ref = None
     for split in (4, 8):
         log(f"LLaMA2-70B RS bf16 m={wl.m} k={wl.k} n={wl.n} split={split} rank={rank}")
@@ -172,16 +211,12 @@ def test_llama_reduce_scatter(llama_rs):
             y, p = tgc.matmul_reduce_scatter(xd, wd, peers, rank, split=split, deterministic=det)
             torch.cuda.synchronize()
             assert torch.isfinite(y.float()).all(), "NaN from an unread peer row leaked in"
-            # rows j of this rank's slice are rows rank*b + j of the all-reduced sum
-            glob = rank * b + local
-            y_ref, _ = oracle.matmul_all_reduce(
-                _f64_rows(x, glob, "bf16"), wf,
-                [None if sl is None else _f64_rows(sl, local, "bf16") for sl in slices], rank)
-            assert_close(y[torch.as_tensor(local)], y_ref, "bf16", f"y split={split} det={det}")
-            prow = sample_rows(wl.m, split, n=24, seed=split)
-            assert_close(p[torch.as_tensor(prow)], oracle.matmul(_f64_rows(x, prow, "bf16"), wf), "bf16",
-                         "partial_out")
+            assert_close(y, y_ref, "bf16", f"y split={split} det={det}")
+            assert_close(p, p_ref, "bf16", f"partial_out split={split} det={det}")
             if det:
+                own = p[rank * b:(rank + 1) * b]
+                assert_fixed_order(y, own, [None if s is None else s for s in slices], rank, "bf16",
+                                   f"y det split={split} vs the fixed-order emulation")
                 if ref is None:
                     ref = y.clone()
                 else:
@@ -190,14 +225,18 @@ def test_llama_reduce_scatter(llama_rs):
 
 # ------------------------------------------------------------------ BLOOM-176B deterministic all-reduce
 def test_bloom176b_deterministic():
+    """The deterministic variant at full size: y bit for bit against the
+    fixed-order emulation at splits 2, 4 and 8, identical over 10 runs, and
+    y / partial_out against the exact float64 result over the whole tensor."""
     wl = synth.WORKLOADS["bloom176b_ar"]
-    log(f"BLOOM-176B AR bf16 det m={wl.m} k={wl.k} n={wl.n}")
     x = synth.normal(wl.wid, synth.T_X, 0, (wl.m, wl.k), wl.x_sigma, "bf16")
     w = synth.normal(wl.wid, synth.T_W, 0, (wl.k, wl.n), wl.w_sigma, "bf16")
     peers = _peers_full(wl, wl.world, 0, "bf16")
-    xd, wd, pd = x.to(DEV), w.to(DEV), [None if p is None else p.to(DEV) for p in peers]
+    xd, wd, pd = x.to(DEV), w.to(DEV), _dev_list(peers)
+    peers64 = [None if q is None else f64(q, "bf16") for q in peers]
     ref = None
     for split in (2, 4, 8):
+        log(f"BLOOM-176B AR bf16 det m={wl.m} k={wl.k} n={wl.n} split={split}")
         runs = 10 if split == 4 else 1
         for run in range(runs):
             y, p = tgc.matmul_all_reduce(xd, wd, pd, 0, split=split, deterministic=1)
@@ -207,11 +246,12 @@ def test_bloom176b_deterministic():
             else:
                 assert torch.equal(y.view(torch.int16), ref[0].view(torch.int16)), f"y split={split} run={run}"
                 assert torch.equal(p.view(torch.int16), ref[1].view(torch.int16)), f"partial split={split} run={run}"
-    rows = sample_rows(wl.m, 8, n=32, seed=3)
-    y_ref, p_ref = oracle.matmul_all_reduce(
-        _f64_rows(x, rows, "bf16"), f64(w, "bf16"), [None if q is None else _f64_rows(q, rows, "bf16") for q in peers], 0)
-    assert_close(ref[1][torch.as_tensor(rows)], p_ref, "bf16", "partial_out (sampled rows)")
-    assert_close(ref[0][torch.as_tensor(rows)], y_ref, "bf16", "y (sampled rows)")
+        parts = [f64(p, "bf16")] + peers64[1:]
+        assert_bits_equal(y, encode_dtype(oracle.reduce_fixed_order(parts, "bf16"), "bf16"),
+                          f"y split={split} vs the fixed-order emulation")
+    y_ref, p_ref = oracle.matmul_all_reduce(f64(x, "bf16"), f64(w, "bf16"), peers64, 0)
+    assert_close(ref[1], p_ref, "bf16", "partial_out")
+    assert_close(ref[0], y_ref, "bf16", "y")
 
 
 # ------------------------------------------------------------------ w8A16
@@ -224,13 +264,14 @@ def test_w8a16_full(mode):
     shape = {"per_tensor": (1,), "per_channel": (wl.n,), "per_group": (wl.k // wl.group, wl.n)}[mode]
     s = synth.fp16_scales(wl.wid, 0, shape)
     peers = _peers_full(wl, wl.world, 0, "f16")
-    y, p = tgc.matmul_all_reduce_w8a16(x.to(DEV), q.to(DEV), s.to(DEV), mode,
-                                       [None if t is None else t.to(DEV) for t in peers], 0,
-                                       group_size=wl.group, split=4)
-    torch.cuda.synchronize()
-    rows = sample_rows(wl.m, 4, n=40, seed=11)
+    pd = _dev_list(peers)
     wt = oracle.dequant_weight(q.numpy(), f64(s, "f16"), mode, wl.group)
-    y_ref, p_ref = oracle.matmul_all_reduce(
-        _f64_rows(x, rows, "f16"), wt, [None if t is None else _f64_rows(t, rows, "f16") for t in peers], 0)
-    assert_close(p[torch.as_tensor(rows)], p_ref, "f16", "partial_out (sampled rows)")
-    assert_close(y[torch.as_tensor(rows)], y_ref, "f16", "y (sampled rows)")
+    y_ref, p_ref = oracle.matmul_all_reduce(f64(x, "f16"), wt, [None if t is None else f64(t, "f16") for t in peers], 0)
+    for det in (0, 1):
+        y, p = tgc.matmul_all_reduce_w8a16(x.to(DEV), q.to(DEV), s.to(DEV), mode, pd, 0,
+                                           group_size=wl.group, split=4, deterministic=det)
+        torch.cuda.synchronize()
+        assert_close(p, p_ref, "f16", f"partial_out det={det}")
+        assert_close(y, y_ref, "f16", f"y det={det}")
+        if det:
+            assert_fixed_order(y, p, peers, 0, "f16", "y det vs the fixed-order emulation")

@@ -148,3 +148,37 @@ def test_capture_refusals():
             tgc.alltoall_grouped_matmul(own, mp, counts, wm, wl.rank, y=ym, recv_out=recv)
     assert ei.value.status_name == "COC_ERR_CAPTURE"
     torch.cuda.synchronize()
+
+
+def test_second_call_in_one_capture_refused():
+    """One capture holds at most one call of the library: a second call while
+    the same capture is open (here the reduce-scatter after the all-reduce) is
+    refused with COC_ERR_CAPTURE and enqueues nothing.  The graph then holds
+    the first call alone and replays it exactly; the refused call's outputs
+    are never written."""
+    log("second call in one capture refused")
+    dtype, m, n, k, world, rank, split = "bf16", 1024, 512, 256, 8, 3, 4
+    x = dev(synth.normal(WID + 4, synth.T_X, 0, (m, k), 1.0, dtype))
+    w = dev(synth.normal(WID + 4, synth.T_W, rank, (k, n), 0.05, dtype))
+    peers = [None if q is None else dev(q) for q in synth.peers_random(WID + 4, world, rank, (m, n), 0.4, dtype)]
+    y = torch.empty((m, n), dtype=TORCH_DT[dtype], device="cuda")
+    p = torch.empty((m, n), dtype=TORCH_DT[dtype], device="cuda")
+    y2 = torch.zeros((m // world, n), dtype=TORCH_DT[dtype], device="cuda")
+    p2 = torch.zeros((m, n), dtype=TORCH_DT[dtype], device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        want_y, want_p = tgc.matmul_all_reduce(x, w, peers, rank, split=split, deterministic=1)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        tgc.matmul_all_reduce(x, w, peers, rank, y=y, partial_out=p, split=split, deterministic=1)
+        with pytest.raises(tgc.CocError) as ei:
+            tgc.matmul_reduce_scatter(x, w, peers, rank, y=y2, partial_out=p2, split=split, deterministic=1)
+    assert ei.value.status_name == "COC_ERR_CAPTURE"
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(y, want_y, "captured all-reduce y")
+        assert_bits_equal(p, want_p, "captured all-reduce partial")
+    assert not y2.any() and not p2.any(), "the refused call wrote its outputs"

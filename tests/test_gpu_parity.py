@@ -542,6 +542,11 @@ def test_bounded_wait_gives_up_to_nan(monkeypatch):
     assert torch.isnan(y2[:2 * q].float()).all(), "chunks reduced beside the matmul must be NaN"
     assert_bits_equal(y2[2 * q:], ref2[2 * q:], "chunks reduced after the matmul (no wait)")
     assert torch.isfinite(p2.float()).all()
+    # the host sees the time-out, once: the check clears the record
+    with pytest.raises(tgc.CocError) as ei:
+        tgc.check_waits()
+    assert ei.value.status_name == "COC_ERR_TIMEOUT"
+    tgc.check_waits()
 
     monkeypatch.delenv("COC_SPIN_LIMIT")
     monkeypatch.delenv("COC_TEST_UNREACHABLE_WAIT")
@@ -551,6 +556,7 @@ def test_bounded_wait_gives_up_to_nan(monkeypatch):
     torch.cuda.synchronize()
     assert_bits_equal(y, ref, "all-gather matmul after the forced time-out")
     assert_bits_equal(y2, ref2, "reduce-scatter after the forced time-out")
+    tgc.check_waits()   # no wait gave up this time
 
 
 def test_waiting_calls_from_two_streams_at_once():
