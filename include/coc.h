@@ -245,6 +245,29 @@ coc_status coc_allgather_matmul_trans_w(const void* x_shard, const void* const* 
                                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Allocation-free ALL_GATHER_MATMUL, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the plain ALL_GATHER_MATMUL above (same arguments,
+ * same result bits) with the gathered matrix G and the pipeline's hand-over
+ * counters held in a static device array of the library instead of a caller
+ * workspace and the library's per-stream allocation.  The call allocates
+ * nothing and creates no stream or event: all its work goes to `stream`.
+ *
+ * Limit: m * k * element size <= 64 MiB (the LLaMA2-70B TP8 gather, 4096 x
+ * 8192 bf16, is exactly that); larger problems return COC_ERR_WORKSPACE.
+ * The array (64 MiB + 32 KiB) is held on every GPU the library runs on until
+ * the process ends.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (from different streams or threads, or while
+ * another such call's work is still running on another stream) race and
+ * must be ordered by the caller; calls on one stream are ordered by it.
+ * Its waits report through coc_check_waits() like the other calls'.
+ */
+coc_status coc_allgather_matmul_noalloc(const void* x_shard, const void* const* peer_bufs, const void* w,
+                                        void* y, int32_t world, int32_t rank,
+                                        int64_t m, int64_t n, int64_t k, coc_dtype dt,
+                                        int32_t split, int32_t deterministic, hipStream_t stream);
+
+/*
  * Weight gradient of the sequence-parallel pair (CoC guide, "Approach": the
  * fused operators come in forward / backward pairs, and V2 hands back the
  * all-gathered G so that the backward pass can reuse it):

@@ -14,6 +14,7 @@ from .coc import (  # noqa: F401
     matmul_all_reduce,
     matmul_reduce_scatter,
     allgather_matmul,
+    allgather_matmul_noalloc,
     matmul_all_reduce_w8a16,
     weight_grad,
     alltoall_grouped_matmul,

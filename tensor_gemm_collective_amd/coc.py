@@ -34,7 +34,7 @@ KCLASS = ("gemm", "reduce", "gather")
 EXPORTS = (
     "coc_matmul_all_reduce", "coc_matmul_reduce_scatter", "coc_allgather_matmul",
     "coc_matmul_all_reduce_w8a16", "coc_matmul_all_reduce_trans_w", "coc_matmul_reduce_scatter_trans_w",
-    "coc_allgather_matmul_trans_w", "coc_weight_grad", "coc_alltoall_grouped_matmul",
+    "coc_allgather_matmul_trans_w", "coc_allgather_matmul_noalloc", "coc_weight_grad", "coc_alltoall_grouped_matmul",
     "coc_grouped_matmul_alltoall", "coc_workspace_bytes", "coc_status_string",
     "coc_last_error", "coc_check_waits", "coc_plan", "coc_profile_enable", "coc_profile_read",
     "coc_profile_records",
@@ -90,6 +90,9 @@ def lib() -> ctypes.CDLL:
               "coc_allgather_matmul_trans_w", "coc_matmul_all_reduce_w8a16", "coc_weight_grad",
               "coc_alltoall_grouped_matmul", "coc_grouped_matmul_alltoall"):
         getattr(L, f).restype = _i32
+    L.coc_allgather_matmul_noalloc.argtypes = [_vp, ctypes.POINTER(_vp), _vp, _vp, _i32, _i32, _i64, _i64, _i64,
+                                               _i32, _i32, _i32, _vp]
+    L.coc_allgather_matmul_noalloc.restype = _i32
     L.coc_check_waits.argtypes = [_vp]
     L.coc_check_waits.restype = _i32
     L.coc_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64, _i32, _i32, _i32]
@@ -216,6 +219,21 @@ def allgather_matmul(x_shard, peers, w, rank, *, y=None, gathered_out=None, v2=F
         world, rank, m, n, k, _dtype_code(x_shard), split, int(bool(deterministic)),
         _ptr(ws) if not v2 else None, ws_bytes, _stream(stream, x_shard.device)))
     return (y, gathered_out) if v2 else y
+
+
+def allgather_matmul_noalloc(x_shard, peers, w, rank, *, y=None, split=4, deterministic=False, stream=None):
+    """ALL_GATHER_MATMUL through the allocation-free entry point: the gathered
+    matrix and the counters live in the library's static device array
+    (m x k x element size <= 64 MiB).  Returns y."""
+    world = len(peers)
+    shard, k = x_shard.shape
+    m = shard * world
+    n = w.shape[1]
+    y = _empty((m, n), x_shard) if y is None else y
+    _check(lib().coc_allgather_matmul_noalloc(
+        _ptr(x_shard), _peer_array(peers, rank), _ptr(w), _ptr(y), world, rank, m, n, k, _dtype_code(x_shard),
+        split, int(bool(deterministic)), _stream(stream, x_shard.device)))
+    return y
 
 
 def weight_grad(g, dy, *, dw=None, stream=None):

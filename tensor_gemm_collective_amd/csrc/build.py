@@ -21,8 +21,10 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(PKG, "libcoc.so")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["kernels.hip"]
-HOST_SOURCES = ["coc_plan.cpp", "coc_api.cpp"]
+# coc_api.cpp holds host code and one device array (the allocation-free entry
+# point's scratch memory), so it takes the device pass as well.
+DEVICE_SOURCES = ["kernels.hip", "coc_api.cpp"]
+HOST_SOURCES = ["coc_plan.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{HERE}"]
 # Device code: gfx950 only, packed-fp32 instructions disabled.

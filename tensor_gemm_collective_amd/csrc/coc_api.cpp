@@ -17,7 +17,7 @@
 // from and joined back into the caller's stream with events, so a call is
 // ordered like a single kernel on that stream.  split == 1 is the serial
 // baseline: everything on the caller's stream.
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cstdlib>
@@ -144,11 +144,57 @@ coc_status capture_once(hipStream_t s, bool* cap) {
     return COC_OK;
 }
 
-// The gave-up word of the allocation-free entry points' counters on device
-// `dev`, or NULL while they have not been set up there.
+// ------------------------------------------------------------------ scratch memory
+// The allocation-free all-gather matmul (coc_allgather_matmul_noalloc) keeps
+// what the plain one takes from the caller's workspace (the gathered matrix)
+// and from the library's per-stream allocation (the hand-over counters) in
+// `scratch`, a file-scope device array that every GPU the library runs on
+// holds until the process ends.  Layout: the counter lines (kSyncLines lines
+// of 128 bytes, the same layout as a stream context's) from offset 0, then
+// the gathered matrix from kScratchGatherOffset (128-byte aligned, as the
+// one-launch all-gather needs), at most kScratchGatherBytes.  In host code
+// the array's name only stands for the symbol: its device address, one per
+// GPU, comes from hipGetSymbolAddress on that GPU.
+constexpr size_t kScratchGatherOffset = size_t(32) << 10;
+constexpr size_t kScratchGatherBytes = size_t(64) << 20;
+static_assert(size_t(kSyncLines) * kSyncWords * sizeof(uint32_t) <= kScratchGatherOffset,
+              "the counter lines fit before the gathered matrix");
+
+}  // namespace
+}  // namespace coc
+
+static __device__ __align__(256) uint8_t scratch[coc::kScratchGatherOffset + coc::kScratchGatherBytes];
+
+namespace coc {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[kMaxDevices] = {};   // the address of `scratch` on each device, once set up
+
+// The address of `scratch` on the current device: looked up with that device
+// current on its first use there, then kept.
+coc_status scratch_base(uint8_t** out) {
+    int dev = 0;
+    COC_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(COC_ERR_HIP, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        COC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (p == nullptr) return fail(COC_ERR_HIP, "hipGetSymbolAddress returned no address for the scratch array");
+        g_scratch[dev] = (uint8_t*)p;
+    }
+    *out = g_scratch[dev];
+    return COC_OK;
+}
+
+// The gave-up word of the scratch counters on device `dev`, or NULL while
+// they have not been set up there.
 uint32_t* static_gave_up(int dev) {
-    (void)dev;
-    return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    return g_scratch[dev] ? (uint32_t*)g_scratch[dev] + kGaveUpLine * kSyncWords : nullptr;
 }
 
 coc_status get_ctx(hipStream_t main, StreamCtx** out) {
@@ -487,13 +533,12 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
 // shard, read straight from x_shard (nothing to wait for), then each chunk's
 // other rows from the gathered matrix once that chunk's gather is counted
 // complete.
-coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const GatherLaunch& a0,
-                                 hipStream_t main) {
-    StreamCtx* c = nullptr;
-    COC_TRY(get_ctx(main, &c));
-    ChainedCall chain;
-    COC_TRY(chain.begin(c, main));
-    const size_t es = elem_size(P.dt);
+// The matmul launch of the one-launch all-gather pipeline: this rank's own
+// shard first, read straight from x_shard, then each chunk's rows outside
+// it from the gathered matrix, each piece waiting for its chunk's ready
+// lines at `ready`.  grow0 / grows receive each chunk's gathered rows.
+ChunksLaunch comm_first_launch(const Plan& P, const GemmLaunch& g0, const GatherLaunch& a0, uint32_t* ready,
+                               int64_t* grow0, int64_t* grows) {
     const int64_t shard = P.m / P.world;
     const int64_t own0 = P.rank * shard, own1 = own0 + shard;
     ChunksLaunch L{};
@@ -502,39 +547,59 @@ coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const Gath
     L.c = g0.c;
     L.n = g0.n;
     L.k = g0.k;
-    L.ready = c->sync + COC_MAX_SPLIT * kSyncWords;
+    L.ready = ready;
     L.order = 1;
     L.trans_b = g0.trans_b;
     add_piece(&L, a0.src[P.rank], -own0, own0, shard, -1);
-    int64_t grow0[COC_MAX_SPLIT], grows[COC_MAX_SPLIT];
-    double bytes = 0;
     for (int i = 0; i < P.nchunks; ++i) {
         grow0[i] = P.chunk[i].red_base;
         grows[i] = P.chunk[i].red_rows;
-        bytes += 2.0 * double(grows[i]) * double(P.k) * double(es);
         // the chunk's rows outside the own shard (AG chunks are contiguous)
         const int64_t r0 = P.chunk[i].base, r1 = r0 + P.chunk[i].rows_per_blk * P.chunk[i].nblk;
         add_piece(&L, g0.a, 0, r0, (r1 < own0 ? r1 : own0) - r0, i);
         add_piece(&L, g0.a, 0, r0 > own1 ? r0 : own1, r1 - (r0 > own1 ? r0 : own1), i);
     }
+    L.gather_nchunks = P.nchunks;   // (the fused-gather plan depends on it)
+    return L;
+}
+
+// The fused-gather fields of L for plan fp (the launch copies the rows
+// itself); the ready targets are left to the caller.
+void set_fused_gather(ChunksLaunch* L, const Plan& P, const GatherLaunch& a0, const FusedGatherPlan& fp,
+                      const int64_t* grow0, const int64_t* grows) {
+    L->gather_plan = fp;
+    for (int r = 0; r < COC_MAX_WORLD; ++r) L->gather_src[r] = a0.src[r < a0.nsrc ? r : 0];
+    L->gather_dst = a0.dst;
+    L->gather_row_bytes = P.k * (int64_t)elem_size(P.dt);
+    L->gather_shard_rows = P.m / P.world;
+    for (int i = 0; i < P.nchunks; ++i) {
+        L->gather_row0[i] = grow0[i];
+        L->gather_rows[i] = grows[i];
+    }
+}
+
+coc_status run_comm_first_chunks(const Plan& P, const GemmLaunch& g0, const GatherLaunch& a0,
+                                 hipStream_t main) {
+    StreamCtx* c = nullptr;
+    COC_TRY(get_ctx(main, &c));
+    ChainedCall chain;
+    COC_TRY(chain.begin(c, main));
+    const size_t es = elem_size(P.dt);
+    int64_t grow0[COC_MAX_SPLIT], grows[COC_MAX_SPLIT];
+    ChunksLaunch L = comm_first_launch(P, g0, a0, c->sync + COC_MAX_SPLIT * kSyncWords, grow0, grows);
+    double bytes = 0;
+    for (int i = 0; i < P.nchunks; ++i) bytes += 2.0 * double(grows[i]) * double(P.k) * double(es);
     int32_t tiles[kMaxPieces + 1];
-    L.gather_nchunks = P.nchunks;   // (the plan depends on it)
     L.gave_up = c->gave_up();
     const FusedGatherPlan fp = COC_FUSED_GATHER ? chunks_fused_gather(L) : FusedGatherPlan{};
     if (fp.gatherers > 0) {
         // the matmul launch copies the rows itself, chunk by chunk; the host's
         // running targets advance only once that launch is enqueued
-        L.gather_plan = fp;
-        for (int r = 0; r < COC_MAX_WORLD; ++r) L.gather_src[r] = a0.src[r < a0.nsrc ? r : 0];
-        L.gather_dst = a0.dst;
-        L.gather_row_bytes = P.k * (int64_t)es;
-        L.gather_shard_rows = shard;
+        set_fused_gather(&L, P, a0, fp, grow0, grows);
         L.spin_limit = spin_limit_override();
         const uint32_t off = target_offset();
         uint32_t sent[COC_MAX_SPLIT];
         for (int i = 0; i < P.nchunks; ++i) {
-            L.gather_row0[i] = grow0[i];
-            L.gather_rows[i] = grows[i];
             sent[i] = c->ready_sent[i] + (uint32_t)(i < fp.early ? fp.workgroups : fp.gatherers);
             L.ready_target[i] = sent[i] + off;
         }
@@ -995,6 +1060,94 @@ coc_status allgather_op(const void* x_shard, const void* const* peer_bufs, const
     return run_comm_first(P, g0, a0, stream, cap);
 }
 
+// ALL_GATHER_MATMUL with the gathered matrix and the hand-over counters in
+// `scratch`: no allocation, no library stream or event, everything on the
+// caller's stream.  The counters are cleared by a kernel at the start of the
+// call, so every wait target is absolute.
+coc_status allgather_noalloc(const void* x_shard, const void* const* peer_bufs, const void* w, void* y,
+                             int32_t world, int32_t rank, int64_t m, int64_t n, int64_t k, coc_dtype dt,
+                             int32_t split, int32_t deterministic, hipStream_t stream) {
+    clear_error();
+    Plan P;
+    COC_TRY(make_plan(COC_OP_ALLGATHER_MATMUL, m, n, k, dt, world, rank, split, deterministic, &P));
+    const int64_t es = (int64_t)elem_size(P.dt);
+    const int64_t shard = m / world;
+    if (m == 0 || n == 0) return COC_OK;
+    const size_t gbytes = size_t(m) * size_t(k) * size_t(es);
+    if (gbytes > kScratchGatherBytes)
+        return fail(COC_ERR_WORKSPACE, "the allocation-free all-gather matmul stages at most %zu bytes of "
+                                       "gathered rows; m x k needs %zu",
+                    kScratchGatherBytes, gbytes);
+    std::vector<Range> ins, outs;
+    COC_TRY(check_ptr(x_shard, shard * k * es, "x_shard"));
+    COC_TRY(check_ptr(w, k * n * es, "w"));
+    COC_TRY(check_ptr(y, m * n * es, "y"));
+    ins.push_back(mk(x_shard, shard * k * es, "x_shard"));
+    ins.push_back(mk(w, k * n * es, "w"));
+    COC_TRY(check_peers(peer_bufs, P, shard * k * es, &ins));
+    outs.push_back(mk(y, m * n * es, "y"));
+    COC_TRY(check_alias(outs, ins));
+    uint8_t* base = nullptr;
+    COC_TRY(scratch_base(&base));
+    bool cap = false;
+    COC_TRY(capture_once(stream, &cap));
+    uint32_t* sync = (uint32_t*)base;
+    void* g = base + kScratchGatherOffset;
+
+    GatherLaunch a0{};
+    a0.dt = P.dt;
+    a0.nsrc = world;
+    for (int r = 0; r < world; ++r) a0.src[r] = (r == rank) ? x_shard : peer_bufs[r];
+    a0.shard_rows = shard;
+    a0.dst = g;
+    a0.k = k;
+    GemmLaunch g0{};
+    g0.kind = kind_of(P.dt);
+    g0.a = g;
+    g0.b = w;
+    g0.c = y;
+    g0.n = n;
+    g0.k = k;
+
+    if (P.split > 1 && one_launch_gather(P, g0)) {
+        // the counters start from zero (the gave-up line is kept for coc_check_waits)
+        COC_HIP(hipError_t(launch_zero_words(sync, kGaveUpLine * kSyncWords, stream)));
+        int64_t grow0[COC_MAX_SPLIT], grows[COC_MAX_SPLIT];
+        ChunksLaunch L = comm_first_launch(P, g0, a0, sync + COC_MAX_SPLIT * kSyncWords, grow0, grows);
+        L.gave_up = sync + kGaveUpLine * kSyncWords;
+        L.spin_limit = spin_limit_override();
+        const uint32_t off = target_offset();
+        const FusedGatherPlan fp = COC_FUSED_GATHER ? chunks_fused_gather(L) : FusedGatherPlan{};
+        if (fp.gatherers > 0) {
+            set_fused_gather(&L, P, a0, fp, grow0, grows);
+            for (int i = 0; i < P.nchunks; ++i)
+                L.ready_target[i] = (uint32_t)(i < fp.early ? fp.workgroups : fp.gatherers) + off;
+        } else {
+            // the copy as its own launch ahead of the matmul on the same stream
+            L.gather_nchunks = 0;
+            int32_t per_chunk = 0;
+            COC_HIP(hipError_t(launch_gather_chunks(a0, P.nchunks, grow0, grows, L.ready, stream, &per_chunk)));
+            for (int i = 0; i < P.nchunks; ++i) L.ready_target[i] = (uint32_t)per_chunk + off;
+        }
+        int32_t tiles[kMaxPieces + 1];
+        COC_HIP(hipError_t(launch_gemm_chunks(L, stream, tiles)));
+        return COC_OK;
+    }
+    // every gathered row, then the matmul over them (the serial form)
+    GatherLaunch a = a0;
+    a.row0 = 0;
+    a.rows = m;
+    COC_HIP(hipError_t(launch_gather(a, stream)));
+    GemmLaunch gg = g0;
+    gg.base = 0;
+    gg.stride = 0;
+    gg.rpb = m;
+    gg.nblk = 1;
+    gg.concurrent = 1;
+    COC_HIP(hipError_t(launch_gemm(gg, stream)));
+    return COC_OK;
+}
+
 
 }  // namespace
 }  // namespace coc
@@ -1073,6 +1226,12 @@ coc_status coc_allgather_matmul_trans_w(const void* x_shard, const void* const* 
                                         hipStream_t stream) {
     return allgather_op(x_shard, peer_bufs, w, y, gathered_out, world, rank, m, n, k, dt, split, deterministic,
                         1, ws, ws_bytes, stream);
+}
+
+coc_status coc_allgather_matmul_noalloc(const void* x_shard, const void* const* peer_bufs, const void* w,
+                                        void* y, int32_t world, int32_t rank, int64_t m, int64_t n, int64_t k,
+                                        coc_dtype dt, int32_t split, int32_t deterministic, hipStream_t stream) {
+    return allgather_noalloc(x_shard, peer_bufs, w, y, world, rank, m, n, k, dt, split, deterministic, stream);
 }
 
 coc_status coc_weight_grad(const void* g, const void* dy, void* dw, int64_t m, int64_t n, int64_t k,

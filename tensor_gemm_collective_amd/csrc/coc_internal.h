@@ -200,6 +200,8 @@ struct A2ALaunch {
 // Launchers (kernels.hip).  Return a hipError_t value (0 = success).  The
 // caller guarantees that every size and pointer has been validated.
 int launch_gemm(const GemmLaunch& g, void* stream);
+// Zeroes n 32-bit words at p (device memory) on `stream`.
+int launch_zero_words(uint32_t* p, int n, void* stream);
 int launch_reduce(const ReduceLaunch& r, void* stream);
 int launch_reduce_chunks(const ReduceChunksLaunch& r, void* stream);
 // *groups (if given) receives the number of workgroups launched (signals sent).

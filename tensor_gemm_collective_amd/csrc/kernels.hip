@@ -1858,6 +1858,13 @@ __global__ __launch_bounds__(256) void a2a_combine(A2AParams p) {
     }
 }
 
+// Clears n 32-bit words: the allocation-free entry point's hand-over
+// counters at the start of each call (a kernel rather than a memset node, so
+// that a call captured into a graph clears them on every replay).
+__global__ __launch_bounds__(256) void zero_words(uint32_t* p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
 int grid_for(int64_t total_vec, int per_thread = 1) {
     const int64_t want = (total_vec + 256 * per_thread - 1) / (256 * per_thread);
     const int64_t cap = 256 * 8;
@@ -1976,6 +1983,13 @@ int launch_gemm(const GemmLaunch& g, void* stream) {
             return launch_w8_any(p, s);
     }
     return hipErrorInvalidValue;
+}
+
+int launch_zero_words(uint32_t* p, int n, void* stream) {
+    if (n <= 0) return hipSuccess;
+    const int grid = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+    hipLaunchKernelGGL(zero_words, dim3(grid), dim3(256), 0, (hipStream_t)stream, p, n);
+    return hipGetLastError();
 }
 
 int launch_reduce(const ReduceLaunch& r, void* stream) {
