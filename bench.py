@@ -147,6 +147,95 @@ def sample_clock(step, torch, seconds=1.0, batch=40, per_batch=5, period=0.003):
     return out
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+STAMP_RECORDS = 1 << 16
+
+
+def stamp_buffer(torch, dev):
+    """Device buffer for the kernels' activity records (layout in include/coc.h)."""
+    return torch.zeros(3 * STAMP_RECORDS, dtype=torch.int64, device=dev)
+
+
+def stamped(torch, tgc, buf, fn):
+    """Run fn once with the activity records on; returns (kind, chunk, start_us,
+    end_us) per record written (the device counter runs at 100 MHz)."""
+    buf.zero_()
+    torch.cuda.synchronize()
+    tgc.profile_stamps(buf)
+    try:
+        fn()
+        torch.cuda.synchronize()
+        n = tgc.profile_stamp_count()
+    finally:
+        tgc.profile_stamps(None)
+    h = buf[:3 * n].cpu().numpy().reshape(n, 3)
+    return [((int(w) & 255) - 1, (int(w) >> 8) & 255, t0 / 100.0, t1 / 100.0) for w, t0, t1 in h if w != 0]
+
+
+def _union(iv):
+    out = []
+    for a, b in sorted(iv):
+        if out and a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    return out
+
+
+def overlap_of(recs, comm_bytes):
+    """The Overlap blog's profiler view of one op call, from the kernels' own
+    activity records: the matmul's span (first tile started to last tile
+    stored), the communication's active time (union of the reduce / gather
+    workgroups' intervals, waiting excluded), how much of it falls inside the
+    matmul's span (hidden) and outside it (exposed)."""
+    mm = [(a, b) for k, c, a, b in recs if k == 0]
+    comm = _union([(a, b) for k, c, a, b in recs if k in (1, 2)])
+    active = sum(b - a for a, b in comm)
+    if not mm:
+        return {"comm_active_us": round(active, 2), "comm_hidden_us": 0.0, "comm_exposed_us": round(active, 2)}
+    s0, s1 = min(a for a, b in mm), max(b for a, b in mm)
+    hidden = sum(max(0.0, min(b, s1) - max(a, s0)) for a, b in comm)
+    return {
+        "matmul_span_us": round(s1 - s0, 2),
+        "comm_active_us": round(active, 2),
+        "comm_hidden_us": round(hidden, 2),
+        "comm_exposed_us": round(active - hidden, 2),
+        "overlap_frac": round(hidden / active, 4) if active > 0 else None,
+        "comm_gbs_active": round(comm_bytes / (active * 1e-6) / 1e9, 1) if active > 0 else None,
+    }
+
+
+def mean_dicts(ds):
+    keys = [k for k in ds[0] if all(isinstance(d.get(k), (int, float)) for d in ds)]
+    return {k: round(sum(d[k] for d in ds) / len(ds), 4) for k in keys}
+
+
+def serial_parts(torch, tgc, fn, iters=10):
+    """Per-call launch time of the matmul and of the communication kernels of
+    fn (the serial, split-1 form: each runs alone), from the library's
+    per-launch events."""
+    fn()
+    torch.cuda.synchronize()
+    tgc.profile_enable(True)
+    tgc.profile_read()
+    for _ in range(iters):
+        fn()
+    torch.cuda.synchronize()
+    pr = tgc.profile_read()
+    tgc.profile_enable(False)
+    return pr["gemm"]["ms"] / iters, (pr["reduce"]["ms"] + pr["gather"]["ms"]) / iters
+
+
 def flops_of(inp):
     ag, rs = inp["ag"], inp["rs"]
     return 2.0 * ag.m * ag.n * ag.k, 2.0 * rs.m * rs.n * rs.k
@@ -202,6 +291,7 @@ def cpu_baseline(inp, frac, min_seconds=10.0):
     flops = passes * (2.0 * world * shard_rows * ag.n * ag.k + 2.0 * world * slice_rows * rs.n * rs.k)
     return {
         "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"the same step with m scaled by {frac:g} (AG {world}x{shard_rows} gathered rows, "
                   f"RS {world}x{slice_rows} rows), all n and k; float64 numpy oracle incl. decoding the "
                   f"bf16 inputs; {passes} passes in {dt:.2f} s",
@@ -491,6 +581,101 @@ def run_moe(torch, tgc, synth, dev, iters=10, prewarm_s=0.5):
         torch.cuda.empty_cache()
 
 
+CASES = ("bloom7b_ar", "bloom176b_ar", "w8a16_ar", "llama70b_ag", "llama70b_rs")
+
+
+def run_case(args, torch, tgc, synth, dev):
+    """One workload's op alone (--case NAME) at --split, timed like the step:
+    prewarm, W warmup calls, K timed calls on the caller's stream; then the
+    serial (split 1) form and the overlap view.  One JSON line on stdout."""
+    W = synth.WORKLOADS
+    wl = W[args.case]
+    world, rank = wl.world, 0
+    det = 1 if args.case == "bloom176b_ar" else 0
+    split = {"split": args.split}
+    if args.case in ("bloom7b_ar", "bloom176b_ar"):
+        x = synth.normal(wl.wid, synth.T_X, 0, (wl.m, wl.k), 1.0, "bf16").to(dev)
+        w = synth.normal(wl.wid, synth.T_W, 0, (wl.k, wl.n), wl.w_sigma, "bf16").to(dev)
+        pr = [None] + [synth.normal(wl.wid, synth.T_PEER, r, (wl.m, wl.n), wl.peer_sigma, "bf16").to(dev)
+                       for r in range(1, world)]
+        y = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device=dev)
+        po = torch.empty_like(y)
+
+        def op():
+            tgc.matmul_all_reduce(x, w, pr, rank, y=y, partial_out=po, split=split["split"], deterministic=det)
+        comm_bytes = (world + 1.0) * wl.m * wl.n * 2
+        what = f"MATMUL_ALL_REDUCE bf16 X {wl.m}x{wl.k} @ W {wl.k}x{wl.n}, {world} partials"
+    elif args.case == "w8a16_ar":
+        x = synth.normal(wl.wid, synth.T_X, 0, (wl.m, wl.k), 1.0, "f16").to(dev)
+        q = synth.integers(wl.wid, synth.T_W, 0, (wl.k, wl.n), -127, 127, "i8").to(dev)
+        sc = synth.fp16_scales(wl.wid, 0, (wl.n,)).to(dev)
+        pr = [None] + [synth.normal(wl.wid, synth.T_PEER, r, (wl.m, wl.n), wl.peer_sigma, "f16").to(dev)
+                       for r in range(1, world)]
+        y = torch.empty((wl.m, wl.n), dtype=torch.float16, device=dev)
+        po = torch.empty_like(y)
+
+        def op():
+            tgc.matmul_all_reduce_w8a16(x, q, sc, "per_channel", pr, rank, y=y, partial_out=po,
+                                        split=split["split"], deterministic=det)
+        comm_bytes = (world + 1.0) * wl.m * wl.n * 2
+        what = f"w8A16 MATMUL_ALL_REDUCE per channel, X {wl.m}x{wl.k} fp16 @ int8 W {wl.k}x{wl.n}, {world} partials"
+    else:
+        inp = make_inputs(torch, tgc, synth, args.split, dev)
+        if args.case == "llama70b_ag":
+            def op():
+                tgc.allgather_matmul(inp["ag_x"], inp["ag_peers"], inp["ag_w"], rank, y=inp["ag_y"], ws=inp["ag_ws"],
+                                     split=split["split"])
+            comm_bytes = 2.0 * wl.m * wl.k * 2
+            what = f"ALL_GATHER_MATMUL bf16 {world}x({wl.m // world}x{wl.k}) @ W {wl.k}x{wl.n}"
+        else:
+            def op():
+                tgc.matmul_reduce_scatter(inp["rs_x"], inp["rs_w"], inp["rs_peers"], rank, y=inp["rs_y"],
+                                          partial_out=inp["rs_part"], split=split["split"])
+            comm_bytes = (world + 1.0) * (wl.m // world) * wl.n * 2
+            what = f"MATMUL_REDUCE_SCATTER bf16 X {wl.m}x{wl.k} @ W {wl.k}x{wl.n} -> {wl.m // world}x{wl.n}"
+    flops = 2.0 * wl.m * wl.n * wl.k
+    log(f"case {args.case}: {what}, split {args.split}, det {det}")
+    t_pre = time.perf_counter()
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        for _ in range(10):
+            op()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        op()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        op()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} calls: {ms:.4f} ms")
+    out = {"case": args.case, "op": what, "split": args.split, "deterministic": det, "ms": round(ms, 5),
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    if not args.no_breakdown:
+        split["split"] = 1
+        e0.record()
+        for _ in range(args.steps):
+            op()
+        e1.record()
+        torch.cuda.synchronize()
+        out["serial_ms"] = round(e0.elapsed_time(e1) / args.steps, 5)
+        g1, c1 = serial_parts(torch, tgc, op)
+        split["split"] = args.split
+        sbuf = stamp_buffer(torch, dev)
+        o = mean_dicts([overlap_of(stamped(torch, tgc, sbuf, op), comm_bytes) for _ in range(5)])
+        o["serial_matmul_ms"] = round(g1, 5)
+        o["serial_comm_ms"] = round(c1, 5)
+        o["hidden_frac_vs_serial"] = round((g1 + c1 - ms) / c1, 4) if c1 > 0 else None
+        o["unhidden_frac_vs_serial"] = None if o["hidden_frac_vs_serial"] is None else \
+            round(1 - o["hidden_frac_vs_serial"], 4)
+        out["overlap"] = o
+        out["vs_serial_matmul"] = round(ms / g1, 4) if g1 > 0 else None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -518,6 +703,9 @@ def main():
     ap.add_argument("--lone", action="store_true",
                     help="only time the lone matmuls of the step's two ops and of the backward dX "
                          "against hipBLASLt, interleaved (stderr lines), and exit")
+    ap.add_argument("--case", choices=CASES,
+                    help="only time one workload's op at --split (prewarm, W warmup calls, K timed calls), "
+                         "then its serial form and the overlap view; one JSON line, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) three "
                          "times, for scaling the HBM byte counters, and exit")
@@ -558,6 +746,9 @@ def main():
         return
     if args.backward:
         run_backward_only(torch, tgc, synth, dev, warm_passes=3 if args.prewarm_s > 0 else 0)
+        return
+    if args.case:
+        run_case(args, torch, tgc, synth, dev)
         return
     log("generating inputs ...")
     inp = make_inputs(torch, tgc, synth, args.split, dev)
@@ -661,7 +852,7 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / iters
 
-    def time_cold(fn, iters=20):
+    def time_cold(fn, iters=50):
         """Per-call times with the caches cold: before each call a 512 MB write
         evicts the L2s and the 256 MB memory-side cache (outside the events).
         Returns (median, p10, p90) in ms."""
@@ -681,7 +872,11 @@ def main():
         q = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
         return q(0.5), q(0.1), q(0.9)
 
+    ag, rs, world = inp["ag"], inp["rs"], inp["world"]
+    comm_bytes = {"allgather_matmul": 2.0 * ag.m * ag.k * 2,                     # gathered rows read + written
+                  "matmul_reduce_scatter": (world + 1.0) * (rs.m // world) * rs.n * 2}   # 8 partial slices + y
     cold = None
+    overlap = None
     if args.no_breakdown:
         ms_ag = ms_rs = ms_serial = float("nan")
     else:
@@ -691,9 +886,33 @@ def main():
         split_saved = split
         split = 1
         ms_serial = time_op(step)
+        serial = {"allgather_matmul": serial_parts(torch, tgc, run_ag),
+                  "matmul_reduce_scatter": serial_parts(torch, tgc, run_rs)}
         split = split_saved
+        # Overlap (the Overlap blog's profiler view; SURVEY's definitions):
+        # from the kernels' activity records, the communication's active time
+        # and the part of it inside the matmul's span; and hidden =
+        # (T_matmul alone + T_comm alone - T_pipelined) / T_comm alone, with
+        # the split-1 launches as the "alone" times.
+        log("overlap (activity records) ...")
+        sbuf = stamp_buffer(torch, dev)
+        overlap = {}
+        tot_active = tot_exposed = 0.0
+        for name, fn, ms_op in (("allgather_matmul", run_ag, ms_ag), ("matmul_reduce_scatter", run_rs, ms_rs)):
+            per = [overlap_of(stamped(torch, tgc, sbuf, fn), comm_bytes[name]) for _ in range(5)]
+            o = mean_dicts(per)
+            g1, c1 = serial[name]
+            o["serial_matmul_ms"] = round(g1, 5)
+            o["serial_comm_ms"] = round(c1, 5)
+            o["pipelined_ms"] = round(ms_op, 5)
+            o["hidden_frac_vs_serial"] = round((g1 + c1 - ms_op) / c1, 4) if c1 > 0 else None
+            overlap[name] = o
+            tot_active += o.get("comm_active_us", 0.0)
+            tot_exposed += o.get("comm_exposed_us", 0.0)
+        overlap["step_unhidden_comm_frac"] = round(tot_exposed / tot_active, 4) if tot_active > 0 else None
+        del sbuf
         log("cold-cache timings ...")
-        cold = {"flush_bytes": 512 << 20, "iterations": 20}
+        cold = {"flush_bytes": 512 << 20, "iterations": 50}
         for name, fn, fl in (("allgather_matmul", run_ag, f_ag), ("matmul_reduce_scatter", run_rs, f_rs),
                              ("step", step, f_ag + f_rs)):
             med, p10, p90 = time_cold(fn)
@@ -710,12 +929,7 @@ def main():
     avg_ms = g["ms"] / max(1, g["launches"])
     flops_per_launch = g["work"] / max(1, g["launches"])
     achieved = g["work"] / (g["busy_ms"] * 1e-3) / 1e12 if g["busy_ms"] > 0 else 0.0
-    comm_ms = (prof["reduce"]["busy_ms"] + prof["gather"]["busy_ms"]) / args.steps
     gemm_ms = g["busy_ms"] / args.steps
-    hidden = (gemm_ms + comm_ms - ms_step) / comm_ms if comm_ms > 0 else None
-
-    def gbs(c):
-        return round(c["work"] / (c["ms"] * 1e-3) / 1e9, 1) if c["ms"] > 0 else None
 
     def tf(flops, ms):
         return None if ms != ms else round(flops / (ms * 1e-3) / 1e12, 2)
@@ -750,15 +964,16 @@ def main():
             "cold_cache": cold,
             "kernel_busy_ms_per_step": {k: round(v["busy_ms"] / args.steps, 5) for k, v in prof.items()},
             "kernel_launches_per_step": {k: v["launches"] / args.steps for k, v in prof.items()},
-            "reduce_gbs": gbs(prof["reduce"]),
-            "gather_gbs": gbs(prof["gather"]),
-            "comm_hidden_frac": None if hidden is None else round(hidden, 3),
+            "overlap": overlap,
             # the part of the step with no matmul launch running: exposed
             # communication, launch gaps and the reduce of the last round
             "no_matmul_ms_per_step": round(ms_step - gemm_ms, 5),
             "no_matmul_frac_of_step": round(max(0.0, ms_step - gemm_ms) / ms_step, 4),
-            "comm_note": "reduce and gather launches start beside the matmul and wait on its per-chunk "
-                         "counters, so their intervals (and the GB/s above) include the waiting",
+            "overlap_note": "comm_active_us: union of the reduce / gather workgroups' active intervals "
+                            "(waiting on counters excluded), from the kernels' activity records; "
+                            "comm_hidden_us: the part inside the matmul's span; comm_gbs_active: the op's "
+                            "communication bytes over its active time; hidden_frac_vs_serial: "
+                            "(T_matmul + T_comm of the split-1 launches - T_pipelined) / T_comm",
         },
         "roofline": {
             "bound": "mfma",

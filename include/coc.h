@@ -59,7 +59,13 @@
  *   - `split` is the number of m-chunks the work is pipelined over: 1
  *     (serial, no overlap), 2, 4 or 8 (CoC guide, "Usage": the split count
  *     options; the m dimension must divide by it, CoC guide "Approach" and
- *     Overlap blog, third-layer caveats).
+ *     Overlap blog, third-layer caveats).  For the compute-first ops (all-
+ *     reduce, reduce-scatter, w8A16) on one GPU the reduction beside the
+ *     matmul competes with it for the compute units' memory path and power,
+ *     so the library pipelines them only when the reduction would take at
+ *     least a sixth of the matmul's time (estimated from the sizes);
+ *     otherwise the call runs the serial schedule.  Result bits never depend
+ *     on the split or on this choice.
  *   - The *_trans_w entry points (matmul all-reduce / reduce-scatter /
  *     all-gather) take the same arguments as the plain ones, but `w` holds
  *     the weights transposed, n rows of k elements, so the backward pass of
@@ -440,6 +446,23 @@ coc_status coc_profile_read(double* total_ms, int64_t* launches, double* work_un
  * launches ran concurrently. */
 coc_status coc_profile_records(int32_t* kclass, double* start_ms, double* end_ms, double* work_units,
                                int32_t max, int32_t* n);
+
+/* Activity stamps, for measuring overlap.  coc_profile_stamps(buf, records)
+ * hands the library a DEVICE buffer of `records` three-word (64-bit)
+ * records, owned by the caller and zeroed by it (NULL turns the stamps off).
+ * Each later launch of the library's matmul, reduce and gather kernels takes
+ * the next consecutive region of it (one record per workgroup and piece of
+ * work); a launch that no longer fits takes none.  coc_profile_stamp_count()
+ * returns how many records have been handed out since the buffer was set.
+ * A record a workgroup wrote holds:
+ *   word 0  1 + kind (0 matmul: first tile started to last tile's stores
+ *           issued; 1 reduce: its wait done to its last store issued; 2
+ *           gather: copy start to last store issued) | chunk << 8 | XCD << 16
+ *   word 1  start, word 2  end: the 100 MHz real-time counter
+ * Records left zero had no work.  Per process; not for use while another
+ * thread issues library calls. */
+void coc_profile_stamps(void* buf, int64_t records);
+int64_t coc_profile_stamp_count(void);
 
 #ifdef __cplusplus
 }

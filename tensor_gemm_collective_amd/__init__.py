@@ -23,6 +23,8 @@ from .coc import (  # noqa: F401
     check_waits,
     plan,
     profile_enable,
+    profile_stamps,
+    profile_stamp_count,
     profile_read,
     profile_records,
 )

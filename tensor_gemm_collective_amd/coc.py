@@ -37,7 +37,7 @@ EXPORTS = (
     "coc_allgather_matmul_trans_w", "coc_allgather_matmul_noalloc", "coc_weight_grad", "coc_alltoall_grouped_matmul",
     "coc_grouped_matmul_alltoall", "coc_workspace_bytes", "coc_status_string",
     "coc_last_error", "coc_check_waits", "coc_plan", "coc_profile_enable", "coc_profile_read",
-    "coc_profile_records",
+    "coc_profile_records", "coc_profile_stamps", "coc_profile_stamp_count",
 )
 
 
@@ -105,6 +105,10 @@ def lib() -> ctypes.CDLL:
     L.coc_plan.restype = _i32
     L.coc_profile_enable.argtypes = [_i32]
     L.coc_profile_enable.restype = None
+    L.coc_profile_stamps.argtypes = [_vp, _i64]
+    L.coc_profile_stamps.restype = None
+    L.coc_profile_stamp_count.argtypes = []
+    L.coc_profile_stamp_count.restype = _i64
     L.coc_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64),
                                    ctypes.POINTER(ctypes.c_double)]
     L.coc_profile_read.restype = _i32
@@ -335,6 +339,20 @@ def plan(op: int, m: int, world: int, rank: int, split: int):
 
 def profile_enable(on: bool) -> None:
     lib().coc_profile_enable(1 if on else 0)
+
+
+def profile_stamps(buf) -> None:
+    """Point the kernels' activity records at `buf`, a zeroed int64 device
+    tensor of 3 x records words (coc.h describes the records); None turns them off."""
+    if buf is None:
+        lib().coc_profile_stamps(None, 0)
+    else:
+        lib().coc_profile_stamps(buf.data_ptr(), buf.numel() // 3)
+
+
+def profile_stamp_count() -> int:
+    """Records handed out to launches since the buffer was set."""
+    return int(lib().coc_profile_stamp_count())
 
 
 def profile_read():

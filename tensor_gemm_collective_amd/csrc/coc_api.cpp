@@ -456,6 +456,27 @@ double total_flops(const Plan& P) {
     return f;
 }
 
+// Whether overlapping a compute-first op's reduction with its matmul can pay
+// on one GPU.  The reduce beside the matmul shares the compute units' memory
+// path and the power budget with it; measured on MI355X, that slows the
+// matmul by about as much as a small reduction saves (LLaMA2-70B TP8
+// reduce-scatter, 75 MB against a 240 GFLOP matmul: 217 us pipelined
+// against 207 us serial), while a large one gains (BLOOM-176B all-reduce,
+// 528 MB against 421 GFLOP: 406 against 417 us; the w8A16 all-reduce, 604 MB
+// against 240 GFLOP: 293 against 315 us).  The pipeline is used when the
+// reduction alone would take at least a sixth of the matmul's time (both
+// estimated at measured rates: 5.5 TB/s, 1.2 PFLOP/s); otherwise the call
+// runs the serial schedule, which gives the same bits.
+constexpr double kReduceBytesPerS = 5.5e12, kMatmulFlopPerS = 1.2e15, kOverlapMinRatio = 1.0 / 6.0;
+
+bool overlap_pays(const Plan& P) {
+    const int64_t red_rows = P.op == COC_OP_MATMUL_REDUCE_SCATTER ? P.m / P.world : P.m;
+    const double bytes = double(P.world + 1) * double(red_rows) * double(P.n) * double(elem_size(P.dt));
+    const double flops = 2.0 * double(P.m) * double(P.n) * double(P.k);
+    if (flops <= 0) return false;
+    return (bytes / kReduceBytesPerS) >= kOverlapMinRatio * (flops / kMatmulFlopPerS);
+}
+
 // One-launch pipeline, compute first: the matmul walks the chunks in order on
 // the caller's stream and counts finished tiles per chunk; the reduce of each
 // early chunk, on the side stream from the start, waits for that chunk's
@@ -515,6 +536,7 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
         ReduceLaunch r = r0;
         r.src_row0 = P.chunk[early].red_base;
         r.dst_row0 = P.chunk[early].out_base;
+        r.wide = true;   // after the matmul on the caller's stream
         r.rows = 0;
         for (int i = early; i < P.nchunks; ++i) r.rows += P.chunk[i].red_rows;
         const double lb = double(r.nsrc + 1) * double(r.rows) * double(P.n) * double(es);
@@ -632,17 +654,19 @@ coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLa
         const GemmLaunch g = gemm_for_chunk(P, g0, P.chunk[i]);
         return launch(KC_GEMM, gemm_flops(P, P.chunk[i]), s, [&] { return launch_gemm(g, s); });
     };
-    auto reduce = [&](int i, hipStream_t s) {
+    // alone: the serial form's reduce, after its matmul on the same stream
+    auto reduce = [&](int i, hipStream_t s, bool alone) {
         ReduceLaunch r = r0;
         r.src_row0 = P.chunk[i].red_base;
         r.dst_row0 = P.chunk[i].out_base;
         r.rows = P.chunk[i].red_rows;
+        r.wide = alone;
         const double bytes = double(r.nsrc + 1) * double(r.rows) * double(P.n) * double(es);
         return launch(KC_REDUCE, bytes, s, [&] { return launch_reduce(r, s); });
     };
     if (P.split == 1) {
         COC_TRY(gemm(0, main));
-        return reduce(0, main);
+        return reduce(0, main, true);
     }
     if (one_launch(P, g0) && !cap) return run_compute_first_chunks(P, g0, r0, main);
     StreamCtx* c = nullptr;
@@ -654,7 +678,7 @@ coc_status run_compute_first(const Plan& P, const GemmLaunch& g0, const ReduceLa
         COC_TRY(gemm(i, cs));
         COC_HIP(hipEventRecord(c->ev[i], cs));
         COC_HIP(hipStreamWaitEvent(c->side, c->ev[i], 0));
-        COC_TRY(reduce(i, c->side));
+        COC_TRY(reduce(i, c->side, false));
     }
     COC_HIP(hipEventRecord(c->join2, c->gemm2));
     COC_HIP(hipStreamWaitEvent(main, c->join2, 0));
@@ -778,6 +802,13 @@ coc_status compute_first_op(coc_op op, const void* x, const void* w, const void*
     r0.n = n;
     bool cap = false;
     COC_TRY(capture_once(stream, &cap));
+    if (P.split > 1 && !cap && one_launch(P, g0) && !overlap_pays(P)) {
+        // a reduction too small to hide pays less than it costs beside the
+        // matmul: the serial schedule (the split-1 plan of the same op)
+        Plan S;
+        COC_TRY(make_plan(op, m, n, k, dt, world, rank, 1, det, &S));
+        return run_compute_first(S, g0, r0, stream, cap);
+    }
     return run_compute_first(P, g0, r0, stream, cap);
 }
 
@@ -1385,6 +1416,10 @@ coc_status coc_check_waits(hipStream_t stream) {
 }
 
 void coc_profile_enable(int32_t on) { g_prof_on.store(on ? 1 : 0); }
+
+void coc_profile_stamps(void* buf, int64_t records) { set_stamp_buffer((uint64_t*)buf, records); }
+
+int64_t coc_profile_stamp_count(void) { return stamp_records_used(); }
 
 coc_status coc_profile_read(double* total_ms, int64_t* launches, double* work_units) {
     clear_error();

@@ -69,6 +69,7 @@ struct ReduceLaunch {
     int32_t nsrc;
     void* dst;
     int64_t src_row0, dst_row0, rows, n;
+    bool wide;   // the launch runs alone (not beside a matmul): more loads in flight per thread
 };
 
 // Bit copy of gathered rows: dst[row] = shard (row / shard_rows), local row
@@ -200,6 +201,12 @@ struct A2ALaunch {
 // Launchers (kernels.hip).  Return a hipError_t value (0 = success).  The
 // caller guarantees that every size and pointer has been validated.
 int launch_gemm(const GemmLaunch& g, void* stream);
+// Activity stamps for measurement: while buf is set, launches of the matmul,
+// reduce and gather kernels take consecutive regions of its `records` slots
+// (three words each; layout in kernels.hip); stamp_records_used() is how many
+// slots have been handed out since.
+void set_stamp_buffer(uint64_t* buf, int64_t records);
+int64_t stamp_records_used();
 // Zeroes n 32-bit words at p (device memory) on `stream`.
 int launch_zero_words(uint32_t* p, int n, void* stream);
 int launch_reduce(const ReduceLaunch& r, void* stream);

@@ -654,3 +654,53 @@ def test_pipeline_handover_reuses_buffers_without_stale_rows(split):
         assert_bits_equal(y_ag, ref_ag, f"all-gather matmul, call {it}")
         assert_bits_equal(p_ar, ref_p, f"partial, call {it}")
         assert_bits_equal(y_ar, ref_ar, f"all-reduce, call {it}")
+
+
+def test_activity_stamps_change_nothing_and_stay_in_bounds():
+    """The kernels' activity records (a measurement hook): with them on, every
+    output keeps its bits; the records name the launches' kinds with start <=
+    end, inside the slots handed out; a buffer too small for a launch gets no
+    records from it and nothing past it is written."""
+    bf = torch.bfloat16
+    g0 = torch.Generator(device="cuda").manual_seed(21)
+    world, rank, m, n, k = 8, 2, 4096, 8192, 256
+    x = torch.randn(m, k, device="cuda", generator=g0).to(bf)
+    w = (torch.randn(k, n, device="cuda", generator=g0) * 0.02).to(bf)
+    peers = [None if r == rank else torch.randn(m // world, n, device="cuda", generator=g0).to(bf)
+             for r in range(world)]
+    full = [None if p is None else torch.cat([p] * world) for p in peers]
+    shards = [torch.randn(512, k, device="cuda", generator=g0).to(bf) for _ in range(world)]
+    speers = [None if r == rank else shards[r] for r in range(world)]
+    want_rs, want_p = tgc.matmul_reduce_scatter(x, w, full, rank, split=4, deterministic=1)
+    want_ag = tgc.allgather_matmul(shards[rank], speers, w, rank, split=4)
+    torch.cuda.synchronize()
+    for cap in (1 << 14, 3):
+        log(f"activity stamps, capacity {cap}")
+        whole = torch.full((3 * cap + 64,), -7, dtype=torch.int64, device="cuda")
+        buf = whole[:3 * cap]
+        buf.zero_()
+        torch.cuda.synchronize()
+        tgc.profile_stamps(buf)
+        try:
+            y, p = tgc.matmul_reduce_scatter(x, w, full, rank, split=4, deterministic=1)
+            ya = tgc.allgather_matmul(shards[rank], speers, w, rank, split=4)
+            torch.cuda.synchronize()
+            used = tgc.profile_stamp_count()
+        finally:
+            tgc.profile_stamps(None)
+        assert_bits_equal(y, want_rs, "reduce-scatter with stamps")
+        assert_bits_equal(p, want_p, "partial with stamps")
+        assert_bits_equal(ya, want_ag, "all-gather matmul with stamps")
+        h = whole.cpu().numpy()
+        assert (h[3 * cap:] == -7).all(), "a record was written past the buffer"
+        assert 0 <= used <= cap
+        recs = h[:3 * cap].reshape(cap, 3)
+        assert not recs[used:].any(), "a record was written outside the slots handed out"
+        written = recs[:used][recs[:used, 0] != 0]
+        kinds = set((int(v) & 255) - 1 for v in written[:, 0])
+        assert kinds <= {0, 1, 2}
+        assert (written[:, 1] <= written[:, 2]).all() and (written[:, 1] > 0).all()
+        if cap > 3:
+            assert kinds == {0, 1, 2}, kinds
+        else:
+            assert used == 0 and len(written) == 0
