@@ -147,6 +147,40 @@ def sample_clock(step, torch, seconds=1.0, batch=40, per_batch=5, period=0.003):
     return out
 
 
+def run_mfma_loop(torch, tgc, dev, iters=500, reps=30):
+    """The MFMA-rate diagnostic (coc_diag_mfma_loop): v_mfma_f32_32x32x16_bf16
+    on register operands, 8 waves per CU (as the ring matmul), random N(0,1)
+    operands against one repeated value; launch time by events, then the clock
+    and socket power amdsmi reads while it runs.  One JSON line."""
+    props = torch.cuda.get_device_properties(dev)
+    wgs = 2 * props.multi_processor_count   # two 4-wave workgroups per CU
+    g = torch.Generator(device=dev).manual_seed(7)
+    kinds = {"random": torch.randn(1 << 15, generator=g, device=dev).to(torch.bfloat16),
+             "constant": torch.full((1 << 15,), 1.0, device=dev, dtype=torch.bfloat16)}
+    out = torch.empty(wgs * 256, device=dev, dtype=torch.float32)
+    res = {"diagnostic": "MFMA register loop: v_mfma_f32_32x32x16_bf16, 8 independent accumulators per wave, "
+                         "operands in registers, no memory traffic",
+           "workgroups": wgs, "waves_per_cu": 8, "iters": iters}
+    for name, ops in kinds.items():
+        def launch():
+            return tgc.diag_mfma_loop(ops, out, wgs, iters)
+        t_end = time.perf_counter() + 0.5
+        while time.perf_counter() < t_end:   # reach the load's clock
+            for _ in range(20):
+                launch()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = sum(launch() for _ in range(reps))
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"launch_ms": round(ms, 4), "tflops": round(flops / reps / (ms * 1e-3) / 1e12, 1),
+                     "gpu_clock": sample_clock(launch, torch, seconds=1.0, batch=40)}
+        log(f"mfma loop, {name} operands: {res[name]['tflops']} TFLOP/s")
+    print(json.dumps(res), flush=True)
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -706,6 +740,8 @@ def main():
     ap.add_argument("--case", choices=CASES,
                     help="only time one workload's op at --split (prewarm, W warmup calls, K timed calls), "
                          "then its serial form and the overlap view; one JSON line, and exit")
+    ap.add_argument("--mfma-loop", action="store_true",
+                    help="diagnostic: the bf16 MFMA rate on register operands, random against constant values")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) three "
                          "times, for scaling the HBM byte counters, and exit")
@@ -738,6 +774,9 @@ def main():
                           "bytes_written_per_launch": 4 * n, "launches": 3}), flush=True)
         return
     tgc.lib()
+    if args.mfma_loop:
+        run_mfma_loop(torch, tgc, dev)
+        return
     if args.moe:
         run_moe(torch, tgc, synth, dev, prewarm_s=args.prewarm_s)
         return

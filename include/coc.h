@@ -63,7 +63,9 @@
  *     reduce, reduce-scatter, w8A16) on one GPU the reduction beside the
  *     matmul competes with it for the compute units' memory path and power,
  *     so the library pipelines them only when the reduction would take at
- *     least a sixth of the matmul's time (estimated from the sizes);
+ *     least a sixth of the matmul's time (estimated from the sizes) and some
+ *     chunk's tiles all come before the matmul's last round of tiles (a
+ *     matmul that fills the GPU once finishes every chunk together);
  *     otherwise the call runs the serial schedule.  Result bits never depend
  *     on the split or on this choice.
  *   - The *_trans_w entry points (matmul all-reduce / reduce-scatter /
@@ -463,6 +465,23 @@ coc_status coc_profile_records(int32_t* kclass, double* start_ms, double* end_ms
  * thread issues library calls. */
 void coc_profile_stamps(void* buf, int64_t records);
 int64_t coc_profile_stamp_count(void);
+
+/* Diagnostic for measurement (not part of the fused path): the rate the bf16
+ * MFMA unit sustains with nothing else running.  Launches `workgroups`
+ * workgroups of four waves on `stream`; each wave holds eight independent
+ * 32 x 32 fp32 accumulators and, `iters` times, issues one
+ * v_mfma_f32_32x32x16_bf16 into each, its operands kept in registers after
+ * one load from `operands` (a DEVICE buffer of bf16 values, at least 128
+ * bytes, 16-byte aligned; lane t takes vectors (8 t + i) mod count).  Writes
+ * one float per thread to `out` (a DEVICE buffer of at least workgroups x 256
+ * floats).  Work per launch: workgroups x 4 x iters x 8 x 32768 flops.
+ * Random operand values make the arrays toggle as a matmul of random data
+ * does; one repeated value barely toggles them, so timing both shows what the
+ * operand data alone does to the clock the chip holds.  Errors: NULL
+ * pointers (COC_ERR_NULL), misalignment (COC_ERR_ALIGN), sizes out of range
+ * (COC_ERR_SHAPE); nothing is launched then. */
+coc_status coc_diag_mfma_loop(const void* operands, size_t operand_bytes, float* out, size_t out_floats,
+                              int32_t workgroups, int32_t iters, hipStream_t stream);
 
 #ifdef __cplusplus
 }

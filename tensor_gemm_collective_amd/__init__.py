@@ -27,4 +27,5 @@ from .coc import (  # noqa: F401
     profile_stamp_count,
     profile_read,
     profile_records,
+    diag_mfma_loop,
 )

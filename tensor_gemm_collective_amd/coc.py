@@ -37,7 +37,7 @@ EXPORTS = (
     "coc_allgather_matmul_trans_w", "coc_allgather_matmul_noalloc", "coc_weight_grad", "coc_alltoall_grouped_matmul",
     "coc_grouped_matmul_alltoall", "coc_workspace_bytes", "coc_status_string",
     "coc_last_error", "coc_check_waits", "coc_plan", "coc_profile_enable", "coc_profile_read",
-    "coc_profile_records", "coc_profile_stamps", "coc_profile_stamp_count",
+    "coc_profile_records", "coc_profile_stamps", "coc_profile_stamp_count", "coc_diag_mfma_loop",
 )
 
 
@@ -109,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.coc_profile_stamps.restype = None
     L.coc_profile_stamp_count.argtypes = []
     L.coc_profile_stamp_count.restype = _i64
+    L.coc_diag_mfma_loop.argtypes = [_vp, _sz, _vp, _sz, _i32, _i32, _vp]
+    L.coc_diag_mfma_loop.restype = _i32
     L.coc_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64),
                                    ctypes.POINTER(ctypes.c_double)]
     L.coc_profile_read.restype = _i32
@@ -353,6 +355,18 @@ def profile_stamps(buf) -> None:
 def profile_stamp_count() -> int:
     """Records handed out to launches since the buffer was set."""
     return int(lib().coc_profile_stamp_count())
+
+
+def diag_mfma_loop(operands, out, workgroups: int, iters: int, stream=None) -> float:
+    """Enqueue the MFMA-rate diagnostic (coc.h, coc_diag_mfma_loop) on the
+    current stream: `operands` a bf16 device tensor, `out` a float32 device
+    tensor of at least workgroups x 256 elements.  Returns the launch's flops."""
+    import torch
+    assert operands.is_cuda and out.is_cuda and out.dtype == torch.float32
+    s = _stream(stream, operands.device)
+    _check(lib().coc_diag_mfma_loop(operands.data_ptr(), operands.numel() * operands.element_size(),
+                                     out.data_ptr(), out.numel(), workgroups, iters, s))
+    return float(workgroups) * 4 * iters * 8 * 32768
 
 
 def profile_read():

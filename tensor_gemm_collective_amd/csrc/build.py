@@ -22,8 +22,9 @@ LIB_PATH = os.path.join(PKG, "libcoc.so")
 ARCH = "gfx950"
 
 # coc_api.cpp holds host code and one device array (the allocation-free entry
-# point's scratch memory), so it takes the device pass as well.
-DEVICE_SOURCES = ["kernels.hip", "coc_api.cpp"]
+# point's scratch memory), so it takes the device pass as well; diag.hip holds
+# the MFMA-rate diagnostic.
+DEVICE_SOURCES = ["kernels.hip", "coc_api.cpp", "diag.hip"]
 HOST_SOURCES = ["coc_plan.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{HERE}"]

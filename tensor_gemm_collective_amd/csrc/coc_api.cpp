@@ -477,6 +477,23 @@ bool overlap_pays(const Plan& P) {
     return (bytes / kReduceBytesPerS) >= kOverlapMinRatio * (flops / kMatmulFlopPerS);
 }
 
+// Chunks of a compute-first one-launch plan that reduce beside the matmul:
+// those whose tiles all fall before the matmul's last round of workgroups
+// (the reduce waits on their counters, at most one workgroup per CU).  The
+// rest finish with the matmul; their rows (consecutive in every plan) reduce
+// in one full-grid launch after it on the caller's stream.  tiles receives
+// the per-chunk tile counts (chunks_tiles).
+int early_chunks(const Plan& P, const ChunksLaunch& L, int32_t tiles[kMaxPieces + 1]) {
+    chunks_tiles(L, tiles);
+    const int64_t groups = tiles[kMaxPieces] > 0 ? tiles[kMaxPieces] : 1;
+    int64_t total = 0;
+    for (int i = 0; i < P.nchunks; ++i) total += tiles[i];
+    const int64_t last_round = ((total - 1) / groups) * groups;   // first tile index of the last round
+    int early = 0;
+    for (int64_t cum = 0; early < P.nchunks - 1 && cum + tiles[early] <= last_round; ++early) cum += tiles[early];
+    return early;
+}
+
 // One-launch pipeline, compute first: the matmul walks the chunks in order on
 // the caller's stream and counts finished tiles per chunk; the reduce of each
 // early chunk, on the side stream from the start, waits for that chunk's
@@ -492,18 +509,8 @@ coc_status run_compute_first_chunks(const Plan& P, const GemmLaunch& g0, const R
     COC_TRY(chain.begin(c, main));
     const size_t es = elem_size(P.dt);
     ChunksLaunch L = chunks_for(P, g0);
-    // Chunks whose tiles all fall before the matmul's last round of workgroups
-    // reduce beside it (waiting on its counters, at most one workgroup per
-    // CU).  The rest finish with the matmul; their rows (consecutive in every
-    // plan) reduce in one full-grid launch after it on the caller's stream.
     int32_t tiles[kMaxPieces + 1];
-    chunks_tiles(L, tiles);
-    const int64_t groups = tiles[kMaxPieces] > 0 ? tiles[kMaxPieces] : 1;
-    int64_t total = 0;
-    for (int i = 0; i < P.nchunks; ++i) total += tiles[i];
-    const int64_t last_round = ((total - 1) / groups) * groups;   // first tile index of the last round
-    int early = 0;
-    for (int64_t cum = 0; early < P.nchunks - 1 && cum + tiles[early] <= last_round; ++early) cum += tiles[early];
+    const int early = early_chunks(P, L, tiles);
     if (early > 0) {
         COC_HIP(hipEventRecord(c->fork, main));
         COC_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
@@ -802,9 +809,18 @@ coc_status compute_first_op(coc_op op, const void* x, const void* w, const void*
     r0.n = n;
     bool cap = false;
     COC_TRY(capture_once(stream, &cap));
-    if (P.split > 1 && !cap && one_launch(P, g0) && !overlap_pays(P)) {
-        // a reduction too small to hide pays less than it costs beside the
-        // matmul: the serial schedule (the split-1 plan of the same op)
+    int32_t tiles[kMaxPieces + 1];
+    if (P.split > 1 && !cap && one_launch(P, g0) &&
+        (!overlap_pays(P) || early_chunks(P, chunks_for(P, g0), tiles) == 0)) {
+        // A reduction too small to hide pays less than it costs beside the
+        // matmul, and a matmul that finishes every chunk in its last round
+        // (BLOOM-7B: one round) leaves nothing to reduce beside it: the serial
+        // schedule (the split-1 plan of the same op; its two launches carry
+        // less host work than the pipeline's).  The stream's pipeline context
+        // is still set up here, so that a later capture of a split call on
+        // this stream (which runs the per-chunk pipeline) finds it.
+        StreamCtx* ctx = nullptr;
+        COC_TRY(get_ctx(stream, &ctx));
         Plan S;
         COC_TRY(make_plan(op, m, n, k, dt, world, rank, 1, det, &S));
         return run_compute_first(S, g0, r0, stream, cap);

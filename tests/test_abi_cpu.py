@@ -51,6 +51,18 @@ def test_status_strings():
         assert L.coc_status_string(code).decode() == name
 
 
+def test_mfma_loop_diagnostic_rejects_bad_arguments_on_the_host():
+    """Validation happens before any HIP call (nothing is launched)."""
+    L = tgc.lib()
+    assert L.coc_diag_mfma_loop(None, 4096, None, 256, 1, 1, None) == 1          # COC_ERR_NULL
+    assert L.coc_diag_mfma_loop(8, 4096, 40, 256, 1, 1, None) == 6              # COC_ERR_ALIGN
+    assert L.coc_diag_mfma_loop(4096, 64, 8192, 256, 1, 1, None) == 3           # too few operand vectors
+    assert L.coc_diag_mfma_loop(4096, 4096, 8192, 255, 1, 1, None) == 3         # out too small
+    assert L.coc_diag_mfma_loop(4096, 4096, 8192, 256, 0, 1, None) == 3         # no workgroups
+    assert L.coc_diag_mfma_loop(4096, 4096, 8192, 256, 1, 0, None) == 3         # no iterations
+    assert "out must hold" in L.coc_last_error().decode() or "iters" in L.coc_last_error().decode()
+
+
 def _rows_of(ch):
     rows = []
     for b in range(ch["nblk"]):

@@ -704,3 +704,18 @@ def test_activity_stamps_change_nothing_and_stay_in_bounds():
             assert kinds == {0, 1, 2}, kinds
         else:
             assert used == 0 and len(written) == 0
+
+
+@pytest.mark.gpu
+def test_mfma_loop_diagnostic_sums_exactly():
+    """coc_diag_mfma_loop with every operand 1.0: each of a thread's 8 x 16
+    accumulator elements gains 16 per iteration, so each output is 2048 x iters
+    exactly (bf16 products of ones, binary32 sums of small integers)."""
+    import torch
+    log("mfma loop diagnostic, 3 workgroups, 5 iterations")
+    ops = torch.ones(4096, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((3 * 256,), -1.0, dtype=torch.float32, device="cuda")
+    flops = tgc.diag_mfma_loop(ops, out, 3, 5)
+    torch.cuda.synchronize()
+    assert flops == 3 * 4 * 5 * 8 * 32768
+    assert torch.equal(out, torch.full_like(out, 2048.0 * 5))
