@@ -147,7 +147,7 @@ def sample_clock(step, torch, seconds=1.0, batch=40, per_batch=5, period=0.003):
     return out
 
 
-def run_mfma_loop(torch, tgc, dev, iters=500, reps=30):
+def run_mfma_loop(torch, tgc, dev, iters=4000, reps=20):
     """The MFMA-rate diagnostic (coc_diag_mfma_loop): v_mfma_f32_32x32x16_bf16
     on register operands, 8 waves per CU (as the ring matmul), random N(0,1)
     operands against one repeated value; launch time by events, then the clock
