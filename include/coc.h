@@ -363,8 +363,12 @@ coc_status coc_grouped_matmul_alltoall(const void* h, const void* w, void* y_loc
  *   coc_matmul_all_reduce.
  *
  * x_f16: m x k fp16; w_q: k x n int8; scales_f16: fp16 as above; y_f16,
- * partial_out, peer_bufs[r]: m x n fp16.  The int8 weight is dequantised to
- * fp16 (rounded to nearest even) inside the matmul main loop.  PER_GROUP
+ * partial_out, peer_bufs[r]: m x n fp16.  PER_TENSOR and PER_CHANNEL: the
+ * matmul multiplies X by q (each product exact in binary32), and the binary32
+ * sums are scaled before rounding to fp16.  PER_GROUP: the weight is
+ * dequantised to fp16 (q * s rounded to nearest even) inside the matmul main
+ * loop.  Either way the result matches X @ W~ within fp16 accuracy, and is
+ * exact when the scales are powers of two and the sums are exact.  PER_GROUP
  * requires group_size > 0, group_size % 8 == 0 and k % group_size == 0
  * (group_size is ignored otherwise).  Requires m % split == 0.  `ws` unused.
  */

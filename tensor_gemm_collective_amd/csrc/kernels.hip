@@ -6,8 +6,9 @@
 //               storage dtype.  The "Matmul" of the CoC guide's
 //               matmul/collective pairs ("Problem analysis").
 //   gemm_dma    the same for any k (a multiple of 8), 128 x 128 tiles.
-//   gemm_w8     the same with int8 weights dequantised to fp16 in the main
-//               loop (w8A16).
+//   gemm_w8     the same with int8 weights (w8A16): converted to fp16 in
+//               the main loop and scaled there per group, or the fp32 sums
+//               scaled in the epilogue per tensor / per channel.
 //   gemm_f32    the same for binary32 inputs on the vector ALUs.
 //   reduce_rows fixed-order sum of the ranks' partials for a block of rows:
 //               the AllReduce / ReduceScatter half of a pair.
@@ -280,8 +281,9 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 
 // Register-staged kernel for int8 weights (w8A16): tile BM x BN x 64, 256
 // threads as 2 x 2 waves.  Each thread loads an 8 k x 8 n block of int8
-// weights, dequantises it to fp16 (q * scale, rounded to nearest even) in
-// registers and stores it K-contiguous to LDS ([BN columns][64 k]); A goes to
+// weights, converts it to fp16 in registers (per group q * scale, rounded to
+// nearest even; otherwise q, and the epilogue scales the fp32 sums) and
+// stores it K-contiguous to LDS ([BN columns][64 k]); A goes to
 // LDS as [BM rows][64 k].  The 16-byte chunk c of an LDS row sits at
 // c ^ swz(row), which keeps the row stores and the MFMA operand reads of 8
 // consecutive lanes on distinct banks.
@@ -327,16 +329,8 @@ __global__ __launch_bounds__(256) void gemm_w8(GemmParams p) {
     u32x4 ra[A_ITERS];
     u32x4 rb[8];      // 16-bit weights: 8 k rows x 8 columns
     u32x2 rq[8];      // int8 weights:   8 k rows x 8 columns
-    u32x4 rs;         // fp16 scales of the 8 columns (per-channel / per-group)
-    uint32_t s0 = 0;  // per-tensor scale bits
-    if constexpr (KIND == GK_W8_F16) {
-        rs = u32x4{0, 0, 0, 0};
-        if (p.qmode == COC_PER_TENSOR) {
-            s0 = p.scales[0];
-        } else if (p.qmode == COC_PER_CHANNEL && bcolv) {
-            rs = *(const u32x4*)(p.scales + bcol);
-        }
-    }
+    u32x4 rs;         // fp16 scales of the 8 columns (per group)
+    if constexpr (KIND == GK_W8_F16) rs = u32x4{0, 0, 0, 0};
 
     auto load = [&](int k0) {
 #pragma unroll
@@ -371,18 +365,19 @@ __global__ __launch_bounds__(256) void gemm_w8(GemmParams p) {
         }
         if (bact) {
             if constexpr (KIND == GK_W8_F16) {
-                // dequantise: w = fp16(q) * scale, rounded to nearest even in fp16
+                // per group dequantise: w = fp16(q) * scale, rounded to nearest
+                // even in fp16; per tensor / per channel the tile holds q itself
+                // (exact in fp16) and the epilogue scales the fp32 sums
+                const bool grouped = p.qmode == COC_PER_GROUP;
                 uint32_t h[8][8];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    uint32_t sb;
-                    if (p.qmode == COC_PER_TENSOR) sb = s0;
-                    else sb = (c & 1) ? (rs[c >> 1] >> 16) : (rs[c >> 1] & 0xffffu);
+                    const uint32_t sb = (c & 1) ? (rs[c >> 1] >> 16) : (rs[c >> 1] & 0xffffu);
                     const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)sb);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int8_t q = (int8_t)((rq[j][c >> 2] >> (8 * (c & 3))) & 0xffu);
-                        const _Float16 w = (_Float16)(int)q * sc;
+                        const _Float16 w = grouped ? (_Float16)(int)q * sc : (_Float16)(int)q;
                         h[j][c] = __builtin_bit_cast(uint16_t, w);
                     }
                 }
@@ -459,6 +454,8 @@ __global__ __launch_bounds__(256) void gemm_w8(GemmParams p) {
     }
 
     // ---- epilogue: lane holds n = j*8 + (lane/32)*4 + {0..3} of row m = lane%32
+    // (w8A16 per tensor / per channel: sum * scale in fp32, then rounded;
+    // n % 8 == 0, so a group of four columns is wholly in range or wholly out)
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int r = m0 + wm * WTM + i * 32 + (lane & 31);
@@ -471,9 +468,22 @@ __global__ __launch_bounds__(256) void gemm_w8(GemmParams p) {
             for (int q = 0; q < 4; ++q) {
                 const int col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
                 if (col < p.n) {
+                    float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+                    if constexpr (KIND == GK_W8_F16) {
+                        if (p.qmode == COC_PER_TENSOR) {
+                            const float s0 = (float)__builtin_bit_cast(_Float16, p.scales[0]);
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) sc[t] = s0;
+                        } else if (p.qmode == COC_PER_CHANNEL) {
+                            const u32x2 sv = *(const u32x2*)(p.scales + col);
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                sc[t] = (float)__builtin_bit_cast(_Float16, (uint16_t)(sv[t >> 1] >> (16 * (t & 1))));
+                        }
+                    }
                     u32x2 v;
-                    v[0] = pack2<OUT_DT>(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-                    v[1] = pack2<OUT_DT>(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+                    v[0] = pack2<OUT_DT>(acc[i][j][q * 4 + 0] * sc[0], acc[i][j][q * 4 + 1] * sc[1]);
+                    v[1] = pack2<OUT_DT>(acc[i][j][q * 4 + 2] * sc[2], acc[i][j][q * 4 + 3] * sc[3]);
                     *(u32x2*)(crow + (int64_t)col * 2) = v;
                 }
             }
@@ -807,10 +817,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma(GemmParams p) {
 // w8A16 ring tiles keep the tile's per-group fp16 scales in LDS: at most this
 // many bytes (k / group rows of BN scales).
 constexpr int kW8TableBytes = 32768;
+// Kernel-side kind of the int8-weight ring kernels with per-group scales (the
+// host passes GK_W8_F16 and the scale mode): the main loop multiplies each
+// k-group by its scale, where the GK_W8_F16 kernels scale the fp32 sums in
+// the epilogue (per tensor / per channel).
+constexpr int GK_W8G_F16 = 4;
+constexpr bool is_w8(int kind) { return kind == GK_W8_F16 || kind == GK_W8G_F16; }
 
 template <int BM, int BN, int S, int WM, int WN, int KIND = GK_BF16>
 constexpr int ring_lds_bytes() {
-    const int ring = S * (BM * 32 * 2 + 32 * BN * (KIND == GK_W8_F16 ? 1 : 2)) + (KIND == GK_W8_F16 ? kW8TableBytes : 0);
+    const int ring = S * (BM * 32 * 2 + 32 * BN * (is_w8(KIND) ? 1 : 2)) + (is_w8(KIND) ? kW8TableBytes : 0);
     return ring > BM * BN * 2 ? ring : BM * BN * 2;   // the epilogue stages the tile in the same LDS
 }
 
@@ -831,7 +847,8 @@ template <int BM, int BN, int S, int WM, int WN, int KIND, bool SYS = false, boo
 __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb, int64_t base, int64_t stride,
                                           int64_t ashift, int m0, int n0, uint8_t* sm, bool poison) {
     constexpr int BK = 32, NW = WM * WN;
-    constexpr bool W8 = KIND == GK_W8_F16;   // int8 weights, fp16 activations
+    constexpr bool W8 = is_w8(KIND);           // int8 weights, fp16 activations
+    constexpr bool grouped = KIND == GK_W8G_F16;   // per-group scales
     constexpr int BE = W8 ? 1 : 2;            // weight bytes per element
     constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * BE, STAGE = A_BYTES + B_BYTES;
@@ -1016,7 +1033,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             dma16_sbase(bof[d - APW], p.b + (int64_t)kt * bstep, l + A_BYTES + (wave * BPW + d - APW) * 1024);
     };
     u32x4 af[2][FM], bf[2][FN];
-    u32x2 bq[2][FN];   // w8: raw int8 weight fragments, dequantised right before use
+    u32x2 bq[2][FN];   // w8: raw int8 weight fragments, converted right before use
     // fragment r of k step ks of a slot: weight fragments (two halves each, or
     // one int8 read each), then activation rows
     // h: PA, the stage's half of its pair block (kt & 1, a constant at every call)
@@ -1095,13 +1112,14 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
         }
     };
 
-    // w8A16 scales: spk[j] = this lane's scale (packed twice) for weight
-    // fragment j at the current stage.  Per tensor / per channel they are fixed
-    // for the tile; per group (group a multiple of 32, so one k-group per stage)
-    // the tile's k / group rows of BN scales sit in LDS and spn prefetches the
-    // next stage's.
+    // w8A16 scales.  Per tensor and per channel the scale is constant along k,
+    // so the main loop multiplies the activations by q itself (every product
+    // x * q is exact in fp32) and the epilogue multiplies the fp32 sums by the
+    // scale.  Per group (group a multiple of 32, so one k-group per stage) the
+    // weight is dequantised in registers: spk[j] = this lane's scale (packed
+    // twice) for weight fragment j at the current stage; the tile's k / group
+    // rows of BN scales sit in LDS and spn prefetches the next stage's.
     uint32_t spk[FN] = {}, spn[FN] = {};
-    const bool grouped = W8 && p.qmode == COC_PER_GROUP;
     auto scales_of = [&](int kt, uint32_t* out) {
         const COC_LDS uint16_t* tbl = (const COC_LDS uint16_t*)((const COC_LDS uint8_t*)sm + TBL);
         const int row = kt * BK / p.group;
@@ -1112,8 +1130,8 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
         }
     };
     // int8 fragment -> fp16: 0x6400 | (q ^ 0x80) is 1024 + q + 128 exactly, so
-    // subtracting 1152 gives q; one fp16 multiply by the scale then rounds
-    // q * scale to nearest even, the dequantised weight.
+    // subtracting 1152 gives q exactly.  Per group one fp16 multiply by the
+    // scale then rounds q * scale to nearest even, the dequantised weight.
     auto deq = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -1122,27 +1140,22 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
                                    __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u),
                                    __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u),
                                    __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)};
-            const f16x2 sc = __builtin_bit_cast(f16x2, spk[j]);
             const f16x2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+            if constexpr (grouped) {
+                const f16x2 sc = __builtin_bit_cast(f16x2, spk[j]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                bf[buf][j][e] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, d[e]) + off) * sc);
+                for (int e = 0; e < 4; ++e)
+                    bf[buf][j][e] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, d[e]) + off) * sc);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    bf[buf][j][e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, d[e]) + off);
+            }
         }
     };
     if constexpr (W8) {
-        const uint16_t* sg = (const uint16_t*)p.scales;
-        if (p.qmode == COC_PER_TENSOR) {
-            const uint32_t s = sg[0];
-#pragma unroll
-            for (int j = 0; j < FN; ++j) spk[j] = s | (s << 16);
-        } else if (p.qmode == COC_PER_CHANNEL) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-                const uint32_t s = sg[col < p.n ? col : 0];
-                spk[j] = s | (s << 16);
-            }
-        } else {
+        if constexpr (grouped) {
+            const uint16_t* sg = (const uint16_t*)p.scales;
             // the tile's scale rows into LDS: rows of BN fp16, 8 per 16-byte vector
             uint8_t* tbl = sm + TBL;
             const int rows_t = (p.k + p.group - 1) / p.group;
@@ -1196,11 +1209,11 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
         constexpr bool load = decltype(LOAD)::value, more = decltype(MORE)::value;
         constexpr int par = decltype(PAR)::value;   // PA: kt & 1
         const int slot = kt % S;
-        if constexpr (W8) {
-            if (grouped) {
+        if constexpr (grouped) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j) spk[j] = spn[j];
-            }
+            for (int j = 0; j < FN; ++j) spk[j] = spn[j];
+        }
+        if constexpr (W8) {
             deq(0);
         }
         // Phase 1 at the low wave priority: a wave that is still in phase 2
@@ -1232,8 +1245,8 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (W8) {
-            if (grouped && kt + 1 < KT) scales_of(kt + 1, spn);
+        if constexpr (grouped) {
+            if (kt + 1 < KT) scales_of(kt + 1, spn);
         }
     };
     using yes = std::true_type;
@@ -1293,6 +1306,41 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_nanf("");
     }
+    // w8A16 per tensor / per channel: the staging below stores sum * scale,
+    // in fp32, rounded once (lane columns as there; n % 16 == 0 on this path,
+    // so a group of four columns is wholly in range or wholly out).
+    constexpr bool SCALED = W8 && !grouped;
+    float sc[SCALED ? FN : 1][4][4];
+    if constexpr (SCALED) {
+        const uint16_t* sg = (const uint16_t*)p.scales;
+        if (p.qmode == COC_PER_CHANNEL) {
+            // (an opaque lane copy, as for the staging addresses below)
+            int sl;
+            asm volatile("v_mov_b32 %0, %1" : "=v"(sl) : "v"(lane));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = n0 + wn * WTN + j * 32 + q * 8 + (sl >> 5) * 4;
+                    const u32x2 v = col < p.n ? *(const u32x2*)(sg + col) : u32x2{0, 0};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        sc[j][q][t] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[t >> 1] >> (16 * (t & 1))));
+                }
+        } else {
+            const float s0 = (float)__builtin_bit_cast(_Float16, sg[0]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) sc[j][q][t] = s0;
+        }
+    }
+    auto outv = [&](int i, int j, int q, int t) {
+        if constexpr (SCALED) return acc[i][j][q * 4 + t] * sc[j][q][t];
+        else return acc[i][j][q * 4 + t];
+    };
 
     // Epilogue through LDS.  A lane holds n = q*8 + (lane/32)*4 + {0..3} of row
     // m = lane%32 in each 32 x 32 block; stored directly that gives 16-byte
@@ -1322,8 +1370,8 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
             for (int q = 0; q < 4; ++q) {
                 const int row = i * 32 + (el & 31);
                 u32x2 v;
-                v[0] = pack2<OUT_DT>(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-                v[1] = pack2<OUT_DT>(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+                v[0] = pack2<OUT_DT>(outv(i, j, q, 0), outv(i, j, q, 1));
+                v[1] = pack2<OUT_DT>(outv(i, j, q, 2), outv(i, j, q, 3));
                 *(COC_LDS u32x2*)(stg + row * RP + (((j * 4 + q) ^ (row & 7)) << 4) + (el >> 5) * 8) = v;
             }
     // (keeps the store addresses below from being computed while the
@@ -2016,7 +2064,7 @@ hipError_t launch_dma_kind(GemmParams p, int concurrent, hipStream_t s, bool tra
     // zero-fills the k tail.  Every choice walks k the same way, so it never
     // changes the result bits.
     if (p.k >= 32 && p.k % 32 == 0) {
-        if (concurrent <= 1 || KIND == GK_W8_F16 || trans_b) {
+        if (concurrent <= 1 || is_w8(KIND) || trans_b) {
             // a lone matmul: the chunk-walking launch with one chunk (measured
             // faster than one workgroup per tile: no second dispatch wave)
             ChunksLaunch L{};
@@ -2040,14 +2088,18 @@ hipError_t launch_dma_kind(GemmParams p, int concurrent, hipStream_t s, bool tra
             int32_t tiles[kMaxPieces + 1];
             return launch_chunks_kind<KIND>(L, s, tiles);
         }
-        const int64_t want = COC_RING_MIN_TILES / (concurrent > 1 ? concurrent : 1);
-        const int64_t tm256 = (p.rows + 255) / 256, tm128 = (p.rows + 127) / 128;
-        const int64_t tn256 = (p.n + 255) / 256;
-        if (tm256 * tn256 >= want) return launch_ring<256, 256, 4, 2, 4, KIND>(p, s);
-        if (tm128 * tn256 >= want) return launch_ring<128, 256, 4, 2, 4, KIND>(p, s);
-        return launch_ring<128, 128, 4, 2, 2, KIND>(p, s);
+        if constexpr (!is_w8(KIND)) {
+            const int64_t want = COC_RING_MIN_TILES / (concurrent > 1 ? concurrent : 1);
+            const int64_t tm256 = (p.rows + 255) / 256, tm128 = (p.rows + 127) / 128;
+            const int64_t tn256 = (p.n + 255) / 256;
+            if (tm256 * tn256 >= want) return launch_ring<256, 256, 4, 2, 4, KIND>(p, s);
+            if (tm128 * tn256 >= want) return launch_ring<128, 256, 4, 2, 4, KIND>(p, s);
+            return launch_ring<128, 128, 4, 2, 2, KIND>(p, s);
+        }
     }
-    return launch_dma<128, 128, 2, 2, 4, 32, KIND, false>(p, s);
+    // (int8 weights come here only with k % 32 == 0, through the chunk launch)
+    if constexpr (is_w8(KIND)) return hipErrorInvalidValue;
+    else return launch_dma<128, 128, 2, 2, 4, 32, KIND, false>(p, s);
 }
 
 }  // namespace
@@ -2426,6 +2478,7 @@ hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* til
         if (L.trans_a || L.trans_b) return hipErrorInvalidValue;
         for (int c = 0; c < L.npieces; ++c)
             if (L.bp[c] != nullptr) return hipErrorInvalidValue;   // one weight, one scale table
+        if (L.qmode == COC_PER_GROUP) return launch_chunks_layout<GK_W8G_F16, false, false>(L, s, tiles);
         return launch_chunks_layout<KIND, false, false>(L, s, tiles);
     } else {
         if (L.trans_a && L.trans_b) return hipErrorInvalidValue;
@@ -2440,9 +2493,10 @@ hipError_t launch_chunks_kind(const ChunksLaunch& L, hipStream_t s, int32_t* til
 }  // namespace
 
 bool chunks_reduce_narrow(const ChunksLaunch& L) {
-    // The int8-weight matmul (209-219 VGPRs) and the 256 x 256 paired-stage
-    // ones (208-210) leave 80 VGPRs per SIMD lane beside their two waves, too
-    // few for the two-vector waiting reduce (104); the others (<= 200) leave 112.
+    // The int8-weight matmuls (199-213 VGPRs) and the 256 x 256 paired-stage
+    // ones (208-210) leave 80-96 VGPRs per SIMD lane beside their two waves,
+    // too few for the two-vector waiting reduce (104); the others (<= 200)
+    // leave 112.
     if (L.kind == GK_W8_F16) return true;
     int bm = 0, bn = 0, per_cu = 0;
     const bool paired = COC_PAIR_A && !L.trans_a && L.k % 64 == 0;
