@@ -1790,7 +1790,10 @@ __global__ __launch_bounds__(256) void reduce_rows_wide(ReduceParams p, int per)
 }
 
 // U = 2: two vectors per thread (~100 VGPRs); U = 1 (~50 VGPRs) beside a
-// matmul that leaves less room.
+// matmul that leaves less room.  One workgroup per CU: with 128 or 64 the
+// reduce ran longer beside the matmul without speeding it up (BLOOM-176B
+// 409 / 488 against 401 us).  Streaming stores for the output (nothing in the
+// op reads it again): 0.3-0.6 % faster ops.
 template <int DT, int U>
 __global__ __launch_bounds__(256) void reduce_chunks_wait(ReduceParams p, ReduceChunks C) {
     const int stride = gridDim.x * 256;
@@ -1810,10 +1813,10 @@ __global__ __launch_bounds__(256) void reduce_chunks_wait(ReduceParams p, Reduce
             if (two) load_sources<DT>(p, C.own, so2, y);
             const u32x4 nan = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};   // NaN in every format
             const u32x4 o = ok ? sum_sources<DT>(p, x) : nan;
-            *(u32x4*)(p.dst + (C.dst_row0[c] + row) * p.row_bytes + (int64_t)(v - row * p.vpr) * 16) = o;
+            store16_stream(p.dst + (C.dst_row0[c] + row) * p.row_bytes + (int64_t)(v - row * p.vpr) * 16, o);
             if (two) {
                 const u32x4 o2 = ok ? sum_sources<DT>(p, y) : nan;
-                *(u32x4*)(p.dst + (C.dst_row0[c] + row2) * p.row_bytes + (int64_t)(v2 - row2 * p.vpr) * 16) = o2;
+                store16_stream(p.dst + (C.dst_row0[c] + row2) * p.row_bytes + (int64_t)(v2 - row2 * p.vpr) * 16, o2);
             }
         }
         if (p.stamps) stamp(p.stamps, blockIdx.x * C.nchunks + c, kStampReduce | (c << 8), t0, realtime());
