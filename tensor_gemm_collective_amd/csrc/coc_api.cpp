@@ -593,7 +593,11 @@ ChunksLaunch comm_first_launch(const Plan& P, const GemmLaunch& g0, const Gather
 }
 
 // The fused-gather fields of L for plan fp (the launch copies the rows
-// itself); the ready targets are left to the caller.
+// itself); the ready targets are left to the caller.  The plain all-gather's
+// tiles read the own shard's rows from the shard itself (the first piece of
+// comm_first_launch), so its gathered matrix is a workspace whose own rows
+// nothing reads: each chunk copies only its rows before and after the own
+// shard.  V2 hands the gathered matrix back, so it copies every row.
 void set_fused_gather(ChunksLaunch* L, const Plan& P, const GatherLaunch& a0, const FusedGatherPlan& fp,
                       const int64_t* grow0, const int64_t* grows) {
     L->gather_plan = fp;
@@ -601,9 +605,21 @@ void set_fused_gather(ChunksLaunch* L, const Plan& P, const GatherLaunch& a0, co
     L->gather_dst = a0.dst;
     L->gather_row_bytes = P.k * (int64_t)elem_size(P.dt);
     L->gather_shard_rows = P.m / P.world;
+    const int64_t own0 = P.rank * (P.m / P.world), own1 = own0 + P.m / P.world;
     for (int i = 0; i < P.nchunks; ++i) {
-        L->gather_row0[i] = grow0[i];
-        L->gather_rows[i] = grows[i];
+        const int64_t r0 = grow0[i], r1 = grow0[i] + grows[i];
+        if (P.op == COC_OP_ALLGATHER_MATMUL) {
+            const int64_t a1 = r1 < own0 ? r1 : own0, b0 = r0 > own1 ? r0 : own1;
+            L->gather_row0[i] = r0;
+            L->gather_rows[i] = a1 > r0 ? a1 - r0 : 0;
+            L->gather_row0b[i] = b0;
+            L->gather_rowsb[i] = r1 > b0 ? r1 - b0 : 0;
+        } else {
+            L->gather_row0[i] = r0;
+            L->gather_rows[i] = grows[i];
+            L->gather_row0b[i] = r1;
+            L->gather_rowsb[i] = 0;
+        }
     }
 }
 

@@ -131,16 +131,17 @@ struct ChunksLaunch {
     int32_t order;
     uint32_t spin_limit;     // polls before a wait gives up (0: the default, about 2 s)
     uint32_t* gave_up;       // set to non-zero by a wait that gives up (may be NULL)
-    // All-gather rows that the launch's one-tile workgroups copy before their
-    // tile (gather_nchunks > 0; see chunks_fused_gatherers): gathered row g of
-    // chunk c's rows [gather_row0[c], + gather_rows[c]) comes from row
-    // g % gather_shard_rows of gather_src[g / gather_shard_rows].
+    // All-gather rows that the launch copies itself (gather_nchunks > 0; see
+    // chunks_fused_gather): chunk c's rows [gather_row0[c], + gather_rows[c])
+    // and [gather_row0b[c], + gather_rowsb[c]) (0 rows: none); gathered row g
+    // comes from row g % gather_shard_rows of gather_src[g / gather_shard_rows].
     int32_t gather_nchunks;
     FusedGatherPlan gather_plan;   // as chunks_fused_gather returned it (the launch checks it)
     const void* gather_src[COC_MAX_WORLD];
     void* gather_dst;
     int64_t gather_row_bytes, gather_shard_rows;
     int64_t gather_row0[COC_MAX_SPLIT], gather_rows[COC_MAX_SPLIT];
+    int64_t gather_row0b[COC_MAX_SPLIT], gather_rowsb[COC_MAX_SPLIT];
 };
 
 // Layout of the chunk hand-over counters (device memory, 32-bit words): each

@@ -1447,7 +1447,10 @@ __device__ __forceinline__ const uint8_t* gather_src(const GatherParams& p, int 
 // single tile of the last two rounds, which have a tile's time to spare.
 struct FusedGather {
     GatherParams p;                    // src, dst, row_bytes, shard_rows, vpr (row0 / total per chunk)
+    // a chunk's rows: from row0[c], total[c] vectors, then from row0b[c],
+    // totalb[c] vectors (0: none)
     int32_t row0[COC_MAX_SPLIT], total[COC_MAX_SPLIT];
+    int32_t row0b[COC_MAX_SPLIT], totalb[COC_MAX_SPLIT];
     int32_t nchunks, early, gatherers; // gatherers == 0: no fused gather
 };
 
@@ -1479,7 +1482,8 @@ __device__ __forceinline__ void fused_gather(const FusedGather& F, int c0, int c
     const GatherParams& p = F.p;
     for (int c = c0; c < c1; ++c) {
         const uint64_t t0 = p.stamps ? realtime() : 0;
-        const int row0 = F.row0[c], total = F.total[c];
+        // the chunk's two row ranges as one run of vectors
+        const int row0 = F.row0[c], ta = F.total[c], row0b = F.row0b[c], total = ta + F.totalb[c];
         const int v0 = (int)((int64_t)gi * total / ng), v1 = (int)((int64_t)(gi + 1) * total / ng);
         for (int b = v0 + (int)threadIdx.x; b < v1; b += U * nt) {
             u32x4 x[U];
@@ -1487,7 +1491,8 @@ __device__ __forceinline__ void fused_gather(const FusedGather& F, int c0, int c
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int v = b + u * nt;
-                if (v < v1) x[u] = load16_stream(gather_src(p, row0, v, &off[u]));
+                const bool second = v >= ta;
+                if (v < v1) x[u] = load16_stream(gather_src(p, second ? row0b : row0, second ? v - ta : v, &off[u]));
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -2437,6 +2442,8 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
         for (int c = 0; c < L.gather_nchunks; ++c) {
             F.row0[c] = (int32_t)L.gather_row0[c];
             F.total[c] = (int32_t)(L.gather_rows[c] * F.p.vpr);
+            F.row0b[c] = (int32_t)L.gather_row0b[c];
+            F.totalb[c] = (int32_t)(L.gather_rowsb[c] * F.p.vpr);
         }
         F.gatherers = fp.gatherers;
         F.early = fp.early;

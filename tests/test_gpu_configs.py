@@ -127,16 +127,22 @@ def llama_ag():
     return wl, shards, w, G, y_ref
 
 
-@pytest.mark.parametrize("split", [4, 8])
-@pytest.mark.parametrize("rank", [0, 3])
+@pytest.mark.parametrize("split", [2, 4, 8])
+@pytest.mark.parametrize("rank", [0, 1, 3])
 def test_llama_allgather_matmul(llama_ag, split, rank):
+    """V2's gathered matrix is the shards' bits; the plain op gives V2's bits.
+    The plain op's workspace starts as NaN: its tiles read the own shard's
+    rows from the shard itself and it copies only the other rows, so no NaN
+    may reach y.  Ranks 0, 1, 3 at splits 2, 4, 8 put the own shard at the
+    start, in the middle or at the end of its chunk, or make it the chunk."""
     wl, shards, w, _, y_ref = llama_ag
     log(f"LLaMA2-70B AG bf16 m={wl.m} k={wl.k} n={wl.n} split={split} rank={rank}")
     sd = [s.to(DEV) for s in shards]
     peers = [None if r == rank else sd[r] for r in range(wl.world)]
     wd = w.to(DEV)
     y, g = tgc.allgather_matmul(sd[rank], peers, wd, rank, split=split, v2=True)
-    y1 = tgc.allgather_matmul(sd[rank], peers, wd, rank, split=split)
+    ws = torch.full((wl.m * wl.k * 2,), 0xFF, dtype=torch.uint8, device=DEV)   # bf16 NaN everywhere
+    y1 = tgc.allgather_matmul(sd[rank], peers, wd, rank, split=split, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(g.view(torch.int16), torch.cat(sd).view(torch.int16)), "gathered rows differ"
     assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), "V2 and plain results differ"
