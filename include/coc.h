@@ -213,7 +213,9 @@ coc_status coc_matmul_reduce_scatter(const void* x, const void* w, void* y, void
  *
  * x_shard and peer_bufs[r]: (m/world) x k shards; w: k x n; y: m x n.
  * gathered_out == NULL selects ALL_GATHER_MATMUL (G is staged in `ws`, which
- * must hold coc_workspace_bytes(COC_OP_ALLGATHER_MATMUL, ...) bytes);
+ * must hold coc_workspace_bytes(COC_OP_ALLGATHER_MATMUL, ...) bytes; its
+ * contents afterwards are unspecified: the matmul may read the own shard's
+ * rows from x_shard and leave them out of `ws`);
  * gathered_out != NULL selects ALL_GATHER_MATMUL_V2 and receives G (m x k,
  * bit-exact copy of the shards; `ws` unused).  The gather of chunk i+1
  * overlaps the matmul of chunk i; the pipeline starts with the chunk that
