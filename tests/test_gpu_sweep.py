@@ -1,4 +1,5 @@
-"""Seeded sweep over shapes and options of every op, against the oracle.
+"""Seeded sweep over shapes and options of every op, against the oracle
+(the matmul-collective ops here; the MoE pair and the weight gradient below).
 
 Each case draws, from its own seed: the op (all-reduce, reduce-scatter,
 all-gather, all-gather V2, w8A16 all-reduce), the dtype, world size and rank,
@@ -172,3 +173,85 @@ def test_sweep(c):
         torch.cuda.synchronize()
         p_exact = oracle.matmul(f64(x, "f16"), oracle.dequant_weight(q.numpy(), f64(s, "f16"), mode, group))
         _check_reduce(c, y, p, p_exact, peers, np.arange(m), "w8a16")
+
+
+# ------------------------------------------------------------------ MoE pair and weight gradient
+def _draw_moe(i):
+    r = random.Random(104729 * (i + 1))
+    world = r.choice([1, 2, 4, 8])
+    local = r.choice([1, 2, 4])
+    pieces = r.choice([p for p in (1, 2, 4) if p * local <= 16 and p * local * world <= 128])
+    return synth.MoeWorkload(f"sweep{i}", WID_SWEEP + 200 + i, r.choice(["bf16", "f16"]), world, world * local,
+                             r.choice([1, 2]) if world * local > 1 else 1, r.randint(1, 600),
+                             32 * r.randint(1, 16), 32 * r.randint(1, 16), pieces, rank=r.randrange(world))
+
+
+MOE_CASES = [_draw_moe(i) for i in range(24)]
+
+
+def _moe_id(wl):
+    return (f"{wl.name}-{wl.dtype}-w{wl.world}r{wl.rank}-e{wl.experts}top{wl.topk}-p{wl.pieces}"
+            f"-t{wl.tokens}-h{wl.hidden}-f{wl.ffn}")
+
+
+@pytest.mark.parametrize("wl", MOE_CASES, ids=[_moe_id(w) for w in MOE_CASES])
+def test_sweep_moe(wl):
+    """Dispatch (all-to-all, then the grouped matmul) and combine (grouped
+    matmul, then the all-to-all back) on seeded routings: received rows and
+    returned rows bit for bit, matmul results normwise (Ampipe page, the
+    expert all-to-all pair)."""
+    from tests.test_gpu_moe import check_combine_copy, run_combine, run_dispatch
+    counts = synth.moe_counts(wl)
+    total = int(counts.sum())
+    log(f"sweep moe {_moe_id(wl)}: {total} rows")
+    sends = synth.moe_sends(wl, counts, wl.hidden)
+    w1 = synth.moe_weights(wl, wl.hidden, wl.ffn)
+    y, recv = run_dispatch(wl, counts, sends, w1)
+    y_ref, recv_ref = oracle.alltoall_grouped_matmul([f64(s, wl.dtype) for s in sends], counts,
+                                                     list(f64(w1, wl.dtype)))
+    assert tuple(recv.shape) == (total, wl.hidden) and tuple(y.shape) == (total, wl.ffn)
+    if total:
+        assert_bits_equal(recv, encode_dtype(recv_ref, wl.dtype), "received rows")
+        assert_close(y, y_ref, wl.dtype, "grouped matmul after the dispatch")
+    h = synth.normal(wl.wid, synth.T_SEND, 100, (total, wl.ffn), 1.0, wl.dtype)
+    w2 = synth.moe_weights(wl, wl.ffn, wl.hidden, which=1)
+    outs, y_local = run_combine(wl, counts, h, w2)
+    outs_ref, y2_ref = oracle.grouped_matmul_alltoall(f64(h, wl.dtype), counts, list(f64(w2, wl.dtype)))
+    if total:
+        assert_close(y_local, y2_ref, wl.dtype, "grouped matmul before the combine")
+    for r in range(wl.world):
+        assert outs[r].shape[0] == outs_ref[r].shape[0]
+    check_combine_copy(y_local, outs, counts)
+
+
+def _draw_wgrad(i):
+    r = random.Random(15485863 * (i + 1))
+    return dict(i=i, dt=r.choice(["bf16", "f16"]), m=32 * r.randint(1, 64), n=8 * r.randint(1, 130),
+                k=8 * r.randint(1, 130), integer=r.random() < 0.5)
+
+
+WGRAD_CASES = [_draw_wgrad(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("c", WGRAD_CASES,
+                         ids=[f"{c['i']:02d}-{c['dt']}-{c['m']}x{c['n']}x{c['k']}-{'int' if c['integer'] else 'rnd'}"
+                              for c in WGRAD_CASES])
+def test_sweep_weight_grad(c):
+    """dW = G^T dY (the backward of the sequence-parallel pair): exact bits for
+    integer-valued inputs (|sum| <= 16 m < 2^24), normwise otherwise."""
+    dt, m, n, k = c["dt"], c["m"], c["n"], c["k"]
+    log(f"sweep weight_grad {dt} m={m} n={n} k={k}")
+    wid = WID_SWEEP + 300 + c["i"]
+    if c["integer"]:
+        g = synth.integers(wid, synth.T_X, 0, (m, k), -4, 4, dt)
+        dy = synth.integers(wid, synth.T_W, 0, (m, n), -4, 4, dt)
+    else:
+        g = synth.normal(wid, synth.T_X, 0, (m, k), 1.0, dt)
+        dy = synth.normal(wid, synth.T_W, 0, (m, n), 1.0, dt)
+    dw = tgc.weight_grad(dev(g), dev(dy))
+    torch.cuda.synchronize()
+    ref = oracle.weight_grad(f64(g, dt), f64(dy, dt))
+    if c["integer"]:
+        assert_bits_equal(dw, encode_dtype(ref, dt), "dW")
+    else:
+        assert_close(dw, ref, dt, "dW")
