@@ -127,14 +127,28 @@ def llama_ag():
     return wl, shards, w, G, y_ref
 
 
+@pytest.fixture(scope="module")
+def llama_ag_serial(llama_ag):
+    """y of the serial form (split 1: every row gathered, then one matmul
+    whose tiles each run all of k in one workgroup), as raw bits.  G is the
+    same whatever the rank, so this is every rank's y."""
+    wl, shards, w, _, _ = llama_ag
+    sd = [s.to(DEV) for s in shards]
+    y = tgc.allgather_matmul(sd[0], [None] + sd[1:], w.to(DEV), 0, split=1)
+    torch.cuda.synchronize()
+    return y.cpu().view(torch.int16)
+
+
 @pytest.mark.parametrize("split", [2, 4, 8])
 @pytest.mark.parametrize("rank", [0, 1, 3])
-def test_llama_allgather_matmul(llama_ag, split, rank):
-    """V2's gathered matrix is the shards' bits; the plain op gives V2's bits.
-    The plain op's workspace starts as NaN: its tiles read the own shard's
-    rows from the shard itself and it copies only the other rows, so no NaN
-    may reach y.  Ranks 0, 1, 3 at splits 2, 4, 8 put the own shard at the
-    start, in the middle or at the end of its chunk, or make it the chunk."""
+def test_llama_allgather_matmul(llama_ag, llama_ag_serial, split, rank):
+    """V2's gathered matrix is the shards' bits; the plain op and V2 give the
+    serial form's bits (the chunked one-launch pipeline, its fused copy and
+    its tile order change when each tile runs, never what it adds).  The plain op's
+    workspace starts as NaN: its tiles read the own shard's rows from the
+    shard itself and it copies only the other rows, so no NaN may reach y.
+    Ranks 0, 1, 3 at splits 2, 4, 8 put the own shard at the start, in the
+    middle or at the end of its chunk, or make it the chunk."""
     wl, shards, w, _, y_ref = llama_ag
     log(f"LLaMA2-70B AG bf16 m={wl.m} k={wl.k} n={wl.n} split={split} rank={rank}")
     sd = [s.to(DEV) for s in shards]
@@ -146,6 +160,7 @@ def test_llama_allgather_matmul(llama_ag, split, rank):
     torch.cuda.synchronize()
     assert torch.equal(g.view(torch.int16), torch.cat(sd).view(torch.int16)), "gathered rows differ"
     assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), "V2 and plain results differ"
+    assert torch.equal(y1.cpu().view(torch.int16), llama_ag_serial), "pipelined and serial results differ"
     assert_close(y, y_ref, "bf16", "y")
 
 
