@@ -108,6 +108,13 @@
  * COC_SPIN_LIMIT=n (polls before giving up) and COC_TEST_UNREACHABLE_WAIT=1
  * (the calls made meanwhile wait for counts that never arrive; the library's
  * own counter bookkeeping stays exact, so later calls are unaffected).
+ *
+ * Matmul tiles.  The kernel and tile a call runs never change its result
+ * bits.  A bf16 / fp16 matmul with transposed weights (the *_trans_w entry
+ * points) whose launch runs alone (nothing waits beside it) and fills the
+ * device with 256 x 256 tiles, k % 64 == 0, uses a four-wave tile; every
+ * other launch the eight-wave one.  COC_FOUR_WAVE=0, read at each call,
+ * keeps the eight-wave tile everywhere (for comparisons).
  */
 #ifndef COC_H
 #define COC_H

@@ -1392,6 +1392,217 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
     }
 }
 
+// ------------------------------------------------------------------ four-wave tile
+// The 256 x 256 tile of the bf16 / fp16 launches with transposed weights (W
+// stored n x k, so both operands are k-contiguous) that run alone (no counter
+// to signal or wait on, no copy inside the launch), k % 64 == 0: four waves
+// of 128 x 128 (2 x 2), v_mfma_f32_16x16x32 (16 rows or columns by 32 k per
+// instruction, where ring_tile's v_mfma_f32_32x32x16 takes 32 by 16).  Per
+// 32 k the four waves read 64 KB of LDS fragments where ring_tile's eight
+// 128 x 64 waves read 96 KB.  One workgroup per CU uses nearly the whole
+// register file (one wave per SIMD), so nothing that must share a CU with the
+// matmul (a reduce waiting on its counters) can run beside it: launches that
+// signal, wait or copy keep ring_tile.  Both tiles add each output's products
+// in the same 8-k steps in increasing k (the MFMA shapes differ only in how
+// many steps one instruction takes), so they give the same bits, and no
+// result depends on which one ran.
+//
+// k runs in 64-k stages (whole 128-byte rows of both operands) through two
+// LDS slots of 64 KB: the activations as 256 rows of 128 bytes (chunk c of
+// row r at c ^ gP(r)), then the weights as 256 n rows of 128 bytes the same
+// way.  Within a stage two k steps of 32; each step's 16 fragment reads (one
+// activation and eight weight fragments, then seven activation fragments:
+// first-use order) run under the previous step's 64 MFMAs.  The barrier sits
+// BAR_AT MFMAs into a stage's second step: after it the next stage's
+// fragments are read and the stage after next is loaded into the slot just
+// read, spread one load every DSTEP MFMAs (its remaining loads go in the next
+// stage's first step).
+constexpr int kQuadSlot = 256 * 64 * 2 * 2;   // activations + weights of one 64-k stage
+constexpr int kQuadLds = 2 * kQuadSlot;        // 128 KB
+
+template <int KIND>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (KIND == GK_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                       0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+}
+
+template <int KIND, bool SYS>
+__device__ __forceinline__ void quad_tile(const GemmParams& p, int rows, int rpb, int64_t base, int64_t stride,
+                                          int64_t ashift, int m0, int n0, uint8_t* sm, bool poison) {
+    constexpr int BK = 64;
+    constexpr int A_ST = 256 * BK * 2;   // 32 KB of activations per stage
+    constexpr int OUT_DT = (KIND == GK_BF16) ? COC_BF16 : COC_F16;
+    constexpr int BAR_AT = 16, DSTEP = 4;
+    constexpr int DSPLIT = (64 - BAR_AT + DSTEP - 1) / DSTEP > 16 ? 16 : (64 - BAR_AT + DSTEP - 1) / DSTEP;
+    // An opaque copy of the lane index: in a loop over tiles the compiler
+    // would otherwise compute every lane-only offset once, before the loop,
+    // and hold them all in registers through it (spilling the k loop's).
+    int lane;
+    asm volatile("v_and_b32 %0, 63, %1" : "=v"(lane) : "v"(threadIdx.x));
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t lds0 = lds_u32(sm);
+
+    // loads: each of a wave's 8 activation instructions covers 8 rows of 128
+    // bytes, and each of its 8 weight instructions 8 n rows of 128 bytes
+    uint32_t aof[8], bof[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = (wave * 8 + i) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ gP(row);
+        const int r = m0 + row < rows ? m0 + row : rows - 1;
+        const int64_t gr = map_row(r, rpb, base, stride) + ashift;
+        aof[i] = (uint32_t)(gr * p.k * 2) + (uint32_t)(c * 16);
+        const int nr = n0 + row < p.n ? n0 + row : p.n - 1;
+        bof[i] = (uint32_t)nr * (uint32_t)p.k * 2 + (uint32_t)(c * 16);
+    }
+    auto issue = [&](int d, int kt, int slot) {
+        const uint32_t l = lds0 + slot * kQuadSlot;
+        if (d < 8) dma16_sbase(aof[d], p.a + (int64_t)kt * BK * 2, l + (wave * 8 + d) * 1024);
+        else dma16_sbase(bof[d - 8], p.b + (int64_t)kt * BK * 2, l + A_ST + (wave * 8 + d - 8) * 1024);
+    };
+
+    // fragments: lane l holds row (activations) or column (weights) l % 16
+    // of its 16-wide block, k 8 (l / 16) .. + 7 of the 32-k step
+    const int arow = wm * 128 + (lane & 15), brow = wn * 128 + (lane & 15);
+    u32x4 af[2][8], bf[2][8];
+    auto read_a = [&](int slot, int ks, int buf, int i) {
+        const int c = (ks * 4 + (lane >> 4)) ^ gP(arow);   // gP has a 16-row period
+        af[buf][i] = *(const COC_LDS u32x4*)((const COC_LDS uint8_t*)sm + slot * kQuadSlot + (arow + i * 16) * 128 +
+                                            c * 16);
+    };
+    auto read_b = [&](int slot, int ks, int buf, int j) {
+        const int c = (ks * 4 + (lane >> 4)) ^ gP(brow);
+        bf[buf][j] = *(const COC_LDS u32x4*)((const COC_LDS uint8_t*)sm + slot * kQuadSlot + A_ST + (brow + j * 16) * 128 +
+                                            c * 16);
+    };
+    // read r of a k step's 16, in first-use order: A0, B0 .. B7, A1 .. A7
+    auto read_r = [&](int r, int slot, int ks, int buf) {
+        if (r == 0) read_a(slot, ks, buf, 0);
+        else if (r < 9) read_b(slot, ks, buf, r - 1);
+        else read_a(slot, ks, buf, r - 8);
+    };
+
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int KT = p.k / BK;   // >= 1 (quad_core requires k % 64 == 0)
+    for (int d = 0; d < 16; ++d) issue(d, 0, 0);
+    if (KT > 1) {
+        for (int d = 0; d < 16; ++d) issue(d, 1, 1);
+        wait_vmcnt<16>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    block_barrier();
+    for (int r = 0; r < 16; ++r) read_r(r, 0, 0, 0);
+
+    // MORE: a next stage to read; LOAD2: stage kt + 2 to load; REST: the
+    // remaining loads of stage kt + 1 (its first DSPLIT went in stage kt - 1)
+    auto stage = [&](int kt, auto MORE, auto LOAD2, auto REST) {
+        constexpr bool more = decltype(MORE)::value, load2 = decltype(LOAD2)::value;
+        constexpr bool rest = decltype(REST)::value;
+        const int slot = kt & 1, nslot = slot ^ 1;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 64; ++s) {
+            acc[s >> 3][s & 7] = mfma16<KIND>(bf[0][s & 7], af[0][s >> 3], acc[s >> 3][s & 7]);
+            if (s < 16) read_r(s, slot, 1, 1);
+            if constexpr (rest) {
+                const int g = 64 + s - BAR_AT;
+                if (g % DSTEP == 0) {
+                    const int d = g / DSTEP;
+                    if (d >= DSPLIT && d < 16) issue(d, kt + 1, nslot);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int s = 0; s < BAR_AT; ++s) {
+            acc[s >> 3][s & 7] = mfma16<KIND>(bf[1][s & 7], af[1][s >> 3], acc[s >> 3][s & 7]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (more) {
+            wait_vmcnt<0>();
+            block_barrier();
+        }
+#pragma unroll
+        for (int s = BAR_AT; s < 64; ++s) {
+            acc[s >> 3][s & 7] = mfma16<KIND>(bf[1][s & 7], af[1][s >> 3], acc[s >> 3][s & 7]);
+            if constexpr (more) {
+                if (s - BAR_AT < 16) read_r(s - BAR_AT, nslot, 0, 0);
+            }
+            if constexpr (load2) {
+                const int g = s - BAR_AT;
+                if (g % DSTEP == 0 && g / DSTEP < DSPLIT) issue(g / DSTEP, kt + 2, slot);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    int kt = 0;
+    if (KT > 2) {
+        stage(0, yes{}, yes{}, no{});
+        for (kt = 1; kt + 2 < KT; ++kt) stage(kt, yes{}, yes{}, yes{});
+        stage(kt, yes{}, no{}, yes{});
+        ++kt;
+    } else if (KT == 2) {
+        stage(0, yes{}, no{}, no{});
+        ++kt;
+    }
+    stage(kt, no{}, no{}, no{});
+
+    if (poison) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                                         __builtin_nanf("")};
+    }
+
+    // Epilogue through LDS: lane l of block (i, j) holds rows m = i*16 + l%16,
+    // columns n = j*16 + (l/16)*4 + 0..3.  Each wave stages its 128 x 128 tile
+    // in the storage dtype (rows of 256 bytes, 16-byte chunk c of row r at
+    // c ^ (r & 15)), then stores whole 256-byte rows, 16 bytes per lane.
+    block_barrier();
+    int el;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));   // (see ring_tile's epilogue)
+    COC_LDS uint8_t* stg = (COC_LDS uint8_t*)sm + wave * (128 * 256);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = i * 16 + (el & 15);
+            const int col = j * 16 + (el >> 4) * 4;
+            u32x2 v;
+            v[0] = pack2<OUT_DT>(acc[i][j][0], acc[i][j][1]);
+            v[1] = pack2<OUT_DT>(acc[i][j][2], acc[i][j][3]);
+            *(COC_LDS u32x2*)(stg + row * 256 + (((col >> 3) ^ (row & 15)) << 4) + (col & 7) * 2) = v;
+        }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+        const int row = t * 4 + (el >> 4), ch = el & 15;
+        const u32x4 v = *(const COC_LDS u32x4*)(stg + row * 256 + ((ch ^ (row & 15)) << 4));
+        const int r = m0 + wm * 128 + row, col = n0 + wn * 128 + ch * 8;
+        if (r < rows && col < p.n) {
+            const int64_t off = map_row(r, rpb, base, stride) * (int64_t)p.n * 2 + (int64_t)col * 2;
+            if constexpr (SYS)
+                store16_sys(sys_rsrc(p.c), (uint32_t)off, v);
+            else
+                *(u32x4*)(p.c + off) = v;
+        }
+    }
+}
+
 template <int BM, int BN, int S, int WM, int WN, int KIND>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_ring(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t sm[ring_lds_bytes<BM, BN, S, WM, WN, KIND>()];
@@ -1505,10 +1716,14 @@ __device__ __forceinline__ void fused_gather(const FusedGather& F, int c0, int c
     }
 }
 
+// QUAD: 256 x 256 tiles of quad_tile (four waves, WM = WN = 2; transposed
+// weights, nothing to signal or wait on).
 template <int BM, int BN, int S, int WM, int WN, int KIND, bool SIGNAL, bool TA = false, bool TB = false,
-          bool PA = false>
+          bool PA = false, bool QUAD = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P) {
-    __shared__ __attribute__((aligned(1024))) uint8_t sm[ring_lds_bytes<BM, BN, S, WM, WN, KIND>()];
+    static_assert(!QUAD || (BM == 256 && BN == 256 && WM == 2 && WN == 2 && TB && !TA && !SIGNAL),
+                  "four-wave tile shape");
+    __shared__ __attribute__((aligned(1024))) uint8_t sm[QUAD ? kQuadLds : ring_lds_bytes<BM, BN, S, WM, WN, KIND>()];
     constexpr int NX = 8;
     const int x = blockIdx.x % NX, w = blockIdx.x / NX;
     const int tn_all = P.g.tiles_n;
@@ -1547,8 +1762,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P
         GemmParams g = P.g;
         g.a = P.a[c];
         g.b = P.b[c];
-        ring_tile<BM, BN, S, WM, WN, KIND, SIGNAL, TA, TB, PA>(g, P.rows[c], P.rpb[c], P.base[c], P.stride[c], P.ashift[c],
-                                                   tm * BM, tn * BN, sm, wi >= 0 && !ok);
+        if constexpr (QUAD)
+            quad_tile<KIND, false>(g, P.rows[c], P.rpb[c], P.base[c], P.stride[c], P.ashift[c], tm * BM, tn * BN, sm,
+                                   wi >= 0 && !ok);
+        else
+            ring_tile<BM, BN, S, WM, WN, KIND, SIGNAL, TA, TB, PA>(g, P.rows[c], P.rpb[c], P.base[c], P.stride[c],
+                                                                   P.ashift[c], tm * BM, tn * BN, sm, wi >= 0 && !ok);
         if constexpr (SIGNAL) {
             if (P.signal[c] >= 0) wg_signal(P.done + P.signal[c] * kSyncWords);
         }
@@ -2390,7 +2609,7 @@ int device_cus() {
     return cus[dev];
 }
 
-template <int BM, int BN, int S, int WM, int WN, int KIND, bool TA, bool TB>
+template <int BM, int BN, int S, int WM, int WN, int KIND, bool TA, bool TB, bool QUAD = false>
 hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s, int32_t* tiles) {
     PersistParams P{};
     P.g.b = (const uint8_t*)L.b;
@@ -2451,29 +2670,56 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     tiles[kMaxPieces] = 8 * P.per_xcd;
     P.stamps = stamp_region((int64_t)8 * P.per_xcd * (1 + P.fg.nchunks));
     P.fg.p.stamps = P.stamps;
-    // activations in whole 128-byte row segments, two stages at a time (k % 64 == 0)
-    if constexpr (COC_PAIR_A && !TA) {
-        if (L.k % 64 == 0) {
-            if (signal)
-                hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true, false, TB, true>),
-                                   dim3(8 * P.per_xcd), dim3(64 * WM * WN), 0, s, P);
-            else
-                hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, false, false, TB, true>),
-                                   dim3(8 * P.per_xcd), dim3(64 * WM * WN), 0, s, P);
-            return hipGetLastError();
+    if constexpr (QUAD) {
+        // (the caller checked quad_ok: nothing signals, waits or copies)
+        if (signal || L.gather_nchunks > 0 || L.k % 64 != 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemm_ring_chunks<256, 256, 4, 2, 2, KIND, false, false, true, false, true>),
+                           dim3(8 * P.per_xcd), dim3(256), 0, s, P);
+        return hipGetLastError();
+    } else {
+        // activations in whole 128-byte row segments, two stages at a time (k % 64 == 0)
+        if constexpr (COC_PAIR_A && !TA) {
+            if (L.k % 64 == 0) {
+                if (signal)
+                    hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true, false, TB, true>),
+                                       dim3(8 * P.per_xcd), dim3(64 * WM * WN), 0, s, P);
+                else
+                    hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, false, false, TB, true>),
+                                       dim3(8 * P.per_xcd), dim3(64 * WM * WN), 0, s, P);
+                return hipGetLastError();
+            }
         }
+        if (signal)
+            hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true, TA, TB>), dim3(8 * P.per_xcd),
+                               dim3(64 * WM * WN), 0, s, P);
+        else
+            hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, false, TA, TB>), dim3(8 * P.per_xcd),
+                               dim3(64 * WM * WN), 0, s, P);
+        return hipGetLastError();
     }
-    if (signal)
-        hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, true, TA, TB>), dim3(8 * P.per_xcd),
-                           dim3(64 * WM * WN), 0, s, P);
-    else
-        hipLaunchKernelGGL((gemm_ring_chunks<BM, BN, S, WM, WN, KIND, false, TA, TB>), dim3(8 * P.per_xcd),
-                           dim3(64 * WM * WN), 0, s, P);
-    return hipGetLastError();
+}
+
+// Whether a launch takes the four-wave tile: bf16 / fp16 with transposed
+// weights, 256 x 256 tiles, k % 64 == 0, and nothing beside it to share a CU
+// with (no counter to signal, no wait, no copy inside the launch).
+// COC_FOUR_WAVE=0 keeps ring_tile (the result bits are the same; for A/B
+// timing).
+bool quad_ok(const ChunksLaunch& L) {
+    const char* v = getenv("COC_FOUR_WAVE");
+    if (v != nullptr && v[0] == '0') return false;
+    if (!(L.kind == GK_BF16 || L.kind == GK_F16) || !L.trans_b || L.trans_a || L.k % 64 != 0) return false;
+    if (L.gather_nchunks > 0) return false;
+    for (int c = 0; c < L.npieces; ++c)
+        if (L.wait[c] >= 0 || (L.done != nullptr && L.signal[c] >= 0)) return false;
+    int bm = 0, bn = 0, per_cu = 0;
+    return chunks_shape(L, &bm, &bn, &per_cu) == 0;
 }
 
 template <int KIND, bool TA, bool TB>
 hipError_t launch_chunks_layout(const ChunksLaunch& L, hipStream_t s, int32_t* tiles) {
+    if constexpr ((KIND == GK_BF16 || KIND == GK_F16) && TB && !TA) {
+        if (quad_ok(L)) return launch_chunks_shape<256, 256, 4, 2, 2, KIND, false, true, true>(L, 1, s, tiles);
+    }
     int bm, bn, per_cu;
     switch (chunks_shape(L, &bm, &bn, &per_cu)) {
         case 0: return launch_chunks_shape<256, 256, 4, 2, 4, KIND, TA, TB>(L, 1, s, tiles);

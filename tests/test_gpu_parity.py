@@ -261,6 +261,55 @@ def test_paired_stage_edges(k, trans_w):
     assert_bits_equal(outs[1], raw(outs[0]), "single 32-k stages vs paired")
 
 
+def _nt_operands(kind, m, n, k, dtype, seed):
+    """Activations m x k and transposed weights n x k: N(0,1) x N(0,0.02^2);
+    'wide': both scaled by powers of two per row, over 2^-12 .. 2^12 (bf16) or
+    2^-3 .. 2^3 (fp16, whose outputs must stay below 65504); 'cancel':
+    the second half of k repeats the first with the activations negated and
+    perturbed by one part in 2^7, so each output is a small difference of
+    large partial sums (its rounding depends on the order of the adds)."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(m, k, generator=g, dtype=torch.float64)
+    w = torch.randn(n, k, generator=g, dtype=torch.float64) * 0.02
+    if kind == "wide":
+        e = 12 if dtype == "bf16" else 3
+        x = x * torch.pow(2.0, torch.randint(-e, e + 1, (m, 1), generator=g).double())
+        w = w * torch.pow(2.0, torch.randint(-e, e + 1, (n, 1), generator=g).double())
+    elif kind == "cancel":
+        h = k // 2
+        x[:, h:] = -x[:, :h] * (1 + torch.randn(m, h, generator=g, dtype=torch.float64) / 128)
+        w[:, h:] = w[:, :h]
+    return x.to(TORCH_DT[dtype]), w.to(TORCH_DT[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("kind", ["normal", "wide", "cancel"])
+@pytest.mark.parametrize("m,n,k", [(4096, 4096, 64), (4000, 4104, 320), (4096, 4352, 1024)])
+def test_four_wave_tile_same_bits(dtype, kind, m, n, k, monkeypatch):
+    """A lone matmul with transposed weights and 256 x 256 tiles (k % 64 ==
+    0) runs the four-wave tile (four 128 x 128 waves of 16x16x32 MFMAs);
+    COC_FOUR_WAVE=0 makes the same launch run the eight-wave ring tile
+    (32x32x16 MFMAs).  Both add each output's products in the same 8-k steps
+    in increasing k, so the partials must be the same bits, also on operands
+    whose sums cancel or span a wide exponent range, and on ragged m and n."""
+    log(f"four-wave vs eight-wave tile {dtype} {kind} m={m} n={n} k={k}")
+    x, wt = _nt_operands(kind, m, n, k, dtype, 7 + m + n + k)
+    xd, wtd = dev(x), dev(wt)
+    outs = {}
+    for v in ("1", "0"):
+        monkeypatch.setenv("COC_FOUR_WAVE", v)
+        _, p = tgc.matmul_all_reduce(xd, wtd, [None], 0, split=1, trans_w=True)
+        torch.cuda.synchronize()
+        outs[v] = p
+    monkeypatch.delenv("COC_FOUR_WAVE")
+    assert torch.isfinite(outs["1"].float()).all()
+    assert_bits_equal(outs["1"], raw(outs["0"]), "four-wave vs eight-wave tile")
+    if kind == "normal":
+        rows = torch.arange(0, m, 97)
+        want = oracle.matmul(f64(x[rows], dtype), f64(wt, dtype).T)
+        assert_close(outs["1"][rows.to(outs["1"].device)], want, dtype, "sampled rows vs the oracle")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("m,n,k", TW_SHAPES)
 @pytest.mark.parametrize("split", [1, 4])
