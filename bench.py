@@ -275,6 +275,15 @@ def flops_of(inp):
     return 2.0 * ag.m * ag.n * ag.k, 2.0 * rs.m * rs.n * rs.k
 
 
+def blas_threads():
+    """Threads the host BLAS (numpy's matmul) uses."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(inp, frac, min_seconds=10.0):
     """The oracle on the same step with m scaled by `frac` (all n and k), repeated
     until at least `min_seconds` have passed; the rate is the mean over the passes."""
@@ -282,11 +291,7 @@ def cpu_baseline(inp, frac, min_seconds=10.0):
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = blas_threads()
 
     def f64(t):
         return oracle.decode(t.contiguous().view(__import__("torch").int16).numpy().view(np.uint16), "bf16")
@@ -330,6 +335,77 @@ def cpu_baseline(inp, frac, min_seconds=10.0):
                   f"RS {world}x{slice_rows} rows), all n and k; float64 numpy oracle incl. decoding the "
                   f"bf16 inputs; {passes} passes in {dt:.2f} s",
     }
+
+
+def run_cpu_configs(synth, min_seconds=3.0, target_flops=6e10):
+    """The oracle (host, float64 numpy) on every workload: a bounded sample of
+    the op's rows with all n and k (about target_flops of matmul per pass),
+    repeated until min_seconds have passed, inputs decoded from their stored
+    format inside the timed passes.  One JSON line per workload on stderr; no
+    GPU is used."""
+    import numpy as np
+
+    import oracle
+
+    def f64(t, dt):
+        if dt == "f32":
+            return t.numpy().astype(np.float64)
+        if dt == "i8":
+            return t.numpy().astype(np.float64)
+        return oracle.decode(t.contiguous().view(__import__("torch").int16).numpy().view(np.uint16), dt)
+
+    threads = blas_threads()
+    for wl in synth.WORKLOADS.values():
+        T, dt, n, k = wl.world, wl.dtype, wl.n, wl.k
+        per = max(1, int(target_flops / (2.0 * n * k)))
+        if wl.op in ("all_reduce", "w8a16"):
+            rows = min(wl.m, per)
+            x = synth.normal(wl.wid, synth.T_X, 0, (rows, k), wl.x_sigma, dt)
+            peers = [None] + [synth.normal(wl.wid, synth.T_PEER, r, (rows, n), wl.peer_sigma, dt) for r in range(1, T)]
+            if wl.op == "w8a16":
+                q = synth.integers(wl.wid, synth.T_W, 0, (k, n), -127, 127, "i8")
+                sc = synth.uniform(wl.wid, synth.T_SCALES, 0, (n,), 0.001, 0.02, "f16")
+
+                def one_pass():
+                    return oracle.matmul_all_reduce_w8a16(f64(x, dt), f64(q, "i8"), f64(sc, "f16"), "per_channel", 0,
+                                                         [None] + [f64(p, dt) for p in peers[1:]], 0)[0]
+            else:
+                w = synth.normal(wl.wid, synth.T_W, 0, (k, n), wl.w_sigma, dt)
+
+                def one_pass():
+                    return oracle.matmul_all_reduce(f64(x, dt), f64(w, dt), [None] + [f64(p, dt) for p in peers[1:]],
+                                                    0)[0]
+        elif wl.op == "reduce_scatter":
+            rl = max(1, min(wl.m // T, per // T))
+            rows = T * rl
+            x = synth.normal(wl.wid, synth.T_X, 0, (rows, k), wl.x_sigma, dt)
+            w = synth.normal(wl.wid, synth.T_W, 0, (k, n), wl.w_sigma, dt)
+            peers = [None] + [synth.normal(wl.wid, synth.T_PEER, r, (rows, n), wl.peer_sigma, dt) for r in range(1, T)]
+
+            def one_pass():
+                return oracle.matmul_reduce_scatter(f64(x, dt), f64(w, dt), [None] + [f64(p, dt) for p in peers[1:]],
+                                                    0)[0]
+        else:   # allgather
+            rl = max(1, min(wl.m // T, per // T))
+            rows = T * rl
+            shards = [synth.normal(wl.wid, synth.T_PEER, r, (rl, k), wl.x_sigma, dt) for r in range(T)]
+            w = synth.normal(wl.wid, synth.T_W, 0, (k, n), wl.w_sigma, dt)
+
+            def one_pass():
+                return oracle.allgather_matmul([f64(sh, dt) for sh in shards], f64(w, dt))[0]
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            y = one_pass()
+            passes += 1
+            dt_s = time.perf_counter() - t0
+            if dt_s >= min_seconds:
+                break
+        assert np.all(np.isfinite(y))
+        flops = passes * 2.0 * rows * n * k
+        print(json.dumps({"case": wl.name, "op": wl.op, "dtype": dt, "sample_rows": rows, "of_rows": wl.m,
+                          "n": n, "k": k, "passes": passes, "seconds": round(dt_s, 3),
+                          "oracle_tflops": round(flops / dt_s / 1e12, 6), "threads": int(threads),
+                          "cpu_model": cpu_model()}), file=sys.stderr, flush=True)
 
 
 def run_configs(torch, tgc, synth, dev, iters=10):
@@ -742,6 +818,9 @@ def main():
                          "then its serial form and the overlap view; one JSON line, and exit")
     ap.add_argument("--mfma-loop", action="store_true",
                     help="diagnostic: the bf16 MFMA rate on register operands, random against constant values")
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="only time the CPU oracle on every workload (a bounded sample of rows, all n and k; "
+                         "stderr lines, no GPU) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) three "
                          "times, for scaling the HBM byte counters, and exit")
@@ -759,6 +838,9 @@ def main():
     import tensor_gemm_collective_amd as tgc
     from tensor_gemm_collective_amd import synth
 
+    if args.cpu_configs:
+        run_cpu_configs(synth)
+        return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
     torch.cuda.set_device(0)
