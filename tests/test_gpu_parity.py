@@ -284,14 +284,16 @@ def _nt_operands(kind, m, n, k, dtype, seed):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("kind", ["normal", "wide", "cancel"])
-@pytest.mark.parametrize("m,n,k", [(4096, 4096, 64), (4000, 4104, 320), (4096, 4352, 1024)])
+@pytest.mark.parametrize("m,n,k", [(4096, 4096, 64), (4096, 4096, 128), (4096, 4096, 192), (4000, 4104, 320),
+                                   (4096, 4352, 1024)])
 def test_four_wave_tile_same_bits(dtype, kind, m, n, k, monkeypatch):
     """A lone matmul with transposed weights and 256 x 256 tiles (k % 64 ==
     0) runs the four-wave tile (four 128 x 128 waves of 16x16x32 MFMAs);
     COC_FOUR_WAVE=0 makes the same launch run the eight-wave ring tile
     (32x32x16 MFMAs).  Both add each output's products in the same 8-k steps
     in increasing k, so the partials must be the same bits, also on operands
-    whose sums cancel or span a wide exponent range, and on ragged m and n."""
+    whose sums cancel or span a wide exponent range, and on ragged m and n;
+    k = 64, 128 and 192 take the schedule's one-, two- and three-stage paths."""
     log(f"four-wave vs eight-wave tile {dtype} {kind} m={m} n={n} k={k}")
     x, wt = _nt_operands(kind, m, n, k, dtype, 7 + m + n + k)
     xd, wtd = dev(x), dev(wt)
