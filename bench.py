@@ -818,6 +818,9 @@ def main():
                          "then its serial form and the overlap view; one JSON line, and exit")
     ap.add_argument("--mfma-loop", action="store_true",
                     help="diagnostic: the bf16 MFMA rate on register operands, random against constant values")
+    ap.add_argument("--weights", choices=["kn", "nk"], default="kn",
+                    help="storage of the step's weights: kn (k x n, the default) or nk (n x k, a Linear "
+                         "layer's out x in layout, through the *_trans_w entry points; the same products)")
     ap.add_argument("--cpu-configs", action="store_true",
                     help="only time the CPU oracle on every workload (a bounded sample of rows, all n and k; "
                          "stderr lines, no GPU) and exit")
@@ -888,17 +891,23 @@ def main():
             if t is not None:
                 t[inp["rank"] * b:(inp["rank"] + 1) * b].fill_(1.0)
         args.no_cpu_baseline = True
+    trans = args.weights == "nk"
+    if trans:
+        # the same weights stored n x k (a Linear layer's out x in layout),
+        # multiplied through the *_trans_w entry points: the same products
+        inp["ag_w"] = inp["ag_w"].t().contiguous()
+        inp["rs_w"] = inp["rs_w"].t().contiguous()
     torch.cuda.synchronize()
     f_ag, f_rs = flops_of(inp)
     rank, split = inp["rank"], args.split
 
     def run_ag():
         tgc.allgather_matmul(inp["ag_x"], inp["ag_peers"], inp["ag_w"], rank, y=inp["ag_y"], ws=inp["ag_ws"],
-                             split=split)
+                             split=split, trans_w=trans)
 
     def run_rs():
         tgc.matmul_reduce_scatter(inp["rs_x"], inp["rs_w"], inp["rs_peers"], rank, y=inp["rs_y"],
-                                  partial_out=inp["rs_part"], split=split)
+                                  partial_out=inp["rs_part"], split=split, trans_w=trans)
 
     def step():
         run_ag()
@@ -1076,6 +1085,7 @@ def main():
             "workload": "LLaMA2-70B TP8+SP MLP, one rank: ALL_GATHER_MATMUL 8x(512x8192) @ 8192x7168 "
                         "then MATMUL_REDUCE_SCATTER 4096x3584 @ 3584x8192 -> 512x8192",
             "world": inp["world"], "rank": rank, "split": split, "deterministic": 0,
+            "weight_layout": "n x k (transposed, *_trans_w)" if trans else "k x n",
         },
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "breakdown": {

@@ -111,9 +111,10 @@
  *
  * Matmul tiles.  The kernel and tile a call runs never change its result
  * bits.  A bf16 / fp16 matmul with transposed weights (the *_trans_w entry
- * points) whose launch runs alone (nothing waits beside it) and fills the
- * device with 256 x 256 tiles, k % 64 == 0, uses a four-wave tile; every
- * other launch the eight-wave one.  COC_FOUR_WAVE=0, read at each call,
+ * points) whose launch shares no compute unit with another kernel (nothing
+ * waits beside it; the all-gather forms that copy their rows inside the
+ * launch qualify) and fills the device with 256 x 256 tiles, k % 64 == 0,
+ * uses a four-wave tile; every other launch the eight-wave one.  COC_FOUR_WAVE=0, read at each call,
  * keeps the eight-wave tile everywhere (for comparisons).
  */
 #ifndef COC_H

@@ -1394,15 +1394,16 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, int rows, int rpb
 
 // ------------------------------------------------------------------ four-wave tile
 // The 256 x 256 tile of the bf16 / fp16 launches with transposed weights (W
-// stored n x k, so both operands are k-contiguous) that run alone (no counter
-// to signal or wait on, no copy inside the launch), k % 64 == 0: four waves
+// stored n x k, so both operands are k-contiguous) that share no CU with
+// another kernel (no counter to signal, no wait except for rows the launch
+// copies itself), k % 64 == 0: four waves
 // of 128 x 128 (2 x 2), v_mfma_f32_16x16x32 (16 rows or columns by 32 k per
 // instruction, where ring_tile's v_mfma_f32_32x32x16 takes 32 by 16).  Per
 // 32 k the four waves read 64 KB of LDS fragments where ring_tile's eight
 // 128 x 64 waves read 96 KB.  One workgroup per CU uses nearly the whole
 // register file (one wave per SIMD), so nothing that must share a CU with the
-// matmul (a reduce waiting on its counters) can run beside it: launches that
-// signal, wait or copy keep ring_tile.  Both tiles add each output's products
+// matmul (a reduce waiting on its counters, a copy whose rows it waits for)
+// can run beside it: such launches keep ring_tile.  Both tiles add each output's products
 // in the same 8-k steps in increasing k (the MFMA shapes differ only in how
 // many steps one instruction takes), so they give the same bits, and no
 // result depends on which one ran.
@@ -1717,7 +1718,7 @@ __device__ __forceinline__ void fused_gather(const FusedGather& F, int c0, int c
 }
 
 // QUAD: 256 x 256 tiles of quad_tile (four waves, WM = WN = 2; transposed
-// weights, nothing to signal or wait on).
+// weights, nothing to signal, waits only on the launch's own copy).
 template <int BM, int BN, int S, int WM, int WN, int KIND, bool SIGNAL, bool TA = false, bool TB = false,
           bool PA = false, bool QUAD = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_ring_chunks(PersistParams P) {
@@ -2671,8 +2672,9 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
     P.stamps = stamp_region((int64_t)8 * P.per_xcd * (1 + P.fg.nchunks));
     P.fg.p.stamps = P.stamps;
     if constexpr (QUAD) {
-        // (the caller checked quad_ok: nothing signals, waits or copies)
-        if (signal || L.gather_nchunks > 0 || L.k % 64 != 0) return hipErrorInvalidValue;
+        // (the caller checked quad_ok: nothing signals, and only rows the
+        // launch copies itself are waited for)
+        if (signal || L.k % 64 != 0) return hipErrorInvalidValue;
         hipLaunchKernelGGL((gemm_ring_chunks<256, 256, 4, 2, 2, KIND, false, false, true, false, true>),
                            dim3(8 * P.per_xcd), dim3(256), 0, s, P);
         return hipGetLastError();
@@ -2701,16 +2703,16 @@ hipError_t launch_chunks_shape(const ChunksLaunch& L, int per_cu, hipStream_t s,
 
 // Whether a launch takes the four-wave tile: bf16 / fp16 with transposed
 // weights, 256 x 256 tiles, k % 64 == 0, and nothing beside it to share a CU
-// with (no counter to signal, no wait, no copy inside the launch).
+// with: no counter to signal, and no wait except for rows the launch copies
+// itself (its workgroups are then all resident at once, one per CU).
 // COC_FOUR_WAVE=0 keeps ring_tile (the result bits are the same; for A/B
 // timing).
 bool quad_ok(const ChunksLaunch& L) {
     const char* v = getenv("COC_FOUR_WAVE");
     if (v != nullptr && v[0] == '0') return false;
     if (!(L.kind == GK_BF16 || L.kind == GK_F16) || !L.trans_b || L.trans_a || L.k % 64 != 0) return false;
-    if (L.gather_nchunks > 0) return false;
     for (int c = 0; c < L.npieces; ++c)
-        if (L.wait[c] >= 0 || (L.done != nullptr && L.signal[c] >= 0)) return false;
+        if ((L.wait[c] >= 0 && L.gather_nchunks <= 0) || (L.done != nullptr && L.signal[c] >= 0)) return false;
     int bm = 0, bn = 0, per_cu = 0;
     return chunks_shape(L, &bm, &bn, &per_cu) == 0;
 }
