@@ -190,6 +190,24 @@ def test_llama_backward_pair(llama_ag):
 
 
 # ------------------------------------------------------------------ LLaMA2-70B matmul reduce-scatter
+@pytest.mark.parametrize("split", [4, 8])
+def test_llama_allgather_matmul_nk_weights(llama_ag, llama_ag_serial, split):
+    """The same all-gather product with W stored n x k (a Linear layer's out x
+    in layout) through the transposed-weight entry point: its launch copies
+    the gathered rows itself and takes the four-wave tile (448 tiles of
+    256 x 256, k % 64 == 0), and must give the serial k x n form's bits."""
+    wl, shards, w, _, y_ref = llama_ag
+    rank = 2
+    log(f"LLaMA2-70B AG bf16, W stored n x k, split={split} rank={rank}")
+    sd = [s.to(DEV) for s in shards]
+    wt = w.t().contiguous().to(DEV)
+    y = tgc.allgather_matmul(sd[rank], [None if r == rank else sd[r] for r in range(wl.world)], wt, rank,
+                             split=split, trans_w=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu().view(torch.int16), llama_ag_serial), "n x k weights: bits differ from k x n"
+    assert_close(y, y_ref, "bf16", "y")
+
+
 @pytest.fixture(scope="module")
 def llama_rs():
     wl = synth.WORKLOADS["llama70b_rs"]
@@ -242,6 +260,23 @@ def test_llama_reduce_scatter(llama_rs):
                     ref = y.clone()
                 else:
                     assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), "det bits differ across splits"
+
+
+def test_llama_reduce_scatter_nk_weights(llama_rs):
+    """The reduce-scatter product with W stored n x k through the transposed-
+    weight entry point (its serial matmul runs alone on the four-wave tile):
+    y and the partial must be the k x n call's bits."""
+    wl, rank, x, w, slices, p_ref, y_ref = llama_rs
+    peers = _rs_peers_dev(wl, rank, slices)
+    xd = x.to(DEV)
+    log(f"LLaMA2-70B RS bf16, W stored n x k, rank={rank}")
+    y0, p0 = tgc.matmul_reduce_scatter(xd, w.to(DEV), peers, rank, split=4, deterministic=1)
+    y1, p1 = tgc.matmul_reduce_scatter(xd, w.t().contiguous().to(DEV), peers, rank, split=4, deterministic=1,
+                                       trans_w=True)
+    torch.cuda.synchronize()
+    assert torch.equal(p1.view(torch.int16), p0.view(torch.int16)), "partial: n x k and k x n bits differ"
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16)), "y: n x k and k x n bits differ"
+    assert_close(y1, y_ref, "bf16", "y")
 
 
 # ------------------------------------------------------------------ BLOOM-176B deterministic all-reduce
